@@ -1,0 +1,236 @@
+"""Python entry points over the C ABI (torch tensors in, ctypes out).
+
+Argument marshalling only: every step of the relocation runs in the HIP
+library.  Tensors supply device memory, torch's current stream supplies the
+HIP stream.  Calls are asynchronous like any torch op; keep the tensors alive
+until the stream has run them.
+"""
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _abi
+from ._abi import (KVR_AMORTIZE, KVR_BF16, KVR_F32, KVR_FORGET, KVR_FORGET_NEEDS_PREFILL,  # noqa: F401
+                   KVR_OK, kvr_cache, kvr_directive, kvr_lowrank, kvr_part, kvr_rows)
+
+
+class KVRError(RuntimeError):
+    def __init__(self, fn, status):
+        lib = _abi.load()
+        msg = lib.kvr_status_str(status).decode()
+        if status == -5:
+            msg += f" (hipError {lib.kvr_last_hip_error()})"
+        super().__init__(f"{fn}: {msg} [status {status}]")
+        self.status = status
+
+
+def _check(fn, st):
+    if st < 0:
+        raise KVRError(fn, st)
+    return st
+
+
+_DT = {torch.bfloat16: KVR_BF16, torch.float32: KVR_F32}
+
+
+def _stream_handle():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _part(t):
+    """kvr_part of a [layers, blocks, rows, width] view with a unit last stride."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("cache parts must be [layers, blocks, rows, width] views with unit last stride")
+    return kvr_part(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+class KVCache:
+    """A paged KV cache: ``pf`` (position-free part) and ``rope`` (rotary part)
+    as [layers, blocks, block_size, width] tensor views."""
+
+    def __init__(self, pf, rope, rope_heads, rope_dim, rope_base, inv_freq=None):
+        if pf.shape[:3] != rope.shape[:3]:
+            raise ValueError("pf and rope views must share layers, blocks and rows")
+        if rope.shape[3] != rope_heads * rope_dim:
+            raise ValueError("rope width must be rope_heads * rope_dim")
+        self.pf, self.rope = pf, rope
+        self.n_layers, self.n_blocks, self.block_size = (int(x) for x in pf.shape[:3])
+        self.rope_heads, self.rope_dim, self.rope_base = rope_heads, rope_dim, float(rope_base)
+        self._inv = None
+        if inv_freq is not None:
+            self._inv = (ctypes.c_double * (rope_dim // 2))(*[float(x) for x in inv_freq])
+        self.c = kvr_cache(self.n_layers, self.block_size, self.n_blocks, int(pf.shape[3]), _DT[pf.dtype],
+                           rope_heads, rope_dim, _DT[rope.dtype], self.rope_base,
+                           ctypes.cast(self._inv, ctypes.POINTER(ctypes.c_double)) if self._inv else None,
+                           _part(pf), _part(rope))
+
+    @classmethod
+    def mla(cls, pool, pf_width=512, rope_dim=64, rope_base=10000.0):
+        """MLA pool [layers, blocks, block_size, 576]: row = [cKV | k_rope]."""
+        return cls(pool[..., :pf_width], pool[..., pf_width:], 1, rope_dim, rope_base)
+
+    @classmethod
+    def gqa(cls, k, v, heads, head_dim, rope_base=500000.0):
+        """GQA pools K, V [layers, blocks, block_size, heads*head_dim]."""
+        return cls(v, k, heads, head_dim, rope_base)
+
+
+@dataclass
+class Rows:
+    """Token rows outside the pool for every layer: pf [layers, len, pf_w],
+    rope [layers, len, rope_w] (unit last stride).  A registry entry
+    (cKV, k_r, base_pos) or a splice stub."""
+    pf: torch.Tensor
+    rope: torch.Tensor
+    base_pos: int = 0
+
+    def c(self):
+        if self.pf.shape[1] == 0:
+            return kvr_rows()             # no rows: nothing to copy
+        if self.pf.stride(-1) != 1 or self.rope.stride(-1) != 1:
+            raise ValueError("rows need a unit last stride")
+        return kvr_rows(self.pf.data_ptr(), self.pf.stride(0), self.pf.stride(1),
+                        self.rope.data_ptr(), self.rope.stride(0), self.rope.stride(1),
+                        int(self.pf.shape[1]), int(self.base_pos))
+
+
+@dataclass
+class LowRank:
+    """fp32 factors for every layer: U [layers, len, rank], V [layers, width, rank]."""
+    U: torch.Tensor
+    V: torch.Tensor
+
+    def c(self):
+        r = int(self.U.shape[-1])
+        if not (self.U.is_contiguous() and self.V.is_contiguous()) or self.U.dtype != torch.float32:
+            raise ValueError("factors must be contiguous float32")
+        return kvr_lowrank(self.U.data_ptr(), self.U.stride(0), self.V.data_ptr(), self.V.stride(0), r, 0)
+
+
+_workspaces = {}
+
+
+def _workspace(nbytes, device):
+    """A zero-filled workspace per (device, stream); every call leaves it zeroed."""
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           torch.cuda.current_stream().cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _directives(directives):
+    d = np.asarray(directives, dtype=np.int64).reshape(-1, 4) if len(directives) else np.zeros((0, 4), np.int64)
+    arr = (kvr_directive * max(1, len(d)))()
+    for i, (s, e, r, m) in enumerate(d):
+        arr[i] = kvr_directive(int(s), int(e), int(r), int(m), 0)
+    return arr, len(d)
+
+
+def splice_workspace_bytes(cache, seq_lens, directives):
+    lib = _abi.load()
+    dirs, n = _directives(directives)
+    lens = (ctypes.c_int64 * max(1, n))(*[int(x) for x in seq_lens])
+    return int(lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens, dirs))
+
+
+def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, workspace=None):
+    """In-place AMORTIZE/FORGET splices, one directive (s_start, s_end, r_len, mode) per sequence.
+
+    block_tables: int32 device tensor [n_seq, blocks_per_seq].  stubs: list of
+    Rows (or None per sequence) holding the prefilled replacement rows.
+    Returns (new_lens int64 array, status) -- status 1 means a FORGET was seen.
+    """
+    lib = _abi.load()
+    dirs, n = _directives(directives)
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be an int32 [n_seq, blocks] tensor with unit last stride")
+    lens = (ctypes.c_int64 * max(1, n))(*[int(x) for x in seq_lens])
+    out = (ctypes.c_int64 * max(1, n))()
+    stub_arr = None
+    if stubs is not None:
+        stub_arr = (kvr_rows * max(1, n))()
+        for i, s in enumerate(stubs):
+            if s is not None:
+                stub_arr[i] = s.c()
+    need = lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens, dirs)
+    ws = workspace if workspace is not None else _workspace(need, cache.pf.device)
+    st = lib.leyline_splice(ctypes.byref(cache.c), block_tables.data_ptr(), int(block_tables.stride(0)), n,
+                            lens, dirs, stub_arr, out, ws.data_ptr(), ws.numel() * ws.element_size(),
+                            _stream_handle())
+    _check("leyline_splice", st)
+    return np.array(out[:n], dtype=np.int64), st
+
+
+def kv_relocate_gather(cache, block_table, entries, p_targets, patch_rope=None, patch_pf=None):
+    """Gather registry entries (list of Rows) into one paged destination
+    sequence at logical slots p_targets[i] + t; optional rank-m patches
+    (lists of LowRank or None)."""
+    lib = _abi.load()
+    n = len(entries)
+    if block_table.dtype != torch.int32 or block_table.dim() != 1 or block_table.stride(0) != 1:
+        raise ValueError("block_table must be a contiguous int32 [blocks] tensor")
+    ents = (kvr_rows * max(1, n))(*[e.c() for e in entries])
+    pt = (ctypes.c_int64 * max(1, n))(*[int(x) for x in p_targets])
+
+    def lr(lst):
+        if lst is None:
+            return None
+        arr = (kvr_lowrank * max(1, n))()
+        for i, f in enumerate(lst):
+            if f is not None:
+                arr[i] = f.c()
+        return arr
+
+    st = lib.kv_relocate_gather(ctypes.byref(cache.c), block_table.data_ptr(), int(block_table.numel()), ents,
+                                pt, n, lr(patch_rope), lr(patch_pf), _stream_handle())
+    return _check("kv_relocate_gather", st)
+
+
+def kv_patch_lowrank(cache, block_table, part, p_starts, lens, factors):
+    """In-place X += U V^T on part 0 (position-free) or 1 (rotary) of the
+    logical slots [p_starts[i], p_starts[i] + lens[i]) of every layer."""
+    lib = _abi.load()
+    n = len(factors)
+    ps = (ctypes.c_int64 * max(1, n))(*[int(x) for x in p_starts])
+    ln = (ctypes.c_int64 * max(1, n))(*[int(x) for x in lens])
+    fs = (kvr_lowrank * max(1, n))(*[f.c() for f in factors])
+    st = lib.kv_patch_lowrank(ctypes.byref(cache.c), block_table.data_ptr(), int(block_table.numel()), int(part),
+                              ps, ln, fs, n, _stream_handle())
+    return _check("kv_patch_lowrank", st)
+
+
+def mla_decode_rotate_on_read(q_nope, q_rope, cache, layer, block_tables, pending_delta, seq_lens, scale,
+                              max_seq_len=None, out=None, lse=None, workspace=None):
+    """One absorbed-MLA decode step with per-block pending shifts applied to k_r on load.
+    Returns (out bf16 [b, h, 512], lse f32 [b, h])."""
+    lib = _abi.load()
+    b, h = int(q_nope.shape[0]), int(q_nope.shape[1])
+    if max_seq_len is None:
+        max_seq_len = int(block_tables.shape[1]) * cache.block_size
+    if out is None:
+        out = torch.empty((b, h, int(q_nope.shape[2])), dtype=torch.bfloat16, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((b, h), dtype=torch.float32, device=q_nope.device)
+    need = int(lib.kvr_decode_workspace_bytes(b, h, int(max_seq_len)))
+    ws = workspace if workspace is not None else _workspace(need, q_nope.device)
+    st = lib.mla_decode_rotate_on_read(q_nope.data_ptr(), q_rope.data_ptr(), b, h, ctypes.byref(cache.c), int(layer),
+                                       block_tables.data_ptr(), pending_delta.data_ptr(), int(block_tables.stride(0)),
+                                       seq_lens.data_ptr(), int(max_seq_len), float(scale), out.data_ptr(),
+                                       lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                       _stream_handle())
+    _check("mla_decode_rotate_on_read", st)
+    return out, lse
+
+
+def device_errors():
+    """Synchronize and return (then clear) the library's device error bits."""
+    lib = _abi.load()
+    v = ctypes.c_uint32(0)
+    _check("kvr_device_errors", lib.kvr_device_errors(ctypes.byref(v)))
+    return int(v.value)

@@ -1,0 +1,383 @@
+// Host side of the C ABI: argument validation, Delta/delta bookkeeping,
+// tiling, workspace layout and kernel launches.  Nothing here touches device
+// memory before every argument of a call has been validated.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "../../include/kvreloc.h"
+#include "kvr_internal.h"
+
+using namespace kvr;
+
+namespace {
+
+thread_local int32_t t_last_hip = 0;
+std::atomic<uint32_t> g_epoch{1};
+
+uint32_t next_epoch() {
+    uint32_t e = g_epoch.fetch_add(1);
+    if (e == 0) e = g_epoch.fetch_add(1);    // 0 is the value of a cleared flag
+    return e;
+}
+
+kvr_status hip_fail(hipError_t e) {
+    t_last_hip = (int32_t)e;
+    return KVR_E_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool mult16(int64_t v) { return (v % 16) == 0; }
+int esize(int32_t dtype) { return dtype == KVR_BF16 ? 2 : (dtype == KVR_F32 ? 4 : 0); }
+
+// Validate a cache descriptor and build the byte-addressed pool view and the
+// frequency table.
+kvr_status make_pool(const kvr_cache* c, Pool& P, double* theta) {
+    if (!c) return KVR_E_ARG;
+    const int pe = esize(c->pf_dtype), re = esize(c->rope_dtype);
+    if (!pe || !re) return KVR_E_ARG;
+    if (c->n_layers < 1 || c->block_size < 1 || c->n_blocks < 1) return KVR_E_ARG;
+    if (c->pf_width < 1 || c->rope_heads < 1 || c->rope_dim < 2 || (c->rope_dim & 1)) return KVR_E_ARG;
+    if (c->rope_dim / 2 > kMaxPairs || (int64_t)c->rope_heads * c->rope_dim > 4096) return KVR_E_ARG;
+    const int64_t pf_bytes = (int64_t)c->pf_width * pe;
+    const int64_t half_bytes = (int64_t)(c->rope_dim / 2) * re;
+    if (!mult16(pf_bytes) || !mult16(half_bytes) || pf_bytes / 16 > kThreads) return KVR_E_ARG;
+    if (!c->pf.base || !c->rope.base || !aligned16(c->pf.base) || !aligned16(c->rope.base)) return KVR_E_ARG;
+    const int64_t s[6] = {c->pf.layer_stride * pe, c->pf.block_stride * pe, c->pf.row_stride * pe,
+                          c->rope.layer_stride * re, c->rope.block_stride * re, c->rope.row_stride * re};
+    for (int64_t v : s)
+        if (v < 0 || !mult16(v)) return KVR_E_ARG;
+    if (!c->inv_freq && !(c->rope_base > 0.0)) return KVR_E_ARG;
+
+    P.pf = (char*)c->pf.base;   P.pf_l = s[0]; P.pf_b = s[1]; P.pf_r = s[2];
+    P.rp = (char*)c->rope.base; P.rp_l = s[3]; P.rp_b = s[4]; P.rp_r = s[5];
+    P.block_size = c->block_size;
+    P.n_blocks = c->n_blocks;
+    P.n_layers = c->n_layers;
+    P.pf_chunks = (int32_t)(pf_bytes / 16);
+    P.half_chunks = (int32_t)(half_bytes / 16);
+    P.rope_items = c->rope_heads * P.half_chunks;
+    P.head_bytes = (int32_t)(2 * half_bytes);
+    P.half_bytes = (int32_t)half_bytes;
+    P.n_pairs = c->rope_dim / 2;
+    P.pairs_per_chunk = 16 / re;
+    for (int j = 0; j < kMaxPairs; ++j) theta[j] = 0.0;
+    for (int j = 0; j < P.n_pairs; ++j) {
+        theta[j] = c->inv_freq ? c->inv_freq[j]
+                               : std::pow(c->rope_base, -2.0 * (double)j / (double)c->rope_dim);
+        if (!std::isfinite(theta[j])) return KVR_E_ARG;
+    }
+    return KVR_OK;
+}
+
+// Rows per tile and rotation items per thread: a tile's position-free part
+// fills at most kPfItems chunks per thread, its rotary part at most 16.
+void choose_tile(const Pool& P, int& T, int& rs) {
+    T = std::min(kMaxTileRows, (kThreads * kPfItems) / P.pf_chunks);
+    for (;;) {
+        const int need = (T * P.rope_items + kThreads - 1) / kThreads;
+        rs = 1;
+        while (rs < need) rs *= 2;
+        if (rs <= 16 || T == 1) break;
+        T /= 2;
+    }
+}
+
+kvr_status check_rows(const kvr_rows& r, const kvr_cache* c) {
+    const int pe = esize(c->pf_dtype), re = esize(c->rope_dtype);
+    if (!r.pf || !r.rope || !aligned16(r.pf) || !aligned16(r.rope)) return KVR_E_ARG;
+    const int64_t s[4] = {r.pf_layer_stride * pe, r.pf_row_stride * pe, r.rope_layer_stride * re,
+                          r.rope_row_stride * re};
+    for (int64_t v : s)
+        if (v < 0 || !mult16(v)) return KVR_E_ARG;
+    return KVR_OK;
+}
+
+SrcRows src_rows(const kvr_rows& r, const kvr_cache* c) {
+    const int pe = esize(c->pf_dtype), re = esize(c->rope_dtype);
+    SrcRows s;
+    s.pf = (const char*)r.pf;  s.pf_l = r.pf_layer_stride * pe;  s.pf_r = r.pf_row_stride * pe;
+    s.rp = (const char*)r.rope; s.rp_l = r.rope_layer_stride * re; s.rp_r = r.rope_row_stride * re;
+    return s;
+}
+
+// ------------------------------------------------------------------ splice --
+
+struct SpliceSeq {
+    int32_t seq;
+    Item item;
+};
+
+struct SplicePlan {
+    Pool pool;
+    double theta[kMaxPairs];
+    int T = 1, rs = 1;
+    std::vector<std::vector<SpliceSeq>> launches;
+    size_t counters_bytes = 0, flags_bytes = 0;
+    bool forget = false;
+    std::vector<int64_t> new_lens;
+};
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+kvr_status plan_splice(const kvr_cache* c, int32_t bt_stride, int32_t n_seq, const int64_t* seq_lens,
+                       const kvr_directive* dirs, const kvr_rows* stubs, SplicePlan& pl) {
+    kvr_status st = make_pool(c, pl.pool, pl.theta);
+    if (st != KVR_OK) return st;
+    if (n_seq < 0 || bt_stride < 1) return KVR_E_ARG;
+    if (n_seq > 0 && (!seq_lens || !dirs)) return KVR_E_ARG;
+    const int64_t capacity = (int64_t)bt_stride * c->block_size;
+    if (capacity >= (int64_t)1 << 31) return KVR_E_ARG;
+    choose_tile(pl.pool, pl.T, pl.rs);
+    const int T = pl.T;
+    pl.new_lens.assign(n_seq, 0);
+    std::vector<SpliceSeq> cur;
+    int32_t wg = 0;
+    for (int32_t b = 0; b < n_seq; ++b) {
+        const kvr_directive& d = dirs[b];
+        const int64_t N = seq_lens[b];
+        if (d.mode != KVR_AMORTIZE && d.mode != KVR_FORGET) return KVR_E_ARG;
+        if (N < 0 || N > capacity || d.s_start < 0 || d.s_start > d.s_end || d.s_end > N || d.r_len < 0)
+            return KVR_E_RANGE;
+        if (d.mode == KVR_FORGET) {
+            pl.new_lens[b] = d.s_start;
+            pl.forget = true;
+            continue;
+        }
+        const int64_t delta = d.r_len - (d.s_end - d.s_start);
+        if (N + delta > capacity) return KVR_E_CAPACITY;
+        pl.new_lens[b] = N + delta;
+        const bool has_stub = stubs && stubs[b].pf;
+        if (has_stub) {
+            st = check_rows(stubs[b], c);
+            if (st != KVR_OK) return st;
+            if (stubs[b].len != d.r_len) return KVR_E_RANGE;
+        }
+        Item it{};
+        if (has_stub) it.src = src_rows(stubs[b], c);
+        it.a = (int32_t)d.s_end;
+        it.b = (int32_t)d.s_start;
+        it.shift = (int32_t)delta;
+        it.moved = (int32_t)(N - d.s_end);
+        it.r_len = has_stub ? (int32_t)d.r_len : 0;
+        it.move_tiles = (delta != 0 && it.moved > 0) ? (it.moved + T - 1) / T : 0;
+        it.stub_tiles = (it.r_len + T - 1) / T;
+        it.tiles = it.move_tiles + it.stub_tiles;
+        it.bt_off = b * bt_stride;
+        if (it.tiles == 0) continue;
+        const int64_t add = (int64_t)it.tiles * c->n_layers;
+        if ((int)cur.size() == kMaxItems || wg + add >= ((int64_t)1 << 31)) {
+            pl.launches.push_back(cur);
+            cur.clear();
+            wg = 0;
+        }
+        it.wg_off = wg;
+        wg += (int32_t)add;
+        cur.push_back({b, it});
+    }
+    if (!cur.empty()) pl.launches.push_back(cur);
+    size_t maxc = 0, maxf = 0;
+    for (auto& L : pl.launches) {
+        size_t nwg = 0;
+        for (auto& s : L) nwg += (size_t)s.item.tiles * c->n_layers;
+        maxc = std::max(maxc, L.size() * (size_t)c->n_layers * 4);
+        maxf = std::max(maxf, nwg * 4);
+    }
+    pl.counters_bytes = round_up(maxc);
+    pl.flags_bytes = round_up(maxf);
+    return KVR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvr_abi_version(void) { return KVR_ABI_VERSION; }
+
+const char* kvr_status_str(kvr_status s) {
+    switch (s) {
+        case KVR_OK: return "ok";
+        case KVR_FORGET_NEEDS_PREFILL: return "FORGET directive: re-prefill from s_start";
+        case KVR_E_ARG: return "invalid argument (pointer, alignment, dtype, shape or stride)";
+        case KVR_E_RANGE: return "position or length out of range";
+        case KVR_E_CAPACITY: return "result exceeds block-table capacity";
+        case KVR_E_OVERLAP: return "target ranges overlap";
+        case KVR_E_HIP: return "HIP runtime error";
+        case KVR_E_WORKSPACE: return "workspace missing, misaligned or too small";
+        case KVR_E_UNSUPPORTED: return "unsupported configuration";
+        default: return "unknown status";
+    }
+}
+
+int32_t kvr_last_hip_error(void) { return t_last_hip; }
+
+kvr_status kvr_device_errors(uint32_t* flags) {
+    if (!flags) return KVR_E_ARG;
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e);
+    uint32_t v = read_and_clear_errors_relocate();
+    if (v == 0xffffffffu) return hip_fail(hipErrorUnknown);
+    *flags = v;
+    return KVR_OK;
+}
+
+kvr_status kvr_workspace_clear(void* d_ws, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return KVR_OK;
+    if (!d_ws || (reinterpret_cast<uintptr_t>(d_ws) & 3u) || (bytes & 3u)) return KVR_E_ARG;
+    hipError_t e = launch_fill_zero(d_ws, bytes, stream);
+    return e == hipSuccess ? KVR_OK : hip_fail(e);
+}
+
+size_t kvr_splice_workspace_bytes(const kvr_cache* cache, int32_t n_seq, const int64_t* seq_lens,
+                                  const kvr_directive* dirs) {
+    SplicePlan pl;
+    // The block-table stride only bounds capacity; use the largest so that
+    // the query never fails on it.  Stubs do not change the tile count bound
+    // (every stub row counts as if present).
+    std::vector<kvr_rows> fake;
+    if (!cache || n_seq < 0 || (n_seq > 0 && (!seq_lens || !dirs))) return 0;
+    fake.resize(n_seq);
+    for (int32_t b = 0; b < n_seq; ++b) {
+        std::memset(&fake[b], 0, sizeof(kvr_rows));
+        fake[b].pf = cache->pf.base;
+        fake[b].rope = cache->rope.base;
+        fake[b].len = dirs[b].r_len;
+    }
+    const int32_t bt_stride = (int32_t)std::max<int64_t>(1, ((int64_t)1 << 31) / std::max(1, cache->block_size) - 1);
+    if (plan_splice(cache, bt_stride, n_seq, seq_lens, dirs, fake.data(), pl) != KVR_OK) return 0;
+    return pl.counters_bytes + pl.flags_bytes;
+}
+
+kvr_status leyline_splice(const kvr_cache* cache, const int32_t* d_block_tables, int32_t bt_stride,
+                          int32_t n_seq, const int64_t* seq_lens, const kvr_directive* dirs,
+                          const kvr_rows* stubs, int64_t* new_lens, void* d_ws, size_t ws_bytes,
+                          hipStream_t stream) {
+    if (!d_block_tables || (reinterpret_cast<uintptr_t>(d_block_tables) & 3u)) return KVR_E_ARG;
+    if (n_seq > 0 && !new_lens) return KVR_E_ARG;
+    SplicePlan pl;
+    kvr_status st = plan_splice(cache, bt_stride, n_seq, seq_lens, dirs, stubs, pl);
+    if (st != KVR_OK) return st;
+    const size_t need = pl.counters_bytes + pl.flags_bytes;
+    if (!pl.launches.empty()) {
+        if (!d_ws || (reinterpret_cast<uintptr_t>(d_ws) % kAlign) || ws_bytes < need) return KVR_E_WORKSPACE;
+    }
+    for (int32_t b = 0; b < n_seq; ++b) new_lens[b] = pl.new_lens[b];
+    for (auto& L : pl.launches) {
+        RelocArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.pool = pl.pool;
+        a.bt = d_block_tables;
+        a.counters = (uint32_t*)d_ws;
+        a.flags = (uint32_t*)((char*)d_ws + pl.counters_bytes);
+        a.n_items = (int32_t)L.size();
+        a.tile_rows = pl.T;
+        a.epoch = next_epoch();
+        std::memcpy(a.theta, pl.theta, sizeof(a.theta));
+        int64_t nwg = 0;
+        for (size_t i = 0; i < L.size(); ++i) {
+            a.items[i] = L[i].item;
+            nwg += (int64_t)L[i].item.tiles * cache->n_layers;
+        }
+        a.n_wg = (int32_t)nwg;
+        hipError_t e = launch_splice(a, pl.rs, cache->rope_dtype == KVR_F32, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return pl.forget ? KVR_FORGET_NEEDS_PREFILL : KVR_OK;
+}
+
+// ------------------------------------------------------------------ gather --
+
+kvr_status kv_relocate_gather(const kvr_cache* dst, const int32_t* d_block_table, int32_t bt_len,
+                              const kvr_rows* entries, const int64_t* p_target, int32_t n,
+                              const kvr_lowrank* patch_rope, const kvr_lowrank* patch_pf,
+                              hipStream_t stream) {
+    Pool pool;
+    double theta[kMaxPairs];
+    kvr_status st = make_pool(dst, pool, theta);
+    if (st != KVR_OK) return st;
+    if (!d_block_table || (reinterpret_cast<uintptr_t>(d_block_table) & 3u) || bt_len < 1 || n < 0)
+        return KVR_E_ARG;
+    if (n > 0 && (!entries || !p_target)) return KVR_E_ARG;
+    const int64_t capacity = (int64_t)bt_len * dst->block_size;
+    if (capacity >= (int64_t)1 << 31) return KVR_E_ARG;
+    std::vector<std::pair<int64_t, int64_t>> rng;
+    for (int32_t i = 0; i < n; ++i) {
+        if (entries[i].len > 0) {
+            st = check_rows(entries[i], dst);
+            if (st != KVR_OK) return st;
+        }
+        const int64_t len = entries[i].len, p = p_target[i];
+        if (len < 0 || p < 0 || p + len > capacity) return KVR_E_RANGE;
+        const int64_t delta = p - entries[i].base_pos;
+        if (delta > INT32_MAX || delta < -(int64_t)INT32_MAX) return KVR_E_RANGE;
+        if (len > 0) rng.push_back({p, p + len});
+    }
+    std::sort(rng.begin(), rng.end());
+    for (size_t i = 1; i < rng.size(); ++i)
+        if (rng[i].first < rng[i - 1].second) return KVR_E_OVERLAP;
+    bool any_patch = false;
+    for (int32_t i = 0; i < n; ++i) {
+        if (patch_rope && patch_rope[i].rank) any_patch = true;
+        if (patch_pf && patch_pf[i].rank) any_patch = true;
+    }
+    if (any_patch) return KVR_E_UNSUPPORTED;
+
+    int T, rs;
+    choose_tile(pool, T, rs);
+    std::vector<Item> cur;
+    int64_t wg = 0;
+    auto flush = [&]() -> kvr_status {
+        if (cur.empty()) return KVR_OK;
+        RelocArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.pool = pool;
+        a.bt = d_block_table;
+        a.n_items = (int32_t)cur.size();
+        a.tile_rows = T;
+        a.n_wg = (int32_t)wg;
+        std::memcpy(a.theta, theta, sizeof(theta));
+        for (size_t i = 0; i < cur.size(); ++i) a.items[i] = cur[i];
+        hipError_t e = launch_gather(a, rs, dst->rope_dtype == KVR_F32, stream);
+        cur.clear();
+        wg = 0;
+        return e == hipSuccess ? KVR_OK : hip_fail(e);
+    };
+    for (int32_t i = 0; i < n; ++i) {
+        if (entries[i].len == 0) continue;
+        Item it{};
+        it.src = src_rows(entries[i], dst);
+        it.a = (int32_t)p_target[i];
+        it.shift = (int32_t)(p_target[i] - entries[i].base_pos);
+        it.moved = (int32_t)entries[i].len;
+        it.move_tiles = (it.moved + T - 1) / T;
+        it.tiles = it.move_tiles;
+        it.bt_off = 0;
+        const int64_t add = (int64_t)it.tiles * dst->n_layers;
+        if ((int)cur.size() == kMaxItems || wg + add >= ((int64_t)1 << 31)) {
+            st = flush();
+            if (st != KVR_OK) return st;
+        }
+        it.wg_off = (int32_t)wg;
+        wg += add;
+        cur.push_back(it);
+    }
+    return flush();
+}
+
+kvr_status kv_patch_lowrank(const kvr_cache*, const int32_t*, int32_t, int32_t, const int64_t*,
+                            const int64_t*, const kvr_lowrank*, int32_t, hipStream_t) {
+    return KVR_E_UNSUPPORTED;
+}
+
+size_t kvr_decode_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }
+
+kvr_status mla_decode_rotate_on_read(const void*, const void*, int32_t, int32_t, const kvr_cache*, int32_t,
+                                     const int32_t*, const int32_t*, int32_t, const int32_t*, int32_t, float,
+                                     void*, float*, void*, size_t, hipStream_t) {
+    return KVR_E_UNSUPPORTED;
+}
+
+}  // extern "C"

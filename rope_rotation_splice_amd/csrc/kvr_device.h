@@ -1,0 +1,90 @@
+// Device helpers shared by the relocation kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvr {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte global accesses.  Streaming traffic uses the nontemporal hint so
+// the bulk rows do not evict the small, re-read tables from L2/MALL.
+__device__ __forceinline__ v4u ld16(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+}
+__device__ __forceinline__ void st16(char* p, v4u v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p));
+}
+
+// bf16 <-> f32.  Widening is exact (bf16 is the top half of an f32).
+// Narrowing uses the hardware round-to-nearest-even pack (v_cvt_pk_bf16_f32),
+// which also keeps NaN a NaN.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// One rotation pair in fp32: (xl, xh) -> (xl c - xh s, xl s + xh c).
+__device__ __forceinline__ void rot2(float xl, float xh, float c, float s, float& yl, float& yh) {
+    yl = fmaf(xl, c, -(xh * s));
+    yh = fmaf(xl, s, xh * c);
+}
+
+// Rotate the 8 bf16 pairs held in a 16-byte "lo" chunk (x_j..x_{j+7}) and its
+// "hi" partner (x_{j+h}..x_{j+h+7}); cs[e] = (cos, sin) of pair j+e.
+__device__ __forceinline__ void rot_bf16x8(v4u& lo, v4u& hi, const float2* cs) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float2 c0 = cs[2 * w], c1 = cs[2 * w + 1];
+        float a0, b0, a1, b1;
+        rot2(bf_lo(lo[w]), bf_lo(hi[w]), c0.x, c0.y, a0, b0);
+        rot2(bf_hi(lo[w]), bf_hi(hi[w]), c1.x, c1.y, a1, b1);
+        lo[w] = pack_bf16(a0, a1);
+        hi[w] = pack_bf16(b0, b1);
+    }
+}
+
+// Same for 4 fp32 pairs per 16-byte chunk.
+__device__ __forceinline__ void rot_f32x4(v4u& lo, v4u& hi, const float2* cs) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        float a, b;
+        rot2(__uint_as_float(lo[w]), __uint_as_float(hi[w]), cs[w].x, cs[w].y, a, b);
+        lo[w] = __float_as_uint(a);
+        hi[w] = __float_as_uint(b);
+    }
+}
+
+// (cos, sin) of shift * theta_j for j < n_pairs, written to LDS by the first
+// n_pairs threads.  The angle is the float64 product of the integer shift and
+// the float64 frequency; cos/sin are evaluated in float64 (the device math
+// library reduces the argument in double precision) and rounded to float32.
+// The caller must __syncthreads() before reading `cs`.
+__device__ __forceinline__ void angle_table(float2* cs, const double* theta, int n_pairs,
+                                            int shift, int tid) {
+    if (tid < n_pairs) {
+        double s, c;
+        sincos((double)shift * theta[tid], &s, &c);
+        cs[tid] = make_float2((float)c, (float)s);
+    }
+}
+
+// Relaxed device-scope atomics (coherent across the XCDs' L2 caches).
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every vector-memory load this thread issued has returned data.
+// The "memory" clobber also keeps the compiler from sinking loads below it.
+__device__ __forceinline__ void wait_loads() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+}  // namespace kvr

@@ -1,0 +1,72 @@
+// Internal launch descriptors shared by the host entry points (api.cpp) and
+// the kernels.  Everything here is passed by value as kernel arguments, so a
+// launch needs no descriptor upload (no host->device copy before the kernel).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace kvr {
+
+constexpr int kThreads = 256;        // threads per workgroup (4 wave64)
+constexpr int kPfItems = 16;         // 16-byte position-free chunks held per thread
+constexpr int kMaxTileRows = 128;    // rows per tile (LDS row tables)
+constexpr int kMaxPairs = 128;       // rotation pairs per head (rope_dim <= 256)
+constexpr int kMaxItems = 16;        // sequences / entries per launch
+
+// Byte-addressed view of the two parts of a paged pool.
+struct Pool {
+    char* pf;  int64_t pf_l, pf_b, pf_r;     // strides in bytes
+    char* rp;  int64_t rp_l, rp_b, rp_r;
+    int32_t block_size, n_blocks, n_layers;
+    int32_t pf_chunks;      // 16-byte chunks of the position-free part per row
+    int32_t rope_items;     // rotation items per row: heads * half_chunks
+    int32_t half_chunks;    // 16-byte chunks in half a head
+    int32_t head_bytes;     // bytes of one rotary head
+    int32_t half_bytes;     // bytes of half a head
+    int32_t n_pairs;        // rope_dim / 2
+    int32_t pairs_per_chunk;  // 8 (bf16) or 4 (f32)
+};
+
+// Rows living outside the pool: a registry entry or a splice stub.
+struct SrcRows {
+    const char* pf; int64_t pf_l, pf_r;      // bytes
+    const char* rp; int64_t rp_l, rp_r;
+};
+
+// One sequence (splice) or one registry entry (gather) of a launch.
+struct Item {
+    SrcRows src;
+    int32_t a;            // splice: s_end (first moved slot); gather: p_target
+    int32_t b;            // splice: s_start (first stub slot)
+    int32_t shift;        // rotation shift (Delta or delta)
+    int32_t moved;        // splice: rows moved; gather: entry length
+    int32_t r_len;        // splice: stub rows written (0 = none)
+    int32_t move_tiles;   // per layer
+    int32_t stub_tiles;   // per layer
+    int32_t tiles;        // per layer: move_tiles + stub_tiles
+    int32_t bt_off;       // element offset of this item's block-table row
+    int32_t wg_off;       // first workgroup of this item (all layers)
+};
+
+struct RelocArgs {
+    Pool pool;
+    const int32_t* bt;
+    uint32_t* counters;   // splice: one ticket counter per (item, layer)
+    uint32_t* flags;      // splice: one "sources read" flag per tile
+    int32_t n_items;
+    int32_t tile_rows;
+    uint32_t epoch;       // value a flag takes when set in this launch
+    int32_t n_wg;
+    double theta[kMaxPairs];
+    Item items[kMaxItems];
+};
+
+// Launchers (relocate.hip).  rope_f32 selects fp32 keys; rope_slots is the
+// per-thread count of rotation items (1, 2, 4, 8 or 16).
+hipError_t launch_splice(const RelocArgs& a, int rope_slots, bool rope_f32, hipStream_t s);
+hipError_t launch_gather(const RelocArgs& a, int rope_slots, bool rope_f32, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+uint32_t read_and_clear_errors_relocate();
+
+}  // namespace kvr

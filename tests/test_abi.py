@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+entry point, and rejects invalid arguments before enqueuing anything (these
+calls never reach the GPU, so they run without one)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from rope_rotation_splice_amd import _abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvreloc.h")
+
+FAKE = 1 << 40          # 256-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*?[\s\*]+(\w+)\s*\([^;{}]*\)\s*;", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_functions_exported():
+    lib = _abi.load()
+    names = declared_functions()
+    assert {"leyline_splice", "kv_relocate_gather", "kv_patch_lowrank", "mla_decode_rotate_on_read"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_abi.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings():
+    lib = _abi.load()
+    for s in range(-7, 2):
+        assert lib.kvr_status_str(s)
+    assert lib.kvr_abi_version() == 1
+
+
+def mla_cache(n_layers=2, block_size=64, n_blocks=16):
+    c = _abi.kvr_cache()
+    c.n_layers, c.block_size, c.n_blocks = n_layers, block_size, n_blocks
+    c.pf_width, c.pf_dtype = 512, _abi.KVR_BF16
+    c.rope_heads, c.rope_dim, c.rope_dtype, c.rope_base = 1, 64, _abi.KVR_BF16, 10000.0
+    rs = 576
+    c.pf = _abi.kvr_part(FAKE, n_blocks * block_size * rs, block_size * rs, rs)
+    c.rope = _abi.kvr_part(FAKE + 1024, n_blocks * block_size * rs, block_size * rs, rs)
+    return c
+
+
+def splice(c, dirs, lens, bt_stride=8, stubs=None, ws=FAKE, ws_bytes=1 << 20):
+    lib = _abi.load()
+    n = len(dirs)
+    D = (_abi.kvr_directive * max(1, n))(*[_abi.kvr_directive(*d, 0) for d in dirs])
+    Ls = (ctypes.c_int64 * max(1, n))(*lens)
+    out = (ctypes.c_int64 * max(1, n))()
+    return lib.leyline_splice(ctypes.byref(c), FAKE, bt_stride, n, Ls, D, stubs, out, ws, ws_bytes, None), out
+
+
+@pytest.mark.parametrize("d,n,code", [
+    ((10, 5, 1, 0), 100, -2),        # s_start > s_end
+    ((-1, 5, 1, 0), 100, -2),        # negative start
+    ((10, 101, 1, 0), 100, -2),      # s_end beyond the sequence
+    ((10, 20, -1, 0), 100, -2),      # negative replacement length
+    ((10, 20, 1, 7), 100, -1),       # unknown mode
+    ((10, 20, 500, 0), 100, -3),     # grows beyond bt_stride * block_size = 512 slots
+    ((0, 0, 0, 0), 600, -2),         # current length beyond capacity
+])
+def test_splice_validation_errors(d, n, code):
+    st, _ = splice(mla_cache(), [d], [n])
+    assert st == code
+
+
+def test_splice_bad_cache_descriptors():
+    c = mla_cache()
+    c.pf_width = 500                  # 1000 bytes: not a multiple of 16
+    assert splice(c, [(1, 2, 1, 0)], [10])[0] == -1
+    c = mla_cache()
+    c.rope_dim = 63
+    assert splice(c, [(1, 2, 1, 0)], [10])[0] == -1
+    c = mla_cache()
+    c.pf = _abi.kvr_part(FAKE + 8, 0, 0, 576)      # misaligned base
+    assert splice(c, [(1, 2, 1, 0)], [10])[0] == -1
+    c = mla_cache()
+    c.rope_dtype = 9
+    assert splice(c, [(1, 2, 1, 0)], [10])[0] == -1
+
+
+def test_splice_workspace_checked():
+    c = mla_cache()
+    assert splice(c, [(10, 300, 5, 0)], [500], ws=None)[0] == -6
+    assert splice(c, [(10, 300, 5, 0)], [500], ws=FAKE + 16)[0] == -6
+    assert splice(c, [(10, 300, 5, 0)], [500], ws_bytes=8)[0] == -6
+
+
+def test_forget_only_needs_no_launch():
+    st, out = splice(mla_cache(), [(30, 50, 4, 1)], [100], ws=None, ws_bytes=0)
+    assert st == 1 and out[0] == 30
+
+
+def test_splice_workspace_query():
+    lib = _abi.load()
+    c = mla_cache()
+    D = (_abi.kvr_directive * 2)(_abi.kvr_directive(10, 300, 5, 0, 0), _abi.kvr_directive(0, 0, 0, 0, 0))
+    Ls = (ctypes.c_int64 * 2)(500, 500)
+    nbytes = lib.kvr_splice_workspace_bytes(ctypes.byref(c), 2, Ls, D)
+    # 2 layers x (ceil(200/64) move + 1 stub tile) flags, one counter per unit, 256-byte rounded
+    assert nbytes == 256 + 256
+
+
+def gather(c, ents, pts, bt_len=8):
+    lib = _abi.load()
+    n = len(ents)
+    E = (_abi.kvr_rows * max(1, n))(*ents)
+    P = (ctypes.c_int64 * max(1, n))(*pts)
+    return lib.kv_relocate_gather(ctypes.byref(c), FAKE, bt_len, E, P, n, None, None, None)
+
+
+def rows(length, base=0):
+    return _abi.kvr_rows(FAKE, length * 576, 576, FAKE + 1024, length * 576, 576, length, base)
+
+
+def test_gather_validation_errors():
+    c = mla_cache()
+    assert gather(c, [rows(10), rows(10)], [0, 5]) == -4          # overlapping targets
+    assert gather(c, [rows(10), rows(10)], [0, 10], bt_len=0) == -1
+    assert gather(c, [rows(100)], [500]) == -2                     # beyond 512-slot capacity
+    assert gather(c, [rows(10)], [-1]) == -2
+    bad = rows(10)
+    bad.pf = FAKE + 4
+    assert gather(c, [bad], [0]) == -1
+    assert gather(c, [rows(10, base=-(1 << 40))], [0]) == -2       # shift does not fit 32 bits
