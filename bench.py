@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Throughput of the KV-relocation hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the relocation path over one batch of synthetic,
+seeded input that is resident in HBM before the timed region starts.  The
+default workload is the registry gather: 32 registry entries (lengths
+U{256..2048}, base positions U{0..60000}) of a 61-layer MLA cache
+(cKV 512 + k_r 64, bf16) gathered into one 40960-slot paged sequence with
+64-slot blocks and a random block table, each entry rotated by its own
+delta = p_target - base_pos.  Other workloads: ``splice`` (one 4096-slot
+contiguous sequence, [1000, 1800) -> 16 stub slots) and ``splice_batched``
+(64 x 32768 slots x 61 layers, one directive per sequence).
+
+Prints one JSON line: slots relocated per second (a slot = one token
+position of one sequence, all layers), the roofline of the relocation
+kernel (algorithmic bytes / kernel time vs 8 TB/s), and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KV slots relocated/sec (δ-rotate + splice) and achieved HBM GB/s vs peak"
+MLA_ROW_BYTES = 1152
+
+
+def kernel_source_hash():
+    p = os.path.join(ROOT, "rope_rotation_splice_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(p)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(p, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}/{workload}")
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+# --------------------------------------------------------------- workloads ---
+
+class Gather:
+    name = "registry_gather"
+    kernel = "reloc_kernel<gather>"
+
+    def __init__(self):
+        import kvsynth
+        self.w = kvsynth.registry_gather()
+        self.slots = int(self.w.lens.sum())
+        L = self.w.shape.n_layers
+        self.bytes = self.slots * L * MLA_ROW_BYTES * 2 + self.w.block_table.nbytes
+        self.launches = 1
+        self.config = {"workload": "irminsul_registry_gather", "layers": L, "entries": len(self.w.lens),
+                       "dst_slots": self.w.dst_slots, "block_size": self.w.block_size,
+                       "entry_len": "U{256..2048}", "base_pos": "U{0..60000}", "slots_per_step": self.slots,
+                       "row": "cKV 512 + k_r 64 bf16", "rope_base": 10000}
+
+    def setup(self):
+        import torch
+        import kvsynth
+        import rope_rotation_splice_amd as rrs
+        w = self.w
+        L, B = w.shape.n_layers, w.block_size
+        self.pool = torch.empty((L, w.n_blocks, B, 576), dtype=torch.bfloat16, device="cuda")
+        kvsynth.fill_normal_(self.pool, 2, 1)
+        self.cache = rrs.KVCache.mla(self.pool)
+        self.ents = []
+        for i, ln in enumerate(w.lens):
+            ckv = torch.empty((L, int(ln), 512), dtype=torch.bfloat16, device="cuda")
+            kr = torch.empty((L, int(ln), 64), dtype=torch.bfloat16, device="cuda")
+            kvsynth.fill_normal_(ckv, 2, 2, i, 0)
+            kvsynth.fill_normal_(kr, 2, 2, i, 1)
+            self.ents.append(rrs.Rows(ckv, kr, int(w.base_pos[i])))
+        self.bt = torch.from_numpy(w.block_table).cuda()
+        self.pt = w.p_target.tolist()
+        self.rrs = rrs
+
+    def step(self):
+        self.rrs.kv_relocate_gather(self.cache, self.bt, self.ents, self.pt)
+
+    def cpu_baseline(self, budget_s):
+        """The oracle's gather on whole (entry, layer) slabs until the budget is spent."""
+        import kvsynth
+        from oracle import gather as og, rope as orope
+        th = orope.inv_freq(64, 10000.0)
+        w = self.w
+        rows = 0
+        spent = 0.0
+        slabs = 0
+        for i, ln in enumerate(w.lens):
+            r = kvsynth.rng(2, 9, i)
+            d = og.chunk_delta(int(w.p_target[i]), int(w.base_pos[i]))
+            for l in range(w.shape.n_layers):
+                pf = kvsynth.bf16_normal(r, (int(ln), 512))
+                rp = kvsynth.bf16_normal(r, (int(ln), 64))
+                t0 = time.perf_counter()
+                og.relocate_rows(pf, rp, d, 1, 64, th)
+                spent += time.perf_counter() - t0
+                rows += int(ln)
+                slabs += 1
+                if spent >= budget_s:
+                    break
+            if spent >= budget_s:
+                break
+        slots = rows / w.shape.n_layers
+        return {"value": slots / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
+                "sample": f"{slabs} (entry, layer) slabs = {rows} layer-rows of the same draw "
+                          f"({slots:.0f} slots), generation excluded, numpy fp64, one process"}
+
+
+class Splice:
+    name = "single_splice"
+    kernel = "reloc_kernel<splice>"
+
+    def __init__(self):
+        import kvsynth
+        from oracle import splice as osplice  # noqa: F401  (bookkeeping only via the library)
+        self.w = kvsynth.single_splice()
+        d = self.w.directives[0]
+        moved = 4096 - int(d[1])
+        self.slots = moved
+        self.bytes = (moved + int(d[2])) * MLA_ROW_BYTES * 2
+        self.launches = 1
+        self.config = {"workload": "leyline_single_splice", "layers": 1, "slots": 4096,
+                       "directive": [int(d[0]), int(d[1]), int(d[2]), "AMORTIZE"], "delta": int(d[2]) - int(d[1] - d[0]),
+                       "slots_per_step": moved, "layout": "contiguous"}
+
+    def setup(self):
+        import torch
+        import kvsynth
+        import rope_rotation_splice_amd as rrs
+        self.pool = torch.empty((1, 1, 4096, 576), dtype=torch.bfloat16, device="cuda")
+        kvsynth.fill_normal_(self.pool, 1, 1)
+        self.stub = torch.empty((1, 16, 576), dtype=torch.bfloat16, device="cuda")
+        kvsynth.fill_normal_(self.stub, 1, 2)
+        self.cache = rrs.KVCache.mla(self.pool)
+        self.bt = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+        self.dirs = [tuple(int(x) for x in self.w.directives[0])]
+        self.stubs = [rrs.Rows(self.stub[..., :512], self.stub[..., 512:])]
+        self.rrs = rrs
+
+    def step(self):
+        # the same directive on the restored length: same bytes and hazards each step
+        self.rrs.leyline_splice(self.cache, self.bt, [4096], self.dirs, self.stubs)
+
+    def cpu_baseline(self, budget_s):
+        import kvsynth
+        from oracle import splice as osplice, rope as orope
+        th = orope.inv_freq(64, 10000.0)
+        d = self.w.directives[0]
+        p = osplice.plan(4096, int(d[0]), int(d[1]), int(d[2]), 0)
+        r = kvsynth.rng(1, 9)
+        pf = kvsynth.bf16_normal(r, (4096, 512))
+        rp = kvsynth.bf16_normal(r, (4096, 64))
+        spf = kvsynth.bf16_normal(r, (16, 512))
+        srp = kvsynth.bf16_normal(r, (16, 64))
+        n, spent = 0, 0.0
+        while spent < min(budget_s, 3.0):
+            t0 = time.perf_counter()
+            osplice.splice_sequence(p, pf, rp, spf, srp, 1, 64, th)
+            spent += time.perf_counter() - t0
+            n += 1
+        return {"value": n * self.slots / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} repetitions of the whole splice, numpy fp64, one process"}
+
+
+class SpliceBatched:
+    name = "batched_splice"
+    kernel = "reloc_kernel<splice>"
+
+    def __init__(self):
+        import kvsynth
+        self.w = kvsynth.batched_splice()
+        d = self.w.directives
+        moved = (self.w.seq_lens - d[:, 1]).astype(np.int64)
+        delta = d[:, 2] - (d[:, 1] - d[:, 0])
+        moved = np.where(delta != 0, moved, 0)
+        L = self.w.shape.n_layers
+        self.slots = int(moved.sum())
+        self.bytes = int((moved.sum() + d[:, 2].sum()) * L * MLA_ROW_BYTES * 2)
+        self.launches = 2          # 64 sequences, 32 per launch
+        self.config = {"workload": "leyline_batched_splices", "sequences": self.w.n_seq, "slots": self.w.capacity,
+                       "layers": L, "block_size": self.w.block_size, "S_len": "U{64..8192}", "R_len": "U{8..64}",
+                       "slots_per_step": self.slots, "resident_GB": round(self.w.n_blocks * 64 * L * 1152 / 1e9, 1)}
+
+    def setup(self):
+        import torch
+        import kvsynth
+        import rope_rotation_splice_amd as rrs
+        w = self.w
+        L = w.shape.n_layers
+        self.pool = torch.empty((L, w.n_blocks, w.block_size, 576), dtype=torch.bfloat16, device="cuda")
+        kvsynth.fill_normal_(self.pool, 3, 1)
+        self.cache = rrs.KVCache.mla(self.pool)
+        self.bt = torch.from_numpy(w.block_tables).cuda()
+        self.stub_t = []
+        self.stubs = []
+        for b in range(w.n_seq):
+            st = torch.empty((L, int(w.directives[b, 2]), 576), dtype=torch.bfloat16, device="cuda")
+            kvsynth.fill_normal_(st, 3, 2, b)
+            self.stub_t.append(st)
+            self.stubs.append(rrs.Rows(st[..., :512], st[..., 512:]))
+        self.dirs = [tuple(int(x) for x in d) for d in w.directives]
+        self.lens = w.seq_lens.tolist()
+        self.rrs = rrs
+
+    def step(self):
+        self.rrs.leyline_splice(self.cache, self.bt, self.lens, self.dirs, self.stubs)
+
+    def cpu_baseline(self, budget_s):
+        import kvsynth
+        from oracle import splice as osplice, rope as orope
+        th = orope.inv_freq(64, 10000.0)
+        w = self.w
+        rows, spent, units = 0, 0.0, 0
+        for b in range(w.n_seq):
+            d = w.directives[b]
+            p = osplice.plan(int(w.seq_lens[b]), int(d[0]), int(d[1]), int(d[2]), 0)
+            r = kvsynth.rng(3, 9, b)
+            pf = kvsynth.bf16_normal(r, (int(w.seq_lens[b]), 512))
+            rp = kvsynth.bf16_normal(r, (int(w.seq_lens[b]), 64))
+            spf = kvsynth.bf16_normal(r, (int(d[2]), 512))
+            srp = kvsynth.bf16_normal(r, (int(d[2]), 64))
+            t0 = time.perf_counter()
+            osplice.splice_sequence(p, pf, rp, spf, srp, 1, 64, th)
+            spent += time.perf_counter() - t0
+            rows += p.moved_rows if p.delta != 0 else 0
+            units += 1
+            if spent >= budget_s:
+                break
+        slots = rows / w.shape.n_layers
+        return {"value": slots / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
+                "sample": f"{units} (sequence, layer) units of the same directives ({rows} moved layer-rows), "
+                          f"generation excluded, numpy fp64, one process"}
+
+
+class Copy:
+    """A plain device-to-device copy of the registry gather's byte volume
+    (torch's copy kernel): the practical read+write ceiling, and the known-size
+    kernel that calibrates the HBM byte counters."""
+    name = "copy"
+    kernel = "torch copy_"
+
+    def __init__(self):
+        g = Gather()
+        self.nbytes = g.bytes // 2 // 2 * 2
+        self.slots = g.slots
+        self.bytes = 2 * self.nbytes
+        self.launches = 1
+        self.config = {"workload": "device_copy", "bytes_read": self.nbytes, "bytes_written": self.nbytes}
+
+    def setup(self):
+        import torch
+        self.a = torch.empty(self.nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+        self.b = torch.empty_like(self.a)
+
+    def step(self):
+        self.b.copy_(self.a)
+
+    def cpu_baseline(self, budget_s):
+        return None
+
+
+WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "copy": Copy}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gather", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (relocation shards with no "
+              "exchange; see the sharding paragraph of the design notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    wl = WORKLOADS[args.workload]()
+    # the CPU oracle runs before the GPU is touched
+    cpu = None if args.no_cpu_baseline else wl.cpu_baseline(args.cpu_budget)
+
+    import torch
+    torch.cuda.set_device(0)
+    wl.setup()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    import rope_rotation_splice_amd as rrs
+    if rrs.device_errors():
+        raise SystemExit("device error flags set during warmup")
+
+    stream = torch.cuda.current_stream()          # the library launches on this stream
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        wl.step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    if rrs.device_errors():
+        raise SystemExit("device error flags set during the timed steps")
+
+    launches = args.steps * wl.launches
+    kernel_s = gpu_s / launches
+    bytes_per_launch = wl.bytes / wl.launches
+    achieved = bytes_per_launch / kernel_s / 1e9
+    traffic = stored_traffic(wl.kernel, wl.name)
+    out = {
+        "metric": METRIC,
+        "value": wl.slots * args.steps / wall,
+        "unit": "slots/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 cache rows, integer draws as stated in config)",
+        "config": wl.config,
+        "hbm_GBps_per_step": wl.bytes * args.steps / wall / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": wl.kernel, "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "avg_launch_us": kernel_s * 1e6},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -92,14 +92,19 @@ kvr_status check_rows(const kvr_rows& r, const kvr_cache* c) {
                           r.rope_row_stride * re};
     for (int64_t v : s)
         if (v < 0 || !mult16(v)) return KVR_E_ARG;
+    if (s[1] > INT32_MAX || s[3] > INT32_MAX) return KVR_E_ARG;
     return KVR_OK;
 }
 
 SrcRows src_rows(const kvr_rows& r, const kvr_cache* c) {
     const int pe = esize(c->pf_dtype), re = esize(c->rope_dtype);
     SrcRows s;
-    s.pf = (const char*)r.pf;  s.pf_l = r.pf_layer_stride * pe;  s.pf_r = r.pf_row_stride * pe;
-    s.rp = (const char*)r.rope; s.rp_l = r.rope_layer_stride * re; s.rp_r = r.rope_row_stride * re;
+    s.pf = (const char*)r.pf;
+    s.rp = (const char*)r.rope;
+    s.pf_l = r.pf_layer_stride * pe;
+    s.rp_l = r.rope_layer_stride * re;
+    s.pf_r = (int32_t)(r.pf_row_stride * pe);
+    s.rp_r = (int32_t)(r.rope_row_stride * re);
     return s;
 }
 
@@ -164,8 +169,7 @@ kvr_status plan_splice(const kvr_cache* c, int32_t bt_stride, int32_t n_seq, con
         it.moved = (int32_t)(N - d.s_end);
         it.r_len = has_stub ? (int32_t)d.r_len : 0;
         it.move_tiles = (delta != 0 && it.moved > 0) ? (it.moved + T - 1) / T : 0;
-        it.stub_tiles = (it.r_len + T - 1) / T;
-        it.tiles = it.move_tiles + it.stub_tiles;
+        it.tiles = it.move_tiles + (it.r_len + T - 1) / T;
         it.bt_off = b * bt_stride;
         if (it.tiles == 0) continue;
         const int64_t add = (int64_t)it.tiles * c->n_layers;

@@ -12,7 +12,7 @@ constexpr int kThreads = 256;        // threads per workgroup (4 wave64)
 constexpr int kPfItems = 16;         // 16-byte position-free chunks held per thread
 constexpr int kMaxTileRows = 128;    // rows per tile (LDS row tables)
 constexpr int kMaxPairs = 128;       // rotation pairs per head (rope_dim <= 256)
-constexpr int kMaxItems = 16;        // sequences / entries per launch
+constexpr int kMaxItems = 32;        // sequences / entries per launch
 
 // Byte-addressed view of the two parts of a paged pool.
 struct Pool {
@@ -30,8 +30,10 @@ struct Pool {
 
 // Rows living outside the pool: a registry entry or a splice stub.
 struct SrcRows {
-    const char* pf; int64_t pf_l, pf_r;      // bytes
-    const char* rp; int64_t rp_l, rp_r;
+    const char* pf;
+    const char* rp;
+    int64_t pf_l, rp_l;                      // layer strides, bytes
+    int32_t pf_r, rp_r;                      // row strides, bytes
 };
 
 // One sequence (splice) or one registry entry (gather) of a launch.
@@ -43,8 +45,7 @@ struct Item {
     int32_t moved;        // splice: rows moved; gather: entry length
     int32_t r_len;        // splice: stub rows written (0 = none)
     int32_t move_tiles;   // per layer
-    int32_t stub_tiles;   // per layer
-    int32_t tiles;        // per layer: move_tiles + stub_tiles
+    int32_t tiles;        // per layer: move tiles, then stub tiles
     int32_t bt_off;       // element offset of this item's block-table row
     int32_t wg_off;       // first workgroup of this item (all layers)
 };
@@ -61,6 +62,9 @@ struct RelocArgs {
     double theta[kMaxPairs];
     Item items[kMaxItems];
 };
+
+// Kernel arguments must stay within the 4 KB kernarg budget.
+static_assert(sizeof(RelocArgs) <= 4000, "relocation kernel arguments too large");
 
 // Launchers (relocate.hip).  rope_f32 selects fp32 keys; rope_slots is the
 // per-thread count of rotation items (1, 2, 4, 8 or 16).
