@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -33,8 +34,8 @@ bool mult16(int64_t v) { return (v % 16) == 0; }
 int esize(int32_t dtype) { return dtype == KVR_BF16 ? 2 : (dtype == KVR_F32 ? 4 : 0); }
 
 // Validate a cache descriptor and build the byte-addressed pool view and the
-// frequency table.
-kvr_status make_pool(const kvr_cache* c, Pool& P, double* theta) {
+// frequency table (omega_j = theta_j / 2 pi, revolutions per position).
+kvr_status make_pool(const kvr_cache* c, Pool& P, double* omega) {
     if (!c) return KVR_E_ARG;
     const int pe = esize(c->pf_dtype), re = esize(c->rope_dtype);
     if (!pe || !re) return KVR_E_ARG;
@@ -54,6 +55,9 @@ kvr_status make_pool(const kvr_cache* c, Pool& P, double* theta) {
     P.pf = (char*)c->pf.base;   P.pf_l = s[0]; P.pf_b = s[1]; P.pf_r = s[2];
     P.rp = (char*)c->rope.base; P.rp_l = s[3]; P.rp_b = s[4]; P.rp_r = s[5];
     P.block_size = c->block_size;
+    P.bs_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((1 << sh) == c->block_size) P.bs_shift = sh;
     P.n_blocks = c->n_blocks;
     P.n_layers = c->n_layers;
     P.pf_chunks = (int32_t)(pf_bytes / 16);
@@ -63,25 +67,43 @@ kvr_status make_pool(const kvr_cache* c, Pool& P, double* theta) {
     P.half_bytes = (int32_t)half_bytes;
     P.n_pairs = c->rope_dim / 2;
     P.pairs_per_chunk = 16 / re;
-    for (int j = 0; j < kMaxPairs; ++j) theta[j] = 0.0;
+    for (int j = 0; j < kMaxPairs; ++j) omega[j] = 0.0;
     for (int j = 0; j < P.n_pairs; ++j) {
-        theta[j] = c->inv_freq ? c->inv_freq[j]
-                               : std::pow(c->rope_base, -2.0 * (double)j / (double)c->rope_dim);
-        if (!std::isfinite(theta[j])) return KVR_E_ARG;
+        const double th = c->inv_freq ? c->inv_freq[j]
+                                      : std::pow(c->rope_base, -2.0 * (double)j / (double)c->rope_dim);
+        if (!std::isfinite(th)) return KVR_E_ARG;
+        omega[j] = th / (2.0 * M_PI);     // revolutions per position
     }
     return KVR_OK;
 }
 
-// Rows per tile and rotation items per thread: a tile's position-free part
-// fills at most kPfItems chunks per thread, its rotary part at most 16.
-void choose_tile(const Pool& P, int& T, int& rs) {
-    T = std::min(kMaxTileRows, (kThreads * kPfItems) / P.pf_chunks);
+// Tile shape: rows per tile T, and the per-thread counts of position-free
+// chunks (pfi) and rotation items (rs) it needs, both powers of two <= 16.
+// Measured on MI355X (61-layer MLA rows): the gather streams best with about
+// 9 KB of row data per workgroup (many short-lived workgroups), the in-place
+// splice with about 36 KB (its per-tile ticket and flag round trips need
+// more bytes per workgroup to hide).  KVR_TILE_ROWS overrides T (tuning).
+struct TileShape { int T, pfi, rs; };
+
+int pow2_at_least(int v) { int p = 1; while (p < v) p *= 2; return p; }
+int pow2_at_most(int v) { int p = 1; while (p * 2 <= v) p *= 2; return p; }
+
+TileShape choose_tile(const Pool& P, bool rope_f32, bool splice) {
+    const int row_bytes = 16 * (P.pf_chunks + 2 * P.rope_items);
+    int T = pow2_at_most(std::max(1, (splice ? 36864 : 9216) / row_bytes));
+    if (const char* e = std::getenv("KVR_TILE_ROWS")) {
+        const int v = std::atoi(e);
+        if (v > 0) T = v;
+    }
+    T = std::min(T, kMaxTileRows);
+    if (rope_f32) T = std::min(kMaxTileRows, (kThreads * kPfItems) / P.pf_chunks);
     for (;;) {
-        const int need = (T * P.rope_items + kThreads - 1) / kThreads;
-        rs = 1;
-        while (rs < need) rs *= 2;
-        if (rs <= 16 || T == 1) break;
-        T /= 2;
+        TileShape s{T, pow2_at_least((T * P.pf_chunks + kThreads - 1) / kThreads),
+                    pow2_at_least((T * P.rope_items + kThreads - 1) / kThreads)};
+        if (rope_f32) s.pfi = kPfItems;          // fp32 keys: one register shape only
+        s.pfi = std::max(s.pfi, s.rs);
+        if (s.pfi <= kPfItems || T == 1) return s;
+        T = std::max(1, T / 2);
     }
 }
 
@@ -117,8 +139,8 @@ struct SpliceSeq {
 
 struct SplicePlan {
     Pool pool;
-    double theta[kMaxPairs];
-    int T = 1, rs = 1;
+    double omega[kMaxPairs];
+    TileShape tile{1, 1, 1};
     std::vector<std::vector<SpliceSeq>> launches;
     size_t counters_bytes = 0, flags_bytes = 0;
     bool forget = false;
@@ -130,14 +152,14 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 kvr_status plan_splice(const kvr_cache* c, int32_t bt_stride, int32_t n_seq, const int64_t* seq_lens,
                        const kvr_directive* dirs, const kvr_rows* stubs, SplicePlan& pl) {
-    kvr_status st = make_pool(c, pl.pool, pl.theta);
+    kvr_status st = make_pool(c, pl.pool, pl.omega);
     if (st != KVR_OK) return st;
     if (n_seq < 0 || bt_stride < 1) return KVR_E_ARG;
     if (n_seq > 0 && (!seq_lens || !dirs)) return KVR_E_ARG;
     const int64_t capacity = (int64_t)bt_stride * c->block_size;
     if (capacity >= (int64_t)1 << 31) return KVR_E_ARG;
-    choose_tile(pl.pool, pl.T, pl.rs);
-    const int T = pl.T;
+    pl.tile = choose_tile(pl.pool, c->rope_dtype == KVR_F32, true);
+    const int T = pl.tile.T;
     pl.new_lens.assign(n_seq, 0);
     std::vector<SpliceSeq> cur;
     int32_t wg = 0;
@@ -277,16 +299,16 @@ kvr_status leyline_splice(const kvr_cache* cache, const int32_t* d_block_tables,
         a.counters = (uint32_t*)d_ws;
         a.flags = (uint32_t*)((char*)d_ws + pl.counters_bytes);
         a.n_items = (int32_t)L.size();
-        a.tile_rows = pl.T;
+        a.tile_rows = pl.tile.T;
         a.epoch = next_epoch();
-        std::memcpy(a.theta, pl.theta, sizeof(a.theta));
+        std::memcpy(a.omega, pl.omega, sizeof(a.omega));
         int64_t nwg = 0;
         for (size_t i = 0; i < L.size(); ++i) {
             a.items[i] = L[i].item;
             nwg += (int64_t)L[i].item.tiles * cache->n_layers;
         }
         a.n_wg = (int32_t)nwg;
-        hipError_t e = launch_splice(a, pl.rs, cache->rope_dtype == KVR_F32, stream);
+        hipError_t e = launch_splice(a, pl.tile.pfi, pl.tile.rs, cache->rope_dtype == KVR_F32, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
     return pl.forget ? KVR_FORGET_NEEDS_PREFILL : KVR_OK;
@@ -299,8 +321,8 @@ kvr_status kv_relocate_gather(const kvr_cache* dst, const int32_t* d_block_table
                               const kvr_lowrank* patch_rope, const kvr_lowrank* patch_pf,
                               hipStream_t stream) {
     Pool pool;
-    double theta[kMaxPairs];
-    kvr_status st = make_pool(dst, pool, theta);
+    double omega[kMaxPairs];
+    kvr_status st = make_pool(dst, pool, omega);
     if (st != KVR_OK) return st;
     if (!d_block_table || (reinterpret_cast<uintptr_t>(d_block_table) & 3u) || bt_len < 1 || n < 0)
         return KVR_E_ARG;
@@ -329,8 +351,8 @@ kvr_status kv_relocate_gather(const kvr_cache* dst, const int32_t* d_block_table
     }
     if (any_patch) return KVR_E_UNSUPPORTED;
 
-    int T, rs;
-    choose_tile(pool, T, rs);
+    const TileShape tile = choose_tile(pool, dst->rope_dtype == KVR_F32, false);
+    const int T = tile.T;
     std::vector<Item> cur;
     int64_t wg = 0;
     auto flush = [&]() -> kvr_status {
@@ -342,9 +364,9 @@ kvr_status kv_relocate_gather(const kvr_cache* dst, const int32_t* d_block_table
         a.n_items = (int32_t)cur.size();
         a.tile_rows = T;
         a.n_wg = (int32_t)wg;
-        std::memcpy(a.theta, theta, sizeof(theta));
+        std::memcpy(a.omega, omega, sizeof(omega));
         for (size_t i = 0; i < cur.size(); ++i) a.items[i] = cur[i];
-        hipError_t e = launch_gather(a, rs, dst->rope_dtype == KVR_F32, stream);
+        hipError_t e = launch_gather(a, tile.pfi, tile.rs, dst->rope_dtype == KVR_F32, stream);
         cur.clear();
         wg = 0;
         return e == hipSuccess ? KVR_OK : hip_fail(e);

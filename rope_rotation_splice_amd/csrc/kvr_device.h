@@ -59,17 +59,22 @@ __device__ __forceinline__ void rot_f32x4(v4u& lo, v4u& hi, const float2* cs) {
     }
 }
 
-// (cos, sin) of shift * theta_j for j < n_pairs, written to LDS by the first
-// n_pairs threads.  The angle is the float64 product of the integer shift and
-// the float64 frequency; cos/sin are evaluated in float64 (the device math
-// library reduces the argument in double precision) and rounded to float32.
+// (cos, sin) of the angle shift * theta_j for j < n_pairs, written to LDS by
+// the first n_pairs threads.  omega_j = theta_j / (2 pi) is the frequency in
+// revolutions per position (float64).  The angle is reduced in float64:
+// u = shift * omega_j (relative error ~2^-52), and its fractional part
+// f = u - rint(u) in [-1/2, 1/2] is exact.  Only the reduced angle 2 pi f,
+// |2 pi f| <= pi, goes to float32 sincos, so the error stays ~2e-7 absolute at
+// any |shift| (a float32 product shift * theta would lose ~|shift| * 2^-24 rad).
 // The caller must __syncthreads() before reading `cs`.
-__device__ __forceinline__ void angle_table(float2* cs, const double* theta, int n_pairs,
+__device__ __forceinline__ void angle_table(float2* cs, const double* omega, int n_pairs,
                                             int shift, int tid) {
     if (tid < n_pairs) {
-        double s, c;
-        sincos((double)shift * theta[tid], &s, &c);
-        cs[tid] = make_float2((float)c, (float)s);
+        const double u = (double)shift * omega[tid];
+        const double f = u - rint(u);
+        float s, c;
+        sincosf((float)(f * 6.283185307179586476925), &s, &c);
+        cs[tid] = make_float2(c, s);
     }
 }
 

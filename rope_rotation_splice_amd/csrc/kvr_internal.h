@@ -9,7 +9,7 @@
 namespace kvr {
 
 constexpr int kThreads = 256;        // threads per workgroup (4 wave64)
-constexpr int kPfItems = 16;         // 16-byte position-free chunks held per thread
+constexpr int kPfItems = 16;         // max 16-byte position-free chunks held per thread
 constexpr int kMaxTileRows = 128;    // rows per tile (LDS row tables)
 constexpr int kMaxPairs = 128;       // rotation pairs per head (rope_dim <= 256)
 constexpr int kMaxItems = 32;        // sequences / entries per launch
@@ -19,6 +19,7 @@ struct Pool {
     char* pf;  int64_t pf_l, pf_b, pf_r;     // strides in bytes
     char* rp;  int64_t rp_l, rp_b, rp_r;
     int32_t block_size, n_blocks, n_layers;
+    int32_t bs_shift;       // log2(block_size) if a power of two, else -1
     int32_t pf_chunks;      // 16-byte chunks of the position-free part per row
     int32_t rope_items;     // rotation items per row: heads * half_chunks
     int32_t half_chunks;    // 16-byte chunks in half a head
@@ -59,17 +60,18 @@ struct RelocArgs {
     int32_t tile_rows;
     uint32_t epoch;       // value a flag takes when set in this launch
     int32_t n_wg;
-    double theta[kMaxPairs];
+    double omega[kMaxPairs];   // theta_j / (2 pi): revolutions per position
     Item items[kMaxItems];
 };
 
 // Kernel arguments must stay within the 4 KB kernarg budget.
 static_assert(sizeof(RelocArgs) <= 4000, "relocation kernel arguments too large");
 
-// Launchers (relocate.hip).  rope_f32 selects fp32 keys; rope_slots is the
-// per-thread count of rotation items (1, 2, 4, 8 or 16).
-hipError_t launch_splice(const RelocArgs& a, int rope_slots, bool rope_f32, hipStream_t s);
-hipError_t launch_gather(const RelocArgs& a, int rope_slots, bool rope_f32, hipStream_t s);
+// Launchers (relocate.hip).  pf_slots / rope_slots are the per-thread counts
+// of 16-byte position-free chunks and of rotation items a tile needs (powers
+// of two up to 16, rope_slots <= pf_slots); rope_f32 selects fp32 keys.
+hipError_t launch_splice(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
+hipError_t launch_gather(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 uint32_t read_and_clear_errors_relocate();
 

@@ -45,7 +45,7 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return -floor_div(-a, b)
 
 enum Mode { kSplice = 0, kGather = 1 };
 
-template <int MODE, int RS, bool RF32>
+template <int MODE, int PFI, int RS, bool RF32>
 __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
     __shared__ float2 s_cs[kMaxPairs];
     __shared__ int32_t s_src_blk[kMaxTileRows], s_src_row[kMaxTileRows];
@@ -58,7 +58,13 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
 
     // ---- which unit (item, layer) and which tile --------------------------
     int it = 0;
-    while (it + 1 < A.n_items && bid >= A.items[it + 1].wg_off) ++it;
+    {
+        int hi = A.n_items - 1;          // last item whose first workgroup <= bid
+        while (it < hi) {
+            const int mid = (it + hi + 1) >> 1;
+            if (bid >= A.items[mid].wg_off) it = mid; else hi = mid - 1;
+        }
+    }
     const Item& I = A.items[it];
     const int local = bid - I.wg_off;
     const int layer = local / I.tiles;
@@ -96,88 +102,107 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
     const int nrows = r1 - r0;
     const bool src_in_pool = (MODE == kSplice) && is_move;
     const bool rotate = is_move && I.shift != 0;
+    const int32_t* bt = A.bt + I.bt_off;
+    // destination slot of row i of this tile's range
+    const int dbase = (MODE == kGather) ? I.a : (is_move ? I.a + I.shift : I.b);
 
-    // ---- row tables (block-table lookups staged in LDS) -------------------
+    // ---- block-table lookups: one per row, staged in LDS -------------------
+    // Vector-memory loads complete in order, so each row's block-table entry
+    // is requested before any row data: using it later never waits behind a
+    // row load.  Source rows of a splice move live in the pool and need their
+    // entries before the data loads (one round trip + barrier); registry and
+    // stub rows are contiguous and load at once.
+    auto bt_index = [&](int slot) { return P.bs_shift >= 0 ? (slot >> P.bs_shift) : slot / P.block_size; };
+    auto in_block = [&](int slot) {
+        return P.bs_shift >= 0 ? (slot & (P.block_size - 1)) : slot - (slot / P.block_size) * P.block_size;
+    };
+    const int sbase = I.a + r0;            // source slot of row 0 (splice move tiles)
+    const int dslot0 = dbase + r0;
+    const unsigned nb = (unsigned)P.n_blocks;
+    int my_db = 0, my_sb = 0;
     if (tid < nrows) {
-        const int i = r0 + tid;
-        const int32_t* bt = A.bt + I.bt_off;
-        const int B = P.block_size;
-        const int dslot = (MODE == kGather) ? I.a + i : (is_move ? I.a + i + I.shift : I.b + i);
-        int db = bt[dslot / B];
-        bool ok = (unsigned)db < (unsigned)P.n_blocks;
-        int sb = 0, sr = i;
-        if (src_in_pool) {
-            const int sslot = I.a + i;
-            sb = bt[sslot / B];
-            sr = sslot % B;
-            ok = ok && (unsigned)sb < (unsigned)P.n_blocks;
-        }
-        if (!ok) { raise_error(KVR_DEV_BAD_BLOCK); db = -1; }
-        s_dst_blk[tid] = db;
-        s_dst_row[tid] = dslot % B;
-        s_src_blk[tid] = sb;
-        s_src_row[tid] = sr;
+        my_db = bt[bt_index(dslot0 + tid)];
+        if (src_in_pool) my_sb = bt[bt_index(sbase + tid)];
     }
-    if (rotate) angle_table(s_cs, A.theta, P.n_pairs, I.shift, tid);
-    __syncthreads();
-
-    // ---- loads ------------------------------------------------------------
-    const int64_t lpf = (int64_t)layer * (src_in_pool ? P.pf_l : I.src.pf_l);
-    const int64_t lrp = (int64_t)layer * (src_in_pool ? P.rp_l : I.src.rp_l);
-    auto src_pf = [&](int row) -> const char* {
-        return src_in_pool ? P.pf + lpf + (int64_t)s_src_blk[row] * P.pf_b + (int64_t)s_src_row[row] * P.pf_r
-                           : I.src.pf + lpf + (int64_t)(r0 + row) * I.src.pf_r;
-    };
-    auto src_rp = [&](int row) -> const char* {
-        return src_in_pool ? P.rp + lrp + (int64_t)s_src_blk[row] * P.rp_b + (int64_t)s_src_row[row] * P.rp_r
-                           : I.src.rp + lrp + (int64_t)(r0 + row) * I.src.rp_r;
-    };
+    if (src_in_pool) {
+        if (tid < nrows) {
+            const bool ok = (unsigned)my_sb < nb;
+            if (!ok) raise_error(KVR_DEV_BAD_BLOCK);
+            s_src_blk[tid] = ok ? my_sb : -1;
+            s_src_row[tid] = in_block(sbase + tid);
+        }
+        __syncthreads();
+    }
 
     const int pfc = P.pf_chunks;
     const int pf_total = nrows * pfc;
     const int step_row = kThreads / pfc, step_c = kThreads % pfc;
-    v4u pv[kPfItems];
+    const int ri = P.rope_items;
+    const int rp_total = nrows * ri;
+    const char* spf = src_in_pool ? P.pf + (int64_t)layer * P.pf_l : I.src.pf + (int64_t)layer * I.src.pf_l;
+    const char* srp = src_in_pool ? P.rp + (int64_t)layer * P.rp_l : I.src.rp + (int64_t)layer * I.src.rp_l;
+    v4u pv[PFI];
+    int pf_row[PFI], pf_c[PFI];
     {
-        int row = tid / pfc, c = tid % pfc;
+        int row = tid / pfc, c = tid - (tid / pfc) * pfc;
 #pragma unroll
-        for (int k = 0; k < kPfItems; ++k) {
-            const int q = tid + k * kThreads;
-            if (q < pf_total && s_dst_blk[row] >= 0) pv[k] = ld16(src_pf(row) + c * 16);
+        for (int k = 0; k < PFI; ++k) {
+            pf_row[k] = -1;
+            if (tid + k * kThreads < pf_total && (!src_in_pool || s_src_blk[row] >= 0)) {
+                pf_row[k] = row;
+                pf_c[k] = c;
+                const char* p = src_in_pool
+                    ? spf + (int64_t)s_src_blk[row] * P.pf_b + (int64_t)s_src_row[row] * P.pf_r
+                    : spf + (int64_t)(r0 + row) * I.src.pf_r;
+                pv[k] = ld16(p + c * 16);
+            }
             row += step_row; c += step_c;
             if (c >= pfc) { c -= pfc; ++row; }
         }
     }
-    const int ri = P.rope_items;
-    const int rp_total = nrows * ri;
     v4u lo[RS], hi[RS];
+    int rp_row[RS], rp_off[RS];
 #pragma unroll
     for (int k = 0; k < RS; ++k) {
         const int q = tid + k * kThreads;
+        rp_row[k] = -1;
         if (q < rp_total) {
             const int row = q / ri, item = q - row * ri;
-            const int head = item / P.half_chunks, hc = item - head * P.half_chunks;
-            if (s_dst_blk[row] >= 0) {
-                const char* p = src_rp(row) + head * P.head_bytes + hc * 16;
-                lo[k] = ld16(p);
-                hi[k] = ld16(p + P.half_bytes);
+            if (!src_in_pool || s_src_blk[row] >= 0) {
+                const int head = item / P.half_chunks, hc = item - head * P.half_chunks;
+                rp_row[k] = row;
+                rp_off[k] = head * P.head_bytes + hc * 16;
+                const char* p = src_in_pool
+                    ? srp + (int64_t)s_src_blk[row] * P.rp_b + (int64_t)s_src_row[row] * P.rp_r
+                    : srp + (int64_t)(r0 + row) * I.src.rp_r;
+                lo[k] = ld16(p + rp_off[k]);
+                hi[k] = ld16(p + rp_off[k] + P.half_bytes);
             }
         }
     }
 
-    if (MODE == kSplice) {
-        wait_loads();
-        __syncthreads();                 // every source row of this tile is in registers
-        if (is_move && tid == 0)
-            st_dev(A.flags + (I.wg_off + layer * I.tiles) + t, A.epoch);
+    // ---- while the rows are in flight: destination rows, angle table -------
+    if (tid < nrows) {
+        const bool ok = (unsigned)my_db < nb;
+        if (!ok) raise_error(KVR_DEV_BAD_BLOCK);
+        s_dst_blk[tid] = ok ? my_db : -1;
+        s_dst_row[tid] = in_block(dslot0 + tid);
     }
+    if (rotate) angle_table(s_cs, A.omega, P.n_pairs, I.shift, tid);
+
+    if (MODE == kSplice) wait_loads();
+    __syncthreads();                     // destination rows and angle table ready;
+                                         // splice: every source row is in registers
+    if (MODE == kSplice && is_move && tid == 0)
+        st_dev(A.flags + (I.wg_off + layer * I.tiles) + t, A.epoch);
 
     // ---- rotation (fp32, round to nearest even on store) -------------------
     if (rotate) {
 #pragma unroll
         for (int k = 0; k < RS; ++k) {
-            const int q = tid + k * kThreads;
-            if (q < rp_total) {
-                const int row = q / ri, item = q - row * ri;
+            if (rp_row[k] >= 0) {
+                const int q = tid + k * kThreads;
+                const int item = q % ri;
                 const int hc = item % P.half_chunks;
                 const float2* cs = s_cs + hc * P.pairs_per_chunk;
                 if (RF32) rot_f32x4(lo[k], hi[k], cs);
@@ -226,29 +251,20 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
 
     // ---- stores -----------------------------------------------------------
     const int64_t dpf = (int64_t)layer * P.pf_l, drp = (int64_t)layer * P.rp_l;
-    {
-        int row = tid / pfc, c = tid % pfc;
 #pragma unroll
-        for (int k = 0; k < kPfItems; ++k) {
-            const int q = tid + k * kThreads;
-            if (q < pf_total && s_dst_blk[row] >= 0)
-                st16(P.pf + dpf + (int64_t)s_dst_blk[row] * P.pf_b + (int64_t)s_dst_row[row] * P.pf_r + c * 16, pv[k]);
-            row += step_row; c += step_c;
-            if (c >= pfc) { c -= pfc; ++row; }
-        }
+    for (int k = 0; k < PFI; ++k) {
+        const int row = pf_row[k];
+        if (row >= 0 && s_dst_blk[row] >= 0)
+            st16(P.pf + dpf + (int64_t)s_dst_blk[row] * P.pf_b + (int64_t)s_dst_row[row] * P.pf_r + pf_c[k] * 16,
+                 pv[k]);
     }
 #pragma unroll
     for (int k = 0; k < RS; ++k) {
-        const int q = tid + k * kThreads;
-        if (q < rp_total) {
-            const int row = q / ri, item = q - row * ri;
-            const int head = item / P.half_chunks, hc = item - head * P.half_chunks;
-            if (s_dst_blk[row] >= 0) {
-                char* p = P.rp + drp + (int64_t)s_dst_blk[row] * P.rp_b + (int64_t)s_dst_row[row] * P.rp_r +
-                          head * P.head_bytes + hc * 16;
-                st16(p, lo[k]);
-                st16(p + P.half_bytes, hi[k]);
-            }
+        const int row = rp_row[k];
+        if (row >= 0 && s_dst_blk[row] >= 0) {
+            char* p = P.rp + drp + (int64_t)s_dst_blk[row] * P.rp_b + (int64_t)s_dst_row[row] * P.rp_r + rp_off[k];
+            st16(p, lo[k]);
+            st16(p + P.half_bytes, hi[k]);
         }
     }
 }
@@ -258,30 +274,47 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
         p[i] = 0u;
 }
 
-template <int MODE>
-hipError_t launch(const RelocArgs& a, int rs, bool f32, hipStream_t s) {
-    dim3 grid(a.n_wg), block(kThreads);
-#define KVR_CASE(R)                                                                              \
-    case R:                                                                                      \
-        if (f32) hipLaunchKernelGGL((reloc_kernel<MODE, R, true>), grid, block, 0, s, a);         \
-        else     hipLaunchKernelGGL((reloc_kernel<MODE, R, false>), grid, block, 0, s, a);        \
-        break;
-    switch (rs) {
-        KVR_CASE(1)
-        KVR_CASE(2)
-        KVR_CASE(4)
-        KVR_CASE(8)
-        KVR_CASE(16)
-        default: return hipErrorInvalidValue;
-    }
-#undef KVR_CASE
+template <int MODE, int PFI, int RS>
+hipError_t launch_one(const RelocArgs& a, bool f32, hipStream_t s) {
+    if (f32) hipLaunchKernelGGL((reloc_kernel<MODE, PFI, RS, true>), dim3(a.n_wg), dim3(kThreads), 0, s, a);
+    else     hipLaunchKernelGGL((reloc_kernel<MODE, PFI, RS, false>), dim3(a.n_wg), dim3(kThreads), 0, s, a);
     return hipGetLastError();
+}
+
+// Instantiated shapes: (PFI, RS) with RS <= PFI for every power of two up to
+// 16 (the host picks PFI >= RS).
+template <int MODE, int PFI>
+hipError_t launch_rs(const RelocArgs& a, int rs, bool f32, hipStream_t s) {
+    switch (rs) {
+        case 1: return launch_one<MODE, PFI, 1>(a, f32, s);
+        case 2: if (PFI >= 2) return launch_one<MODE, PFI, (PFI >= 2 ? 2 : 1)>(a, f32, s); break;
+        case 4: if (PFI >= 4) return launch_one<MODE, PFI, (PFI >= 4 ? 4 : 1)>(a, f32, s); break;
+        case 8: if (PFI >= 8) return launch_one<MODE, PFI, (PFI >= 8 ? 8 : 1)>(a, f32, s); break;
+        case 16: if (PFI >= 16) return launch_one<MODE, PFI, 16>(a, f32, s); break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int MODE>
+hipError_t launch(const RelocArgs& a, int pfi, int rs, bool f32, hipStream_t s) {
+    switch (pfi) {
+        case 1: return launch_rs<MODE, 1>(a, rs, f32, s);
+        case 2: return launch_rs<MODE, 2>(a, rs, f32, s);
+        case 4: return launch_rs<MODE, 4>(a, rs, f32, s);
+        case 8: return launch_rs<MODE, 8>(a, rs, f32, s);
+        case 16: return launch_rs<MODE, 16>(a, rs, f32, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_splice(const RelocArgs& a, int rs, bool f32, hipStream_t s) { return launch<kSplice>(a, rs, f32, s); }
-hipError_t launch_gather(const RelocArgs& a, int rs, bool f32, hipStream_t s) { return launch<kGather>(a, rs, f32, s); }
+hipError_t launch_splice(const RelocArgs& a, int pfi, int rs, bool f32, hipStream_t s) {
+    return launch<kSplice>(a, pfi, rs, f32, s);
+}
+hipError_t launch_gather(const RelocArgs& a, int pfi, int rs, bool f32, hipStream_t s) {
+    return launch<kGather>(a, pfi, rs, f32, s);
+}
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
     size_t n = bytes / 4;
