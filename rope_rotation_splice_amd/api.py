@@ -105,6 +105,8 @@ class LowRank:
 
     def c(self):
         r = int(self.U.shape[-1])
+        if self.U.numel() == 0:
+            return kvr_lowrank()          # no rows to patch
         if not (self.U.is_contiguous() and self.V.is_contiguous()) or self.U.dtype != torch.float32:
             raise ValueError("factors must be contiguous float32")
         return kvr_lowrank(self.U.data_ptr(), self.U.stride(0), self.V.data_ptr(), self.V.stride(0), r, 0)

@@ -217,6 +217,68 @@ kvr_status plan_splice(const kvr_cache* c, int32_t bt_stride, int32_t n_seq, con
     return KVR_OK;
 }
 
+
+// ------------------------------------------------------------------- patch --
+
+constexpr int kPatchTileRows = 64;       // tokens per workgroup on the patch path (4 x 16)
+
+// The fused patch path needs bf16 parts, 32-feature groups, rotary heads made
+// of whole 32-feature halves, and rope_dim / 2 <= kPatchMaxPairs.
+kvr_status check_patch_cache(const kvr_cache* c) {
+    if (c->pf_dtype != KVR_BF16 || c->rope_dtype != KVR_BF16) return KVR_E_UNSUPPORTED;
+    if (c->pf_width % 32 || c->rope_dim % 64 || c->rope_dim / 2 > kPatchMaxPairs) return KVR_E_UNSUPPORTED;
+    return KVR_OK;
+}
+
+kvr_status check_lowrank(const kvr_lowrank* f, int64_t len, int32_t width) {
+    (void)width;
+    if (!f || f->rank == 0 || len == 0) return KVR_OK;
+    if (f->rank < 0 || f->rank > 64 || (f->rank % 4)) return KVR_E_ARG;
+    if (!f->U || !f->V || !aligned16(f->U) || !aligned16(f->V)) return KVR_E_ARG;
+    if (f->u_layer_stride < 0 || f->v_layer_stride < 0 || (f->u_layer_stride % 4) || (f->v_layer_stride % 4))
+        return KVR_E_ARG;
+    return KVR_OK;
+}
+
+void set_factors(const kvr_lowrank* f, const float*& U, const float*& V, int64_t& ul, int64_t& vl, int32_t& rank) {
+    if (f && f->rank > 0) {
+        U = f->U; V = f->V; ul = f->u_layer_stride; vl = f->v_layer_stride; rank = f->rank;
+    } else {
+        U = nullptr; V = nullptr; ul = vl = 0; rank = 0;
+    }
+}
+
+// Enqueue patch-kernel launches for `items` (at most kPatchMaxItems each).
+kvr_status run_patch(const Pool& pool, const double* omega, const int32_t* d_bt, std::vector<PatchItem>& items,
+                     int n_layers, bool inplace, bool do_rope, bool do_pf, hipStream_t stream) {
+    size_t i = 0;
+    while (i < items.size()) {
+        PatchArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.pool = pool;
+        a.bt = d_bt;
+        a.tile_rows = kPatchTileRows;
+        a.do_rope = do_rope;
+        a.do_pf = do_pf;
+        std::memcpy(a.omega, omega, sizeof(a.omega));
+        int64_t wg = 0;
+        int n = 0;
+        for (; i < items.size() && n < kPatchMaxItems; ++i) {
+            PatchItem it = items[i];
+            const int64_t add = (int64_t)it.tiles * n_layers;
+            if (n > 0 && wg + add >= ((int64_t)1 << 31)) break;
+            it.wg_off = (int32_t)wg;
+            wg += add;
+            a.items[n++] = it;
+        }
+        a.n_items = n;
+        a.n_wg = (int32_t)wg;
+        hipError_t e = launch_patch(a, inplace, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return KVR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -244,9 +306,10 @@ kvr_status kvr_device_errors(uint32_t* flags) {
     if (!flags) return KVR_E_ARG;
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e);
-    uint32_t v = read_and_clear_errors_relocate();
-    if (v == 0xffffffffu) return hip_fail(hipErrorUnknown);
-    *flags = v;
+    const uint32_t v = read_and_clear_errors_relocate();
+    const uint32_t w = read_and_clear_errors_patch();
+    if (v == 0xffffffffu || w == 0xffffffffu) return hip_fail(hipErrorUnknown);
+    *flags = v | w;
     return KVR_OK;
 }
 
@@ -349,7 +412,33 @@ kvr_status kv_relocate_gather(const kvr_cache* dst, const int32_t* d_block_table
         if (patch_rope && patch_rope[i].rank) any_patch = true;
         if (patch_pf && patch_pf[i].rank) any_patch = true;
     }
-    if (any_patch) return KVR_E_UNSUPPORTED;
+    if (any_patch) {
+        st = check_patch_cache(dst);
+        if (st != KVR_OK) return st;
+        for (int32_t i = 0; i < n; ++i) {
+            st = check_lowrank(patch_rope ? &patch_rope[i] : nullptr, entries[i].len, dst->rope_heads * dst->rope_dim);
+            if (st != KVR_OK) return st;
+            st = check_lowrank(patch_pf ? &patch_pf[i] : nullptr, entries[i].len, dst->pf_width);
+            if (st != KVR_OK) return st;
+        }
+        std::vector<PatchItem> items;
+        for (int32_t i = 0; i < n; ++i) {
+            if (entries[i].len == 0) continue;
+            PatchItem it{};
+            const SrcRows s = src_rows(entries[i], dst);
+            it.src_pf = s.pf; it.src_rp = s.rp;
+            it.src_pf_l = s.pf_l; it.src_rp_l = s.rp_l;
+            it.src_pf_r = s.pf_r; it.src_rp_r = s.rp_r;
+            set_factors(patch_rope ? &patch_rope[i] : nullptr, it.U_rp, it.V_rp, it.u_rp_l, it.v_rp_l, it.rank_rp);
+            set_factors(patch_pf ? &patch_pf[i] : nullptr, it.U_pf, it.V_pf, it.u_pf_l, it.v_pf_l, it.rank_pf);
+            it.dst0 = (int32_t)p_target[i];
+            it.shift = (int32_t)(p_target[i] - entries[i].base_pos);
+            it.len = (int32_t)entries[i].len;
+            it.tiles = (it.len + kPatchTileRows - 1) / kPatchTileRows;
+            items.push_back(it);
+        }
+        return run_patch(pool, omega, d_block_table, items, dst->n_layers, false, true, true, stream);
+    }
 
     const TileShape tile = choose_tile(pool, dst->rope_dtype == KVR_F32, false);
     const int T = tile.T;
@@ -393,9 +482,42 @@ kvr_status kv_relocate_gather(const kvr_cache* dst, const int32_t* d_block_table
     return flush();
 }
 
-kvr_status kv_patch_lowrank(const kvr_cache*, const int32_t*, int32_t, int32_t, const int64_t*,
-                            const int64_t*, const kvr_lowrank*, int32_t, hipStream_t) {
-    return KVR_E_UNSUPPORTED;
+kvr_status kv_patch_lowrank(const kvr_cache* cache, const int32_t* d_block_table, int32_t bt_len, int32_t part,
+                            const int64_t* p_start, const int64_t* len, const kvr_lowrank* f, int32_t n,
+                            hipStream_t stream) {
+    Pool pool;
+    double omega[kMaxPairs];
+    kvr_status st = make_pool(cache, pool, omega);
+    if (st != KVR_OK) return st;
+    if (!d_block_table || (reinterpret_cast<uintptr_t>(d_block_table) & 3u) || bt_len < 1 || n < 0) return KVR_E_ARG;
+    if (part != 0 && part != 1) return KVR_E_ARG;
+    if (n > 0 && (!p_start || !len || !f)) return KVR_E_ARG;
+    st = check_patch_cache(cache);
+    if (st != KVR_OK) return st;
+    const int64_t capacity = (int64_t)bt_len * cache->block_size;
+    if (capacity >= (int64_t)1 << 31) return KVR_E_ARG;
+    std::vector<std::pair<int64_t, int64_t>> rng;
+    for (int32_t i = 0; i < n; ++i) {
+        if (len[i] < 0 || p_start[i] < 0 || p_start[i] + len[i] > capacity) return KVR_E_RANGE;
+        st = check_lowrank(&f[i], len[i], part ? cache->rope_heads * cache->rope_dim : cache->pf_width);
+        if (st != KVR_OK) return st;
+        if (len[i] > 0) rng.push_back({p_start[i], p_start[i] + len[i]});
+    }
+    std::sort(rng.begin(), rng.end());
+    for (size_t i = 1; i < rng.size(); ++i)
+        if (rng[i].first < rng[i - 1].second) return KVR_E_OVERLAP;
+    std::vector<PatchItem> items;
+    for (int32_t i = 0; i < n; ++i) {
+        if (len[i] == 0 || f[i].rank == 0) continue;
+        PatchItem it{};
+        if (part == 1) set_factors(&f[i], it.U_rp, it.V_rp, it.u_rp_l, it.v_rp_l, it.rank_rp);
+        else           set_factors(&f[i], it.U_pf, it.V_pf, it.u_pf_l, it.v_pf_l, it.rank_pf);
+        it.dst0 = (int32_t)p_start[i];
+        it.len = (int32_t)len[i];
+        it.tiles = (it.len + kPatchTileRows - 1) / kPatchTileRows;
+        items.push_back(it);
+    }
+    return run_patch(pool, omega, d_block_table, items, cache->n_layers, true, part == 1, part == 0, stream);
 }
 
 size_t kvr_decode_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }

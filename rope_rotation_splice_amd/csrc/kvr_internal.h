@@ -64,6 +64,36 @@ struct RelocArgs {
     Item items[kMaxItems];
 };
 
+// One registry entry (gather with patch) or one slot range (in-place patch).
+constexpr int kPatchMaxPairs = 64;   // rope_dim <= 128 on the patch path
+constexpr int kPatchMaxItems = 16;
+
+struct PatchItem {
+    const char* src_pf; const char* src_rp;    // entry rows (gather); unused in place
+    int64_t src_pf_l, src_rp_l;                // bytes
+    int32_t src_pf_r, src_rp_r;                // bytes
+    const float* U_rp; const float* V_rp;      // rotary-part factors (or null)
+    int64_t u_rp_l, v_rp_l;                    // layer strides, floats
+    const float* U_pf; const float* V_pf;      // position-free-part factors (or null)
+    int64_t u_pf_l, v_pf_l;
+    int32_t rank_rp, rank_pf;                  // 0 = no patch
+    int32_t dst0;                              // destination slot of row 0
+    int32_t shift;                             // rotation (gather); 0 in place
+    int32_t len;                               // rows
+    int32_t tiles;                             // tiles per layer
+    int32_t wg_off;                            // first workgroup of this item
+};
+
+struct PatchArgs {
+    Pool pool;
+    const int32_t* bt;
+    int32_t n_items, tile_rows, n_wg;
+    int32_t do_rope, do_pf;
+    double omega[kPatchMaxPairs];
+    PatchItem items[kPatchMaxItems];
+};
+static_assert(sizeof(PatchArgs) <= 4000, "patch kernel arguments too large");
+
 // Kernel arguments must stay within the 4 KB kernarg budget.
 static_assert(sizeof(RelocArgs) <= 4000, "relocation kernel arguments too large");
 
@@ -74,5 +104,8 @@ hipError_t launch_splice(const RelocArgs& a, int pf_slots, int rope_slots, bool 
 hipError_t launch_gather(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 uint32_t read_and_clear_errors_relocate();
+// Patch kernel (patch.hip): fused gather + patch, or in-place patch.
+hipError_t launch_patch(const PatchArgs& a, bool inplace, hipStream_t s);
+uint32_t read_and_clear_errors_patch();
 
 }  // namespace kvr

@@ -218,3 +218,54 @@ def check_gather(lay, before, after, block_table, block_size, entries, p_targets
         ok = rope_close(lay, rp1[rotated_rows], ref[rotated_rows], scale[rotated_rows])
         if not ok.all():
             raise Mismatch(f"rotated key outside tolerance ({(~ok).sum()} of {ok.size})")
+
+
+def check_gather_patch(lay, before, after, block_table, block_size, entries, p_targets, f_rope, f_pf):
+    """Gather with Kamera's patch: K_out = R(delta) K + U V^T, V_out = V + U' V'^T.
+
+    entries: list of (pf, rope, base_pos) images; f_rope / f_pf: per entry
+    (U [L, len, m], V [L, width, m]) float32 arrays, or None (no patch).
+    Unpatched position-free rows must be bit-exact copies.
+    """
+    from oracle import bf16 as ob, patch as opatch
+    pf0, rp0 = before
+    pf1, rp1 = after
+    L = pf0.shape[0]
+    th = lay.theta()
+    touched = np.zeros(pf0.shape[1], bool)
+    for i, ((epf, erp, base), pt) in enumerate(zip(entries, p_targets)):
+        n = epf.shape[1]
+        if n == 0:
+            continue
+        phys = osplice.physical_rows(pt + np.arange(n), block_table, block_size)
+        touched[phys] = True
+        d = ogather.chunk_delta(pt, base)
+        for l in range(L):
+            k = ob.to_f64(erp[l])
+            fr = f_rope[i] if f_rope is not None else None
+            U, V = (fr[0][l], fr[1][l]) if fr is not None else (None, None)
+            y = opatch.relocate_and_patch_keys(k, d, lay.rope_heads, lay.rope_dim, th, U, V)
+            scale = orope.pair_norms(k, lay.rope_heads, lay.rope_dim)
+            if U is not None:
+                scale = scale + opatch.patch_abs_scale(U, V)
+            if d == 0 and U is None:
+                if not np.array_equal(rp1[l][phys], erp[l]):
+                    raise Mismatch(f"entry {i} layer {l}: unrotated unpatched keys not bit-exact")
+            else:
+                ok = tolerance.bf16_close(rp1[l][phys], y, scale)
+                if not ok.all():
+                    raise Mismatch(f"entry {i} layer {l}: {(~ok).sum()} keys outside tolerance")
+            fp = f_pf[i] if f_pf is not None else None
+            if fp is None:
+                if not np.array_equal(pf1[l][phys], epf[l]):
+                    raise Mismatch(f"entry {i} layer {l}: unpatched values not bit-exact")
+            else:
+                v = ob.to_f64(epf[l])
+                y = opatch.patch_values(v, fp[0][l], fp[1][l])
+                scale = np.abs(v) + opatch.patch_abs_scale(fp[0][l], fp[1][l])
+                ok = tolerance.bf16_close(pf1[l][phys], y, scale)
+                if not ok.all():
+                    raise Mismatch(f"entry {i} layer {l}: {(~ok).sum()} values outside tolerance")
+    if not np.array_equal(pf1[:, ~touched], pf0[:, ~touched]) or \
+            not np.array_equal(bits(rp1)[:, ~touched], bits(rp0)[:, ~touched]):
+        raise Mismatch("rows outside the targets changed")
