@@ -257,6 +257,92 @@ class SpliceBatched:
                           f"generation excluded, numpy fp64, one process"}
 
 
+class GqaPatch:
+    """Kamera GQA relocation with its rank-16 patch, fused into one gather:
+    16 chunks x 1024 tokens, 32 layers, K and V of 8 x 128 bf16, delta ~
+    U{-30000..30000}, RoPE base 500000, factors fp32 N(0, 0.01^2)."""
+    name = "gqa_patch"
+    kernel = "patch_kernel<gather>"
+
+    def __init__(self):
+        import kvsynth
+        self.w = kvsynth.gqa_patch()
+        w = self.w
+        L, n = w.shape.n_layers, len(w.deltas)
+        width = w.shape.width
+        self.slots = n * w.chunk_len
+        factor_bytes = 2 * n * L * (w.chunk_len + width) * w.rank * 4
+        self.bytes = self.slots * L * width * 2 * 2 * 2 + factor_bytes
+        self.flops = 2 * 2 * n * L * w.chunk_len * width * w.rank
+        self.launches = 1
+        self.config = {"workload": "kamera_gqa_relocate_patch", "layers": L, "chunks": n, "chunk_len": w.chunk_len,
+                       "kv_heads": w.shape.heads, "head_dim": w.shape.head_dim, "rope_base": w.shape.rope_base,
+                       "delta": "U{-30000..30000}", "rank": w.rank, "factor_std": w.factor_std,
+                       "slots_per_step": self.slots, "patch_gflop": self.flops / 1e9}
+
+    def setup(self):
+        import torch
+        import kvsynth
+        import rope_rotation_splice_amd as rrs
+        w = self.w
+        L, B, width, m = w.shape.n_layers, w.block_size, w.shape.width, w.rank
+        self.K = torch.empty((L, w.n_blocks, B, width), dtype=torch.bfloat16, device="cuda")
+        self.V = torch.empty_like(self.K)
+        kvsynth.fill_normal_(self.K, 4, 1)
+        kvsynth.fill_normal_(self.V, 4, 2)
+        self.cache = rrs.KVCache.gqa(self.K, self.V, w.shape.heads, w.shape.head_dim, w.shape.rope_base)
+        self.keep, self.ents, self.fk, self.fv = [], [], [], []
+        for i in range(len(w.deltas)):
+            ek = torch.empty((L, w.chunk_len, width), dtype=torch.bfloat16, device="cuda")
+            ev = torch.empty_like(ek)
+            kvsynth.fill_normal_(ek, 4, 3, i, 0)
+            kvsynth.fill_normal_(ev, 4, 3, i, 1)
+            self.ents.append(rrs.Rows(ev, ek, int(w.base_pos[i])))
+            fac = []
+            for j in range(4):
+                shape = (L, w.chunk_len if j % 2 == 0 else width, m)
+                t = torch.empty(shape, dtype=torch.float32, device="cuda")
+                kvsynth.fill_normal_(t, 4, 4, i, j, std=w.factor_std)
+                fac.append(t)
+            self.fk.append(rrs.LowRank(fac[0], fac[1]))
+            self.fv.append(rrs.LowRank(fac[2], fac[3]))
+            self.keep += [ek, ev] + fac
+        self.bt = torch.from_numpy(w.block_table).cuda()
+        self.pt = w.p_target.tolist()
+        self.rrs = rrs
+
+    def step(self):
+        self.rrs.kv_relocate_gather(self.cache, self.bt, self.ents, self.pt, self.fk, self.fv)
+
+    def cpu_baseline(self, budget_s):
+        import kvsynth
+        from oracle import patch as opatch, rope as orope, bf16 as ob
+        w = self.w
+        th = orope.inv_freq(w.shape.head_dim, w.shape.rope_base)
+        rows, spent, units = 0, 0.0, 0
+        for i in range(len(w.deltas)):
+            r = kvsynth.rng(4, 9, i)
+            for l in range(w.shape.n_layers):
+                k = ob.to_f64(kvsynth.bf16_normal(r, (w.chunk_len, w.shape.width)))
+                v = ob.to_f64(kvsynth.bf16_normal(r, (w.chunk_len, w.shape.width)))
+                U = kvsynth.f32_normal(r, (w.chunk_len, w.rank), w.factor_std)
+                V = kvsynth.f32_normal(r, (w.shape.width, w.rank), w.factor_std)
+                t0 = time.perf_counter()
+                opatch.relocate_and_patch_keys(k, int(w.deltas[i]), w.shape.heads, w.shape.head_dim, th, U, V)
+                opatch.patch_values(v, U, V)
+                spent += time.perf_counter() - t0
+                rows += w.chunk_len
+                units += 1
+                if spent >= budget_s:
+                    break
+            if spent >= budget_s:
+                break
+        slots = rows / w.shape.n_layers
+        return {"value": slots / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
+                "sample": f"{units} (chunk, layer) units ({rows} layer-rows, K and V), generation excluded, "
+                          f"numpy fp64 (matmul through numpy's BLAS, single-threaded here)"}
+
+
 class Copy:
     """A plain device-to-device copy of the registry gather's byte volume
     (torch's copy kernel): the practical read+write ceiling, and the known-size
@@ -284,7 +370,8 @@ class Copy:
         return None
 
 
-WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "copy": Copy}
+WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "gqa_patch": GqaPatch,
+             "copy": Copy}
 
 
 def main():
@@ -336,6 +423,11 @@ def main():
     bytes_per_launch = wl.bytes / wl.launches
     achieved = bytes_per_launch / kernel_s / 1e9
     traffic = stored_traffic(wl.kernel, wl.name)
+    extra = {}
+    if getattr(wl, "flops", None):
+        extra["matrix_core"] = {"dtype": "fp32", "achieved_TFLOPs": wl.flops * args.steps / gpu_s / 1e12,
+                                "peak_TFLOPs": 157.3,
+                                "frac": wl.flops * args.steps / gpu_s / 1e12 / 157.3}
     out = {
         "metric": METRIC,
         "value": wl.slots * args.steps / wall,
@@ -357,6 +449,7 @@ def main():
                      "avg_launch_us": kernel_s * 1e6},
         "cpu_baseline": cpu,
     }
+    out.update(extra)
     print(json.dumps(out))
     return 0
 

@@ -220,13 +220,12 @@ kvr_status plan_splice(const kvr_cache* c, int32_t bt_stride, int32_t n_seq, con
 
 // ------------------------------------------------------------------- patch --
 
-constexpr int kPatchTileRows = 64;       // tokens per workgroup on the patch path (4 x 16)
-
-// The fused patch path needs bf16 parts, 32-feature groups, rotary heads made
-// of whole 32-feature halves, and rope_dim / 2 <= kPatchMaxPairs.
+// The fused patch path needs bf16 parts, position-free rows of whole 64-feature
+// (128-byte) pairs of groups, rotary heads made of whole 32-feature halves,
+// and rope_dim / 2 <= kPatchMaxPairs.
 kvr_status check_patch_cache(const kvr_cache* c) {
     if (c->pf_dtype != KVR_BF16 || c->rope_dtype != KVR_BF16) return KVR_E_UNSUPPORTED;
-    if (c->pf_width % 32 || c->rope_dim % 64 || c->rope_dim / 2 > kPatchMaxPairs) return KVR_E_UNSUPPORTED;
+    if (c->pf_width % 64 || c->rope_dim % 64 || c->rope_dim / 2 > kPatchMaxPairs) return KVR_E_UNSUPPORTED;
     return KVR_OK;
 }
 

@@ -66,6 +66,7 @@ struct RelocArgs {
 
 // One registry entry (gather with patch) or one slot range (in-place patch).
 constexpr int kPatchMaxPairs = 64;   // rope_dim <= 128 on the patch path
+constexpr int kPatchTileRows = 64;   // tokens per workgroup on the patch path (4 x 16)
 constexpr int kPatchMaxItems = 16;
 
 struct PatchItem {

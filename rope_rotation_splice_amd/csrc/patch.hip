@@ -143,76 +143,168 @@ __global__ __launch_bounds__(kThreads) void patch_kernel(const PatchArgs A) {
     __syncthreads();
 
     const int tok = lane & 15, g = lane >> 4;
-    const int n_sub = (nrows + 15) >> 4;
     const int64_t lpf = (int64_t)layer * P.pf_l, lrp = (int64_t)layer * P.rp_l;
 
-    // ---- rotary part: units = (head, lo group) ------------------------------
+    // Work of a wave: whole rotary heads (every 32-feature group of the head,
+    // so the two 64-byte halves of each 128-byte line are read and written by
+    // the same wave in consecutive instructions) and pairs of position-free
+    // groups (128 bytes).  Sub-tiles of 16 tokens are taken two at a time:
+    // all their loads are issued before the matrix cores run.  For rank <= 16
+    // (one K block) the U rows of this lane's token stay in registers for the
+    // whole tile and each group's factor rows are loaded once per unit; larger
+    // ranks walk the K blocks with operand reloads (group_patch).
+    constexpr int NS = kPatchTileRows / 16;
+    constexpr int NB = 2;                      // sub-tiles per batch
+    constexpr int MAXG = 4;                    // groups per unit (a 128-dim head)
+
+    auto load_u = [&](const float* Ul, int rank, v4f* ub) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int row = s * 16 + tok;
+            ub[s] = v4f{0, 0, 0, 0};
+            if (row < nrows && 4 * g < rank) ub[s] = *reinterpret_cast<const v4f*>(Ul + (int64_t)(r0 + row) * rank + 4 * g);
+        }
+    };
+    auto load_f = [&](const float* Vl, int f0, int rank, v4f& fa, v4f& fb) {
+        fa = v4f{0, 0, 0, 0};
+        fb = fa;
+        if (4 * g < rank) {
+            const int fr = f0 + 8 * (tok >> 2) + (tok & 3);
+            fa = *reinterpret_cast<const v4f*>(Vl + (int64_t)fr * rank + 4 * g);
+            fb = *reinterpret_cast<const v4f*>(Vl + (int64_t)(fr + 4) * rank + 4 * g);
+        }
+    };
+    auto mfma16 = [&](v4f fa, v4f fb, v4f u, v4f& pa, v4f& pb) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            pa = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[kk], u[kk], pa, 0, 0, 0);
+            pb = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[kk], u[kk], pb, 0, 0, 0);
+        }
+    };
+
+    // ---- rotary part: units = heads -----------------------------------------
     if (A.do_rope) {
-        const int gph = P.head_bytes / 64;           // 32-feature groups per head (bf16: 64 B each)
-        const int half_groups = gph / 2;
-        const int units = (P.rope_items / P.half_chunks) * half_groups;   // heads * half_groups
+        const int gph = P.head_bytes / 64;           // 32-feature groups per head (2 or 4)
+        const int hg = gph / 2;                      // groups per half head
+        const int heads = P.rope_items / P.half_chunks;
         const float* Ul = I.U_rp ? I.U_rp + (int64_t)layer * I.u_rp_l : nullptr;
         const float* Vl = I.V_rp ? I.V_rp + (int64_t)layer * I.v_rp_l : nullptr;
         const int rank = I.rank_rp;
-        for (int u = wave; u < units; u += kThreads / 64) {
-            const int head = u / half_groups, gl = u - head * half_groups;
-            const int f_lo = head * (gph * 32) + gl * 32;           // first feature of the lo group
-            const int f_hi = f_lo + half_groups * 32;
-            const int byte_lo = head * P.head_bytes + gl * 64 + g * 16;
-            const float2* cs = s_cs + gl * 32 + g * 8;
-            for (int s = 0; s < n_sub; ++s) {
-                const int row = s * 16 + tok;
-                const bool live = row < nrows && s_blk[row] >= 0;
-                v4u lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-                char* dst = nullptr;
-                if (live) {
-                    dst = P.rp + lrp + (int64_t)s_blk[row] * P.rp_b + (int64_t)s_row[row] * P.rp_r + byte_lo;
-                    const char* src = INPLACE ? dst
-                                              : I.src_rp + (int64_t)layer * I.src_rp_l + (int64_t)(r0 + row) * I.src_rp_r + byte_lo;
-                    lo = ld16(src);
-                    hi = ld16(src + P.half_bytes);
+        const bool small = rank > 0 && rank <= 16;
+        v4f ub[NS];
+        if (small) load_u(Ul, rank, ub);
+        for (int head = wave; head < heads; head += kThreads / 64) {
+            const int f_head = head * gph * 32;
+            v4f fa[MAXG], fb[MAXG];
+            if (small) {
+#pragma unroll
+                for (int gi = 0; gi < MAXG; ++gi)
+                    if (gi < gph) load_f(Vl, f_head + gi * 32, rank, fa[gi], fb[gi]);
+            }
+#pragma unroll
+            for (int sb = 0; sb < NS; sb += NB) {
+                if (sb * 16 >= nrows) break;
+                v4u x[NB][MAXG];
+                char* dst[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int row = (sb + b) * 16 + tok;
+                    dst[b] = nullptr;
+                    if (row < nrows && s_blk[row] >= 0) {
+                        dst[b] = P.rp + lrp + (int64_t)s_blk[row] * P.rp_b + (int64_t)s_row[row] * P.rp_r +
+                                 head * P.head_bytes + g * 16;
+                        const char* src = INPLACE ? dst[b]
+                                                  : I.src_rp + (int64_t)layer * I.src_rp_l +
+                                                        (int64_t)(r0 + row) * I.src_rp_r + head * P.head_bytes + g * 16;
+#pragma unroll
+                        for (int gi = 0; gi < MAXG; ++gi)
+                            if (gi < gph) x[b][gi] = ld16(src + gi * 64);
+                    }
                 }
-                v4f pla = {0, 0, 0, 0}, plb = pla, pha = pla, phb = pla;
-                if (rank > 0) {
-                    const float* Ut = live ? Ul + (int64_t)(r0 + row) * rank : nullptr;
-                    group_patch(Vl + (int64_t)f_lo * rank, Ut, rank, lane, pla, plb);
-                    group_patch(Vl + (int64_t)f_hi * rank, Ut, rank, lane, pha, phb);
-                }
-                if (live && (rotate || rank > 0 || !INPLACE)) {
-                    rot_patch(lo, hi, cs, rotate, rank > 0, pla, plb, pha, phb);
-                    st16(dst, lo);
-                    st16(dst + P.half_bytes, hi);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int s = sb + b;
+                    if (s * 16 >= nrows) break;
+#pragma unroll
+                    for (int gl = 0; gl < MAXG / 2; ++gl) {
+                        if (gl >= hg) break;
+                        // hi group of this pair: gl + hg (hg is 1 or 2; indices stay compile-time)
+                        const int gh = gl + hg;
+                        v4f pla = {0, 0, 0, 0}, plb = pla, pha = pla, phb = pla;
+                        if (small) {
+                            mfma16(fa[gl], fb[gl], ub[s], pla, plb);
+                            mfma16(hg == 1 ? fa[gl + 1] : fa[gl + 2], hg == 1 ? fb[gl + 1] : fb[gl + 2], ub[s], pha, phb);
+                        } else if (rank > 0) {
+                            const int row = s * 16 + tok;
+                            const float* Ut = (row < nrows) ? Ul + (int64_t)(r0 + row) * rank : nullptr;
+                            group_patch(Vl + (int64_t)(f_head + gl * 32) * rank, Ut, rank, lane, pla, plb);
+                            group_patch(Vl + (int64_t)(f_head + gh * 32) * rank, Ut, rank, lane, pha, phb);
+                        }
+                        if (dst[b] && (rotate || rank > 0 || !INPLACE)) {
+                            v4u lo = x[b][gl], hi = hg == 1 ? x[b][gl + 1] : x[b][gl + 2];
+                            rot_patch(lo, hi, s_cs + gl * 32 + g * 8, rotate, rank > 0, pla, plb, pha, phb);
+                            st16(dst[b] + gl * 64, lo);
+                            st16(dst[b] + gh * 64, hi);
+                        }
+                    }
                 }
             }
         }
     }
 
-    // ---- position-free part: units = 32-feature groups ----------------------
+    // ---- position-free part: units = pairs of 32-feature groups (128 B) ------
     if (A.do_pf) {
-        const int groups = P.pf_chunks / 4;
+        const int pairs = P.pf_chunks / 8;
         const float* Ul = I.U_pf ? I.U_pf + (int64_t)layer * I.u_pf_l : nullptr;
         const float* Vl = I.V_pf ? I.V_pf + (int64_t)layer * I.v_pf_l : nullptr;
         const int rank = I.rank_pf;
-        for (int q = wave; q < groups; q += kThreads / 64) {
-            const int byte = q * 64 + g * 16;
-            for (int s = 0; s < n_sub; ++s) {
-                const int row = s * 16 + tok;
-                const bool live = row < nrows && s_blk[row] >= 0;
-                v4u x = {0, 0, 0, 0};
-                char* dst = nullptr;
-                if (live) {
-                    dst = P.pf + lpf + (int64_t)s_blk[row] * P.pf_b + (int64_t)s_row[row] * P.pf_r + byte;
-                    const char* src = INPLACE ? dst
-                                              : I.src_pf + (int64_t)layer * I.src_pf_l + (int64_t)(r0 + row) * I.src_pf_r + byte;
-                    x = ld16(src);
+        const bool small = rank > 0 && rank <= 16;
+        v4f ub[NS];
+        if (small) load_u(Ul, rank, ub);
+        for (int q = wave; q < pairs; q += kThreads / 64) {
+            v4f fa[2], fb[2];
+            if (small) {
+                load_f(Vl, q * 64, rank, fa[0], fb[0]);
+                load_f(Vl, q * 64 + 32, rank, fa[1], fb[1]);
+            }
+#pragma unroll
+            for (int sb = 0; sb < NS; sb += NB) {
+                if (sb * 16 >= nrows) break;
+                v4u x[NB][2];
+                char* dst[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int row = (sb + b) * 16 + tok;
+                    dst[b] = nullptr;
+                    if (row < nrows && s_blk[row] >= 0) {
+                        dst[b] = P.pf + lpf + (int64_t)s_blk[row] * P.pf_b + (int64_t)s_row[row] * P.pf_r + q * 128 + g * 16;
+                        const char* src = INPLACE ? dst[b]
+                                                  : I.src_pf + (int64_t)layer * I.src_pf_l +
+                                                        (int64_t)(r0 + row) * I.src_pf_r + q * 128 + g * 16;
+                        x[b][0] = ld16(src);
+                        x[b][1] = ld16(src + 64);
+                    }
                 }
-                if (rank > 0) {
-                    v4f pa = {0, 0, 0, 0}, pb = pa;
-                    const float* Ut = live ? Ul + (int64_t)(r0 + row) * rank : nullptr;
-                    group_patch(Vl + (int64_t)(q * 32) * rank, Ut, rank, lane, pa, pb);
-                    if (live) st16(dst, add_patch(x, pa, pb));
-                } else if (live && !INPLACE) {
-                    st16(dst, x);                      // no patch: bit-exact copy
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int s = sb + b;
+                    if (s * 16 >= nrows) break;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        if (rank > 0) {
+                            v4f pa = {0, 0, 0, 0}, pb = pa;
+                            if (small) {
+                                mfma16(fa[h], fb[h], ub[s], pa, pb);
+                            } else {
+                                const int row = s * 16 + tok;
+                                const float* Ut = (row < nrows) ? Ul + (int64_t)(r0 + row) * rank : nullptr;
+                                group_patch(Vl + (int64_t)(q * 64 + h * 32) * rank, Ut, rank, lane, pa, pb);
+                            }
+                            if (dst[b]) st16(dst[b] + h * 64, add_patch(x[b][h], pa, pb));
+                        } else if (dst[b] && !INPLACE) {
+                            st16(dst[b] + h * 64, x[b][h]);      // no patch: bit-exact copy
+                        }
+                    }
                 }
             }
         }

@@ -114,3 +114,49 @@ def test_patch_in_place(part):
             ok = tolerance.bf16_close(after[l][phys], y, np.abs(x) + opatch.patch_abs_scale(U[l], V[l]))
             assert ok.all(), f"range {p} layer {l}: {(~ok).sum()} outside tolerance"
     assert np.array_equal(after[:, ~touched], before[:, ~touched])
+
+
+def test_gqa_patch_workload_sampled():
+    """The full GQA workload (32 layers, 16 chunks x 1024 tokens, rank 16,
+    factors N(0, 0.01^2)) in the launch configuration the benchmark times;
+    layers 0, 17 and 31 of every chunk are compared in full with the oracle."""
+    import torch
+    import rope_rotation_splice_amd as rrs
+    w = kvsynth.gqa_patch()
+    lay = rc.GQA
+    L, B, width, m = w.shape.n_layers, w.block_size, w.shape.width, w.rank
+    K = torch.empty((L, w.n_blocks, B, width), dtype=torch.bfloat16, device="cuda")
+    V = torch.empty_like(K)
+    kvsynth.fill_normal_(K, 4, 1)
+    kvsynth.fill_normal_(V, 4, 2)
+    cache = rrs.KVCache.gqa(K, V, 8, 128, 500000.0)
+    ents, fk, fv, keep = [], [], [], []
+    for i in range(len(w.deltas)):
+        ek = torch.empty((L, w.chunk_len, width), dtype=torch.bfloat16, device="cuda")
+        ev = torch.empty_like(ek)
+        kvsynth.fill_normal_(ek, 4, 3, i, 0)
+        kvsynth.fill_normal_(ev, 4, 3, i, 1)
+        fac = []
+        for j in range(4):
+            t = torch.empty((L, w.chunk_len if j % 2 == 0 else width, m), dtype=torch.float32, device="cuda")
+            kvsynth.fill_normal_(t, 4, 4, i, j, std=w.factor_std)
+            fac.append(t)
+        ents.append(rrs.Rows(ev, ek, int(w.base_pos[i])))
+        fk.append(rrs.LowRank(fac[0], fac[1]))
+        fv.append(rrs.LowRank(fac[2], fac[3]))
+        keep.append((ek, ev, fac))
+    layers = (0, 17, 31)
+    h16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    before_k = {l: h16(K[l]).reshape(-1, width) for l in layers}
+    before_v = {l: h16(V[l]).reshape(-1, width) for l in layers}
+    rrs.kv_relocate_gather(cache, torch.from_numpy(w.block_table).cuda(), ents, w.p_target.tolist(), fk, fv)
+    torch.cuda.synchronize()
+    assert rrs.device_errors() == 0
+    for l in layers:
+        ak = h16(K[l]).reshape(-1, width)
+        av = h16(V[l]).reshape(-1, width)
+        entries = [(h16(ev[l])[None], h16(ek[l])[None], int(w.base_pos[i])) for i, (ek, ev, _) in enumerate(keep)]
+        fr = [(f[0][l:l + 1].cpu().numpy(), f[1][l:l + 1].cpu().numpy()) for (_, _, f) in keep]
+        fp = [(f[2][l:l + 1].cpu().numpy(), f[3][l:l + 1].cpu().numpy()) for (_, _, f) in keep]
+        rc.check_gather_patch(lay, (before_v[l][None], before_k[l][None]), (av[None], ak[None]), w.block_table, B,
+                              entries, w.p_target.tolist(), fr, fp)
