@@ -71,6 +71,7 @@ typedef int32_t kvr_status;
 #define KVR_DEV_BAD_BLOCK   1u  /* a block-table entry was outside [0, n_blocks) */
 #define KVR_DEV_SPIN_LIMIT  2u  /* a splice ordering wait hit its bound (workspace misuse) */
 #define KVR_DEV_BAD_TICKET  4u  /* a splice ticket was out of range (workspace not zeroed) */
+#define KVR_DEV_RANGE       8u  /* decode: scores kept outgrowing the softmax headroom (2^48) */
 
 /* Directive modes m (Leyline 2.1). */
 #define KVR_AMORTIZE 0
@@ -240,7 +241,7 @@ kvr_status kv_patch_lowrank(const kvr_cache* cache, const int32_t* d_block_table
  *   d_seq_lens     : device int32 [batch]; max_seq_len (host) bounds them
  *   out            : device bf16 [batch][heads][512]; lse : device f32 [batch][heads]
  *   d_workspace    : kvr_decode_workspace_bytes() bytes, 256-byte aligned
- * heads must be a multiple of 16 and <= 128.
+ * heads must be 32, 64, 96 or 128; the cache's block_size must be 64.
  * Errors: KVR_E_ARG, KVR_E_RANGE, KVR_E_WORKSPACE, KVR_E_UNSUPPORTED, KVR_E_HIP.
  * ---------------------------------------------------------------------- */
 size_t kvr_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t max_seq_len);

@@ -307,8 +307,9 @@ kvr_status kvr_device_errors(uint32_t* flags) {
     if (e != hipSuccess) return hip_fail(e);
     const uint32_t v = read_and_clear_errors_relocate();
     const uint32_t w = read_and_clear_errors_patch();
-    if (v == 0xffffffffu || w == 0xffffffffu) return hip_fail(hipErrorUnknown);
-    *flags = v | w;
+    const uint32_t x = read_and_clear_errors_decode();
+    if (v == 0xffffffffu || w == 0xffffffffu || x == 0xffffffffu) return hip_fail(hipErrorUnknown);
+    *flags = v | w | x;
     return KVR_OK;
 }
 
@@ -519,12 +520,75 @@ kvr_status kv_patch_lowrank(const kvr_cache* cache, const int32_t* d_block_table
     return run_patch(pool, omega, d_block_table, items, cache->n_layers, true, part == 1, part == 0, stream);
 }
 
-size_t kvr_decode_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }
+// Splits per sequence: enough workgroups to cover the 256 compute units,
+// at most kDecMaxBlocks KV blocks per split.
+static void decode_split(int32_t batch, int32_t max_seq_len, int32_t& n_split, int32_t& bps) {
+    const int32_t blocks = std::max(1, (max_seq_len + kDecBlockTokens - 1) / kDecBlockTokens);
+    n_split = std::max<int32_t>(1, (256 + batch - 1) / std::max(1, batch));
+    n_split = std::max(n_split, (blocks + kDecMaxBlocks - 1) / kDecMaxBlocks);
+    n_split = std::min(n_split, blocks);
+    bps = (blocks + n_split - 1) / n_split;
+    n_split = (blocks + bps - 1) / bps;
+}
 
-kvr_status mla_decode_rotate_on_read(const void*, const void*, int32_t, int32_t, const kvr_cache*, int32_t,
-                                     const int32_t*, const int32_t*, int32_t, const int32_t*, int32_t, float,
-                                     void*, float*, void*, size_t, hipStream_t) {
-    return KVR_E_UNSUPPORTED;
+size_t kvr_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t max_seq_len) {
+    if (batch < 1 || heads < 32 || heads % 32 || heads > 128 || max_seq_len < 0) return 0;
+    int32_t n_split, bps;
+    decode_split(batch, max_seq_len, n_split, bps);
+    const size_t po = (size_t)batch * n_split  * heads * 512 * 4;
+    const size_t pm = (size_t)batch * n_split  * heads * 8;
+    return round_up(po) + round_up(pm);
+}
+
+kvr_status mla_decode_rotate_on_read(const void* q_nope, const void* q_rope, int32_t batch, int32_t heads,
+                                     const kvr_cache* cache, int32_t layer, const int32_t* d_block_tables,
+                                     const int32_t* d_pending_delta, int32_t bt_stride, const int32_t* d_seq_lens,
+                                     int32_t max_seq_len, float scale, void* out, float* lse, void* d_ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+    Pool pool;
+    double omega[kMaxPairs];
+    kvr_status st = make_pool(cache, pool, omega);
+    if (st != KVR_OK) return st;
+    if (cache->pf_dtype != KVR_BF16 || cache->rope_dtype != KVR_BF16 || cache->pf_width != 512 ||
+        cache->rope_heads != 1 || cache->rope_dim != 64 || cache->block_size != kDecBlockTokens)
+        return KVR_E_UNSUPPORTED;
+    if (batch < 1 || heads < 32 || heads % 32 || heads > 128) return KVR_E_UNSUPPORTED;
+    if (layer < 0 || layer >= cache->n_layers) return KVR_E_RANGE;
+    if (!q_nope || !q_rope || !aligned16(q_nope) || !aligned16(q_rope) || !out || !lse) return KVR_E_ARG;
+    if (!d_block_tables || !d_pending_delta || !d_seq_lens || bt_stride < 1) return KVR_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(d_block_tables) | reinterpret_cast<uintptr_t>(d_pending_delta) |
+         reinterpret_cast<uintptr_t>(d_seq_lens) | reinterpret_cast<uintptr_t>(lse)) & 3u)
+        return KVR_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(out) & 1u) || !std::isfinite(scale)) return KVR_E_ARG;
+    if (max_seq_len < 0 || (int64_t)max_seq_len > (int64_t)bt_stride * kDecBlockTokens) return KVR_E_RANGE;
+    const size_t need = kvr_decode_workspace_bytes(batch, heads, max_seq_len);
+    if (!d_ws || (reinterpret_cast<uintptr_t>(d_ws) % kAlign) || ws_bytes < need) return KVR_E_WORKSPACE;
+
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.ckv = pool.pf + (int64_t)layer * pool.pf_l;
+    a.ckv_b = pool.pf_b;
+    a.ckv_r = pool.pf_r;
+    a.kr = pool.rp + (int64_t)layer * pool.rp_l;
+    a.kr_b = pool.rp_b;
+    a.kr_r = pool.rp_r;
+    a.n_blocks = pool.n_blocks;
+    a.q_nope = (const uint16_t*)q_nope;
+    a.q_rope = (const uint16_t*)q_rope;
+    a.bt = d_block_tables;
+    a.pend = d_pending_delta;
+    a.seq_lens = d_seq_lens;
+    a.bt_stride = bt_stride;
+    a.max_len = max_seq_len;
+    a.batch = batch;
+    a.heads = heads;
+    decode_split(batch, max_seq_len, a.n_split, a.blocks_per_split);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.part_o = (float*)d_ws;
+    a.part_ml = (float*)((char*)d_ws + round_up((size_t)batch * a.n_split  * heads * 512 * 4));
+    std::memcpy(a.omega, omega, sizeof(a.omega));
+    hipError_t e = launch_decode(a, (uint16_t*)out, lse, stream);
+    return e == hipSuccess ? KVR_OK : hip_fail(e);
 }
 
 }  // extern "C"

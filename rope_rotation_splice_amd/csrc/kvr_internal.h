@@ -95,6 +95,27 @@ struct PatchArgs {
 };
 static_assert(sizeof(PatchArgs) <= 4000, "patch kernel arguments too large");
 
+// Rotate-on-read MLA decode (decode.hip).
+constexpr int kDecBlockTokens = 64;  // paged block size the decode kernel reads
+constexpr int kDecMaxBlocks = 32;    // KV blocks per split (angle table in LDS)
+
+struct DecodeArgs {
+    const char* ckv; int64_t ckv_b, ckv_r;     // layer applied; bytes
+    const char* kr;  int64_t kr_b, kr_r;
+    int32_t n_blocks;
+    const uint16_t* q_nope;                    // bf16 [batch][heads][512]
+    const uint16_t* q_rope;                    // bf16 [batch][heads][64]
+    const int32_t* bt;                         // [batch][bt_stride]
+    const int32_t* pend;                       // [batch][bt_stride]
+    const int32_t* seq_lens;                   // [batch]
+    int32_t bt_stride, max_len;
+    int32_t batch, heads, n_split, blocks_per_split;
+    float scale_log2;                          // softmax scale * log2(e)
+    float* part_o;                             // [batch][n_split][heads/32][16*16*64]
+    float* part_ml;                            // [batch][n_split][heads] x (max, sum)
+    double omega[32];
+};
+
 // Kernel arguments must stay within the 4 KB kernarg budget.
 static_assert(sizeof(RelocArgs) <= 4000, "relocation kernel arguments too large");
 
@@ -108,5 +129,8 @@ uint32_t read_and_clear_errors_relocate();
 // Patch kernel (patch.hip): fused gather + patch, or in-place patch.
 hipError_t launch_patch(const PatchArgs& a, bool inplace, hipStream_t s);
 uint32_t read_and_clear_errors_patch();
+// Decode (decode.hip): split kernel + combine kernel.
+hipError_t launch_decode(const DecodeArgs& a, uint16_t* out, float* lse, hipStream_t s);
+uint32_t read_and_clear_errors_decode();
 
 }  // namespace kvr

@@ -220,3 +220,25 @@ def test_patch_tolerance_rejects_transposed_factors():
     assert tolerance.bf16_close(good, y, scale).all()
     bad = bf16.round_rne((k + patch.lowrank(V, U)).astype(np.float32).astype(np.float64))
     assert not tolerance.bf16_close(bad, y, scale).all()
+
+
+def test_decode_score_bound_covers_bf16_keys():
+    """The score bound covers the error of storing rotated keys in bf16: a
+    single-token sequence (LSE = its score) with the keys rounded after the
+    float64 rotation stays within the bound of the exact LSE, and the
+    round_keys reading reproduces exactly that rounded-key attention."""
+    from oracle import tolerance
+    r = np.random.default_rng(12)
+    th = rope.inv_freq(64, 10000.0)
+    for trial in range(50):
+        qn, qr = r.standard_normal((4, 512)), r.standard_normal((4, 64))
+        ckv, kr = r.standard_normal((1, 512)), r.standard_normal((1, 64))
+        d = r.integers(-100000, 100000, size=1)
+        o, lse = decode.mla_decode(qn, qr, ckv, kr, d, 0.07, th)
+        k_hat = rope.rotate(kr, d, 1, 64, th)
+        s_dev = 0.07 * (qn @ ckv.T + qr @ bf16.to_f64(bf16.round_rne(k_hat)).T)[:, 0]
+        eps = decode.score_bound(qr, kr, d, 0.07, th)
+        assert np.all(np.abs(s_dev - lse) <= eps)
+        assert tolerance.decode_close(np.tile(ckv, (4, 1)), o, s_dev, lse, eps).all()
+        o_r, lse_r = decode.mla_decode(qn, qr, ckv, kr, d, 0.07, th, round_keys=True)
+        assert np.allclose(lse_r, s_dev, rtol=0, atol=1e-12)
