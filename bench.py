@@ -10,8 +10,11 @@ U{256..2048}, base positions U{0..60000}) of a 61-layer MLA cache
 (cKV 512 + k_r 64, bf16) gathered into one 40960-slot paged sequence with
 64-slot blocks and a random block table, each entry rotated by its own
 delta = p_target - base_pos.  Other workloads: ``splice`` (one 4096-slot
-contiguous sequence, [1000, 1800) -> 16 stub slots) and ``splice_batched``
-(64 x 32768 slots x 61 layers, one directive per sequence).
+contiguous sequence, [1000, 1800) -> 16 stub slots), ``splice_batched``
+(64 x 32768 slots x 61 layers, one directive per sequence), ``gqa_patch``
+(GQA relocation with a rank-16 patch), ``decode`` (rotate-on-read MLA
+decode, batch 32 x 32768 tokens x 128 heads; ``decode_zero_delta`` is the
+same with every pending shift 0) and ``copy`` (a plain device copy).
 
 Prints one JSON line: slots relocated per second (a slot = one token
 position of one sequence, all layers), the roofline of the relocation
@@ -343,6 +346,87 @@ class GqaPatch:
                           f"numpy fp64 (matmul through numpy's BLAS, single-threaded here)"}
 
 
+class Decode:
+    """Rotate-on-read absorbed-MLA decode: batch 32, 32768 cached tokens per
+    sequence, 128 query heads (q_nope 512 + q_rope 64 bf16), paged 64-token
+    blocks each carrying a pending shift ~ U{-1e5..1e5}, scale 1/sqrt(576).
+    A slot is a key rotated on read."""
+    name = "mla_decode"
+    kernel = "mla_decode_kernel + combine"
+
+    def __init__(self, zero_delta=False):
+        import kvsynth
+        self.w = kvsynth.rotate_on_read_decode()
+        self.zero_delta = zero_delta
+        w = self.w
+        self.slots = w.batch * w.ctx
+        cache = w.batch * w.ctx * 1152
+        q = w.batch * w.heads * 576 * 2
+        o = w.batch * w.heads * 512 * 2 + w.batch * w.heads * 4
+        tables = 2 * w.block_tables.nbytes + w.seq_lens.nbytes
+        self.bytes = cache + q + o + tables
+        self.flops = 2 * w.batch * w.ctx * w.heads * (576 + 512)
+        self.launches = 1
+        if zero_delta:
+            self.name = "mla_decode_zero_delta"
+        self.config = {"workload": "mla_decode_rotate_on_read" + ("_zero_delta" if zero_delta else ""),
+                       "batch": w.batch, "ctx": w.ctx, "heads": w.heads, "block_size": w.block_size,
+                       "pending_delta": "0" if zero_delta else "U{-1e5..1e5} per block",
+                       "q": "nope 512 + rope 64 bf16", "scale": "1/sqrt(576)", "keys_per_step": self.slots,
+                       "gflop": self.flops / 1e9}
+
+    def setup(self):
+        import torch
+        import kvsynth
+        import rope_rotation_splice_amd as rrs
+        w = self.w
+        self.pool = torch.empty((1, w.n_blocks, w.block_size, 576), dtype=torch.bfloat16, device="cuda")
+        kvsynth.fill_normal_(self.pool, 5, 1)
+        self.qn = torch.empty((w.batch, w.heads, 512), dtype=torch.bfloat16, device="cuda")
+        self.qr = torch.empty((w.batch, w.heads, 64), dtype=torch.bfloat16, device="cuda")
+        kvsynth.fill_normal_(self.qn, 5, 2)
+        kvsynth.fill_normal_(self.qr, 5, 3)
+        self.cache = rrs.KVCache.mla(self.pool)
+        self.bt = torch.from_numpy(w.block_tables).cuda()
+        pend = np.zeros_like(w.pending_delta) if self.zero_delta else w.pending_delta
+        self.pend = torch.from_numpy(pend).cuda()
+        self.lens = torch.from_numpy(w.seq_lens).cuda()
+        self.out = torch.empty((w.batch, w.heads, 512), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda")
+        self.rrs = rrs
+
+    def step(self):
+        w = self.w
+        self.rrs.mla_decode_rotate_on_read(self.qn, self.qr, self.cache, 0, self.bt, self.pend, self.lens, w.scale,
+                                           max_seq_len=w.ctx, out=self.out, lse=self.lse)
+
+    def cpu_baseline(self, budget_s):
+        import kvsynth
+        from oracle import decode as odec, rope as orope, bf16 as ob
+        w = self.w
+        th = orope.inv_freq(64, 10000.0)
+        keys, spent, seqs = 0, 0.0, 0
+        for b in range(w.batch):
+            r = kvsynth.rng(5, 9, b)
+            ckv = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, 512)))
+            kr = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, 64)))
+            qn = ob.to_f64(kvsynth.bf16_normal(r, (w.heads, 512)))
+            qr = ob.to_f64(kvsynth.bf16_normal(r, (w.heads, 64)))
+            d = odec.token_deltas(w.pending_delta[b], w.ctx, 64)
+            t0 = time.perf_counter()
+            odec.mla_decode(qn, qr, ckv, kr, d, w.scale, th, round_keys=True)
+            spent += time.perf_counter() - t0
+            keys += w.ctx
+            seqs += 1
+            if spent >= budget_s:
+                break
+        import os as _os
+        thr = int(_os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(_os.sched_getaffinity(0))
+        return {"value": keys / spent, "unit": "keys/s", "cores": thr, "kind": "oracle",
+                "sample": f"{seqs} whole sequences ({keys} keys, 128 heads), generation excluded, numpy fp64 "
+                          f"(its two matmuls go through numpy's BLAS, which may use up to {thr} threads)"}
+
+
 class Copy:
     """A plain device-to-device copy of the registry gather's byte volume
     (torch's copy kernel): the practical read+write ceiling, and the known-size
@@ -371,7 +455,7 @@ class Copy:
 
 
 WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "gqa_patch": GqaPatch,
-             "copy": Copy}
+             "decode": Decode, "decode_zero_delta": lambda: Decode(zero_delta=True), "copy": Copy}
 
 
 def main():
@@ -389,6 +473,7 @@ def main():
         return 2
 
     wl = WORKLOADS[args.workload]()
+    unit = "keys/s" if isinstance(wl, Decode) else "slots/s"
     # the CPU oracle runs before the GPU is touched
     cpu = None if args.no_cpu_baseline else wl.cpu_baseline(args.cpu_budget)
 
@@ -425,13 +510,13 @@ def main():
     traffic = stored_traffic(wl.kernel, wl.name)
     extra = {}
     if getattr(wl, "flops", None):
-        extra["matrix_core"] = {"dtype": "fp32", "achieved_TFLOPs": wl.flops * args.steps / gpu_s / 1e12,
-                                "peak_TFLOPs": 157.3,
-                                "frac": wl.flops * args.steps / gpu_s / 1e12 / 157.3}
+        dt, peak = ("bf16", 2500.0) if isinstance(wl, Decode) else ("fp32", 157.3)
+        extra["matrix_core"] = {"dtype": dt, "achieved_TFLOPs": wl.flops * args.steps / gpu_s / 1e12,
+                                "peak_TFLOPs": peak, "frac": wl.flops * args.steps / gpu_s / 1e12 / peak}
     out = {
         "metric": METRIC,
         "value": wl.slots * args.steps / wall,
-        "unit": "slots/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
