@@ -13,6 +13,14 @@
 // pass through registers, are rotated in fp32 by the block's pending delta
 // and land in LDS as bf16.  Nothing rotated is written back to HBM.
 //
+// cKV rows sit in LDS unpadded (1024 bytes) with their 16-byte chunks
+// permuted: chunk c of row r is stored at position c ^ swz(r), where swz
+// maps r mod 16 one-to-one onto 0..15 and puts r's two low bits into
+// position bits 2-3.  The K-row reads (16 rows x one chunk per 16 lanes) and
+// the transpose reads (4 rows x 64 contiguous bytes per 32 lanes) then each
+// touch every LDS bank once.  The direct global->LDS load writes position l
+// from lane l, so lane l fetches chunk l ^ swz(r).
+//
 // Matrix cores (v_mfma_f32_32x32x16_bf16, lane l holds output rows
 // 8*(r/4) + 4*(l/32) + r%4 of column l%32):
 // * S^T = K Q^T per 32-token tile: K rows (A) read from LDS, q (B) from
@@ -52,11 +60,18 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 constexpr int kBlk = kDecBlockTokens;                    // tokens per KV block
-constexpr int kCkvStride = 1040;                        // LDS bytes per cKV row (1024 + 16)
+constexpr int kCkvStride = 1024;                        // LDS bytes per cKV row (chunk-swizzled)
 constexpr int kKrStride = 144;                          // LDS bytes per k_r row (128 + 16)
 constexpr int kCkvBuf = kBlk * kCkvStride;
 constexpr int kKrBuf = kBlk * kKrStride;
-constexpr int kSmem = 2 * kCkvBuf + 2 * kKrBuf + kDecMaxBlocks * 32 * 8;
+constexpr int kCsOff = 2 * kCkvBuf + 2 * kKrBuf;        // (cos, sin) per block and pair
+constexpr int kBlkOff = kCsOff + kDecMaxBlocks * 32 * 8; // block ids of the split
+constexpr int kFlagOff = kBlkOff + kDecMaxBlocks * 4;   // restart flag
+constexpr int kSmem = kFlagOff + 16;
+static_assert(kSmem <= 160 * 1024, "LDS budget");
+
+// chunk permutation of a cKV row in LDS (row r mod 16 -> 0..15, one to one)
+__device__ __forceinline__ uint32_t swz(int r) { return 4u * (r & 3) + ((r >> 2) & 3); }
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ void raise_error(uint32_t bit) {
@@ -65,19 +80,23 @@ __device__ __forceinline__ void raise_error(uint32_t bit) {
 
 __device__ __forceinline__ v8bf as_bf(v4u x) { return __builtin_bit_cast(v8bf, x); }
 
+typedef __attribute__((address_space(3))) v4u lds_v4u;
+
 __device__ __forceinline__ v4u lds16(const char* p) { return *reinterpret_cast<const v4u*>(p); }
 
-__device__ __forceinline__ v4s lds_tr(const char* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+// reads at LDS byte offsets (the swizzled addresses are formed as integers)
+__device__ __forceinline__ v4u lds16_at(uint32_t off) { return *(const lds_v4u*)(size_t)off; }
+__device__ __forceinline__ v4s lds_tr_at(uint32_t off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(size_t)off);
 }
 
 // cKV rows of one block straight into LDS: one wave instruction per row
 // (64 lanes x 16 bytes = the 1024-byte row).
 __device__ __forceinline__ void stage_ckv(const DecodeArgs& A, int blk_id, char* dst, int wave, int n_waves,
                                           int lane) {
-    const char* src = A.ckv + (int64_t)blk_id * A.ckv_b + lane * 16;
+    const char* src = A.ckv + (int64_t)blk_id * A.ckv_b;
     for (int r = wave; r < kBlk; r += n_waves)
-        __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)r * A.ckv_r),
+        __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)r * A.ckv_r + 16 * (lane ^ swz(r))),
                                          (void __attribute__((address_space(3)))*)(dst + r * kCkvStride), 16, 0, 0);
 }
 
@@ -87,11 +106,15 @@ constexpr int kPasses = 3;
 template <int NW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(const DecodeArgs A) {
-    __shared__ __attribute__((aligned(16))) char smem[kSmem];
+    // the only LDS variable, so its 1024-byte alignment makes the cKV row
+    // bases multiples of 1024 and the chunk swizzle a plain XOR of offsets
+    __shared__ __attribute__((aligned(1024))) char smem[kSmem];
     char* ckv_s = smem;
     char* kr_s = smem + 2 * kCkvBuf;
-    float2* cs_s = reinterpret_cast<float2*>(smem + 2 * kCkvBuf + 2 * kKrBuf);
-    __shared__ int32_t s_blk[kDecMaxBlocks];
+    float2* cs_s = reinterpret_cast<float2*>(smem + kCsOff);
+    int32_t* s_blk = reinterpret_cast<int32_t*>(smem + kBlkOff);
+    int& s_overshoot = *reinterpret_cast<int*>(smem + kFlagOff);
+    const uint32_t ckv_off = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
 
     const int tid = threadIdx.x, nthr = NW * 64;
     const int wave = tid >> 6, lane = tid & 63, n_waves = NW;
@@ -133,7 +156,6 @@ void mla_decode_kernel(const DecodeArgs A) {
     v16f acc[16];
     float m_run = kNegInf, l_run = 0.f;
     float m_hint = kNegInf;                 // references carried into a restarted pass
-    __shared__ int s_overshoot;
 
     __syncthreads();
 
@@ -186,7 +208,7 @@ void mla_decode_kernel(const DecodeArgs A) {
 
     for (int i = 0; i < nb; ++i) {
         const int cur = i & 1;
-        const char* ck = ckv_s + cur * kCkvBuf;
+        const uint32_t ck = ckv_off + cur * kCkvBuf;
         const char* kq = kr_s + cur * kKrBuf;
         v4u nlo[KRI], nhi[KRI];
         bool nkr = false;
@@ -202,14 +224,23 @@ void mla_decode_kernel(const DecodeArgs A) {
             const int t0 = tile * 32;
             // S^T tile: rows = 32 tokens, columns = 32 heads
             v16f sacc = v16f{};
-            const char* krow = ck + (t0 + n) * kCkvStride + 16 * half;
-#pragma unroll
-            for (int s = 0; s < 32; ++s)
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(lds16(krow + 32 * s)), q[s], sacc, 0, 0, 0);
+            // chunk 2s + half of row t0 + n sits at position (2s) ^ (half ^ swz(n))
+            const uint32_t krow = ck + (t0 + n) * kCkvStride + 16 * (half ^ swz(n));
             const char* rrow = kq + (t0 + n) * kKrStride + 16 * half;
+            // K-row operands stream from LDS through a 4-deep window so the
+            // matrix core never waits for a read it could have issued earlier
+            auto kop = [&](int s) {
+                return s < 32 ? lds16_at((krow ^ (32u * (s & 7))) + 256u * (s >> 3)) : lds16(rrow + 32 * (s - 32));
+            };
+            v4u kw[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(lds16(rrow + 32 * s)), q[32 + s], sacc, 0, 0, 0);
+            for (int s = 0; s < 4; ++s) kw[s] = kop(s);
+#pragma unroll
+            for (int s = 0; s < 36; ++s) {
+                const v4u cur = kw[s & 3];
+                if (s + 4 < 36) kw[s & 3] = kop(s + 4);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(cur), q[s], sacc, 0, 0, 0);
+            }
 
             // scores (base 2), masking, tile maximum over the head's 32 tokens
             float x[16];
@@ -244,17 +275,25 @@ void mla_decode_kernel(const DecodeArgs A) {
             ls += __shfl_xor(ls, 32);
             l_run += ls;
 
-            // O^T += V^T P^T over two 16-token steps
+            // O^T += V^T P^T over two 16-token steps; transpose reads run
+            // 4 feature tiles ahead of the matrix core
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const int k0 = t0 + 16 * s + 4 * half;
+                // this lane's 8 bytes of feature tile f (64 bytes per row)
+                // start at byte 64f + 16cl + 8(sl&1) of rows ka and ka + 8
                 const int sl = lane & 15;
-                const char* ra = ck + (k0 + (sl >> 2)) * kCkvStride + 2 * (16 * ((lane >> 4) & 1) + 4 * (sl & 3));
-                const char* rb = ra + 8 * kCkvStride;
+                const int ka = t0 + 16 * s + 4 * half + (sl >> 2);
+                const uint32_t cl = 2 * ((lane >> 4) & 1) + ((sl & 3) >> 1);
+                const uint32_t ra = ck + ka * kCkvStride + 16 * (cl ^ swz(ka)) + 8 * (sl & 1);
+                const uint32_t rb = ck + (ka + 8) * kCkvStride + 16 * (cl ^ swz(ka + 8)) + 8 * (sl & 1);
+                auto tr = [&](uint32_t base, int f) { return lds_tr_at((base ^ (64u * (f & 3))) + 256u * (f >> 2)); };
+                v4s wa[4], wb[4];
+#pragma unroll
+                for (int f = 0; f < 4; ++f) { wa[f] = tr(ra, f); wb[f] = tr(rb, f); }
 #pragma unroll
                 for (int f = 0; f < 16; ++f) {
-                    const v4s ta = lds_tr(ra + 64 * f);
-                    const v4s tb = lds_tr(rb + 64 * f);
+                    const v4s ta = wa[f & 3], tb = wb[f & 3];
+                    if (f + 4 < 16) { wa[f & 3] = tr(ra, f + 4); wb[f & 3] = tr(rb, f + 4); }
                     const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
                     acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[f], 0, 0, 0);
                 }
