@@ -8,24 +8,36 @@
 //
 // Work split (flash-decoding): one workgroup per (sequence, KV split), one
 // wave per 32 query heads (4 waves = 128 heads), q held in registers for the
-// whole split.  KV blocks of 64 tokens are double-buffered in LDS: cKV rows go
-// global -> LDS directly (16 bytes per lane, no registers); the 64-d k_r rows
-// pass through registers, are rotated in fp32 by the block's pending delta
-// and land in LDS as bf16.  Nothing rotated is written back to HBM.
+// whole split.  Nothing rotated is written back to HBM.
 //
-// cKV rows sit in LDS unpadded (1024 bytes) with their 16-byte chunks
-// permuted: chunk c of row r is stored at position c ^ swz(r), where swz
-// maps r mod 16 one-to-one onto 0..15 and puts r's two low bits into
-// position bits 2-3.  The K-row reads (16 rows x one chunk per 16 lanes) and
-// the transpose reads (4 rows x 64 contiguous bytes per 32 lanes) then each
-// touch every LDS bank once.  The direct global->LDS load writes position l
-// from lane l, so lane l fetches chunk l ^ swz(r).
+// Load pipeline.  A split is walked in stages of 32 tokens (half a 64-token
+// block).  Both parts of a stage's rows go global -> LDS directly (16 bytes
+// per lane, no registers): the cKV rows into one of 4 stage buffers, the raw
+// k_r rows into one of 4 k_r buffers.  Loads run 3 stages ahead.  At the end
+// of stage j each wave waits until only the loads of stages j+2 and j+3 are
+// outstanding (vmcnt retires loads in order), the workgroup rotates stage
+// j+1's k_r in place in fp32 by its block's pending delta, and one barrier
+// publishes stage j+1.  The direct loads are issued from inline assembly:
+// the compiler would otherwise wait for every outstanding direct load before
+// any later LDS read, which serializes the pipeline; the waits here are
+// explicit and exact instead.  (cos, sin) of each block's shift live in a
+// 4-block ring filled 3 stages before use.
+//
+// LDS layouts.  cKV rows are unpadded (1024 bytes) with their 16-byte chunks
+// permuted: chunk c of row r sits at position c ^ swz(r), where swz maps r
+// mod 16 one-to-one onto 0..15 and puts r's two low bits into position bits
+// 2-3.  The K-row reads (16 rows x one chunk per 16 lanes) and the transpose
+// reads (4 rows x 64 contiguous bytes per 32 lanes) then each touch every LDS
+// bank once.  k_r rows (128 bytes) use chunk c at position c ^ ((r >> 1) & 7),
+// which spreads 16 consecutive rows' chunk reads over all banks.  A direct
+// load writes position l from lane l, so lane l fetches the chunk that
+// belongs there.
 //
 // Matrix cores (v_mfma_f32_32x32x16_bf16, lane l holds output rows
 // 8*(r/4) + 4*(l/32) + r%4 of column l%32):
-// * S^T = K Q^T per 32-token tile: K rows (A) read from LDS, q (B) from
-//   registers.  Lane l then holds 16 tokens of head l%32, so the per-head
-//   softmax statistics need one cross-lane exchange (lanes l and l^32).
+// * S^T = K Q^T per stage: K rows (A) read from LDS, q (B) from registers.
+//   Lane l then holds 16 tokens of head l%32, so the per-head softmax
+//   statistics need one cross-lane exchange (lanes l and l^32).
 // * O^T += V^T P^T per 16-token step: P (B) comes straight from the S^T
 //   registers -- the K-dimension slots are matched to the tokens a lane holds
 //   -- and V^T (A) is read from the row-major cKV tile with the LDS transpose
@@ -33,16 +45,19 @@
 //   C + 4*(s%4); destination lane d of the 16-lane group receives rows
 //   K0..K0+3 of column C + d).  O^T keeps head l%32 in lane l, the same head
 //   as the softmax statistics, so rescaling is lane-local.
+// LDS operands stream through 4-deep register windows ahead of the MFMAs.
 // Softmax runs in base 2 with the scale folded in.  The 256 accumulators of a
 // wave live in AGPRs and the main loop touches them only through the matrix
 // cores (any VALU access there makes the compiler spill): each head keeps a
-// fixed reference maximum (its first tile's maximum) and P = 2^(x - m_ref) may
-// exceed 1 by up to 2^48 (fp32 and bf16 share the exponent range).  If a tile
-// overshoots that headroom, the workgroup finishes the block, abandons the
-// pass and restarts the split from its first block with the observed maxima
-// as references (at most kPasses passes; then KVR_DEV_RANGE is raised and the
-// last pass completes).  Splits write unnormalized partials (lane-native
-// layout) that a combine kernel merges.
+// fixed reference maximum (its first stage's maximum) and P = 2^(x - m_ref)
+// may exceed 1 by up to 2^48 (fp32 and bf16 share the exponent range).  If a
+// stage overshoots that headroom, the workgroup finishes the stage, abandons
+// the pass and restarts the split with the observed maxima as references (at
+// most kPasses passes; then KVR_DEV_RANGE is raised and the last pass
+// completes).  Splits write unnormalized partials (lane-native layout) that a
+// combine kernel merges.
+#include <type_traits>
+
 #include "kvr_device.h"
 #include "kvr_internal.h"
 
@@ -56,23 +71,33 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) v4u lds_v4u;
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2u lds_v2u;
 
 constexpr int kBlk = kDecBlockTokens;                    // tokens per KV block
-constexpr int kCkvStride = 1024;                        // LDS bytes per cKV row (chunk-swizzled)
-constexpr int kKrStride = 144;                          // LDS bytes per k_r row (128 + 16)
-constexpr int kCkvBuf = kBlk * kCkvStride;
-constexpr int kKrBuf = kBlk * kKrStride;
-constexpr int kCsOff = 2 * kCkvBuf + 2 * kKrBuf;        // (cos, sin) per block and pair
-constexpr int kBlkOff = kCsOff + kDecMaxBlocks * 32 * 8; // block ids of the split
-constexpr int kFlagOff = kBlkOff + kDecMaxBlocks * 4;   // restart flag
+constexpr int kStage = 32;                              // tokens per pipeline stage
+constexpr int kNBuf = 4;                                // stage buffers (3 loads ahead)
+constexpr int kCkvRow = 1024;                           // LDS bytes per cKV row (chunk-swizzled)
+constexpr int kKrRow = 128;                             // LDS bytes per k_r row (chunk-swizzled)
+constexpr int kCkvStageB = kStage * kCkvRow;
+constexpr int kKrStageB = kStage * kKrRow;
+constexpr int kKrOff = kNBuf * kCkvStageB;
+constexpr int kCsOff = kKrOff + kNBuf * kKrStageB;      // (cos, sin) ring: 4 blocks x 32 pairs
+constexpr int kBlkOff = kCsOff + 4 * 32 * 8;            // block ids of the split
+constexpr int kPendOff = kBlkOff + kDecMaxBlocks * 4;   // pending shifts of the split
+constexpr int kOmegaOff = kPendOff + kDecMaxBlocks * 4; // theta_j / 2 pi, float64
+constexpr int kFlagOff = kOmegaOff + 32 * 8;            // restart flag
 constexpr int kSmem = kFlagOff + 16;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
-
-// chunk permutation of a cKV row in LDS (row r mod 16 -> 0..15, one to one)
-__device__ __forceinline__ uint32_t swz(int r) { return 4u * (r & 3) + ((r >> 2) & 3); }
 constexpr float kNegInf = -__builtin_inff();
+
+// chunk permutations of the rows in LDS
+__device__ __forceinline__ uint32_t swz(int r) { return 4u * (r & 3) + ((r >> 2) & 3); }
+__device__ __forceinline__ uint32_t swz_kr(int r) { return (uint32_t)(r >> 1) & 7u; }
 
 __device__ __forceinline__ void raise_error(uint32_t bit) {
     __hip_atomic_fetch_or(&g_errors_decode, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -80,24 +105,61 @@ __device__ __forceinline__ void raise_error(uint32_t bit) {
 
 __device__ __forceinline__ v8bf as_bf(v4u x) { return __builtin_bit_cast(v8bf, x); }
 
-typedef __attribute__((address_space(3))) v4u lds_v4u;
-
-__device__ __forceinline__ v4u lds16(const char* p) { return *reinterpret_cast<const v4u*>(p); }
-
-// reads at LDS byte offsets (the swizzled addresses are formed as integers)
+// LDS accesses at byte offsets (the swizzled addresses are formed as integers)
 __device__ __forceinline__ v4u lds16_at(uint32_t off) { return *(const lds_v4u*)(size_t)off; }
+__device__ __forceinline__ v2u lds8_at(uint32_t off) { return *(const lds_v2u*)(size_t)off; }
+__device__ __forceinline__ void lds8_put(uint32_t off, v2u v) { *(lds_v2u*)(size_t)off = v; }
 __device__ __forceinline__ v4s lds_tr_at(uint32_t off) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(size_t)off);
 }
 
-// cKV rows of one block straight into LDS: one wave instruction per row
-// (64 lanes x 16 bytes = the 1024-byte row).
-__device__ __forceinline__ void stage_ckv(const DecodeArgs& A, int blk_id, char* dst, int wave, int n_waves,
-                                          int lane) {
-    const char* src = A.ckv + (int64_t)blk_id * A.ckv_b;
-    for (int r = wave; r < kBlk; r += n_waves)
-        __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)r * A.ckv_r + 16 * (lane ^ swz(r))),
-                                         (void __attribute__((address_space(3)))*)(dst + r * kCkvStride), 16, 0, 0);
+// A pointer the whole wave agrees on, in scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// One direct global -> LDS load: lane l reads 16 bytes at base + off (base
+// wave-uniform, off per lane) and they land at LDS address lds + 16 l.  M0
+// carries the (wave-uniform) LDS address; the compiler sets M0 itself before
+// every use it makes, so the value left here is never relied upon.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Rotate 4 bf16 pairs: lo holds x_j..x_{j+3}, hi holds x_{j+h}..x_{j+h+3}.
+__device__ __forceinline__ void rot_bf16x4(v2u& lo, v2u& hi, const float2* cs) {
+    float a0, b0, a1, b1, a2, b2, a3, b3;
+    rot2(bf_lo(lo.x), bf_lo(hi.x), cs[0].x, cs[0].y, a0, b0);
+    rot2(bf_hi(lo.x), bf_hi(hi.x), cs[1].x, cs[1].y, a1, b1);
+    rot2(bf_lo(lo.y), bf_lo(hi.y), cs[2].x, cs[2].y, a2, b2);
+    rot2(bf_hi(lo.y), bf_hi(hi.y), cs[3].x, cs[3].y, a3, b3);
+    lo = v2u{pack_bf16(a0, a1), pack_bf16(a2, a3)};
+    hi = v2u{pack_bf16(b0, b1), pack_bf16(b2, b3)};
+}
+
+// Combine the values of lanes l and l ^ 32 (v_permlane32_swap leaves one
+// copy of each half's value in each of its two results).
+__device__ __forceinline__ float max_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 constexpr float kHeadroom = 48.f;      // log2 of the largest P before a restart
@@ -106,18 +168,18 @@ constexpr int kPasses = 3;
 template <int NW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(const DecodeArgs A) {
-    // the only LDS variable, so its 1024-byte alignment makes the cKV row
-    // bases multiples of 1024 and the chunk swizzle a plain XOR of offsets
+    // the only LDS variable, so its 1024-byte alignment makes every row base
+    // a multiple of the row size and the chunk swizzles plain XORs of offsets
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
-    char* ckv_s = smem;
-    char* kr_s = smem + 2 * kCkvBuf;
+    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
     float2* cs_s = reinterpret_cast<float2*>(smem + kCsOff);
     int32_t* s_blk = reinterpret_cast<int32_t*>(smem + kBlkOff);
+    int32_t* s_pend = reinterpret_cast<int32_t*>(smem + kPendOff);
+    double* s_omega = reinterpret_cast<double*>(smem + kOmegaOff);
     int& s_overshoot = *reinterpret_cast<int*>(smem + kFlagOff);
-    const uint32_t ckv_off = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
 
     const int tid = threadIdx.x, nthr = NW * 64;
-    const int wave = tid >> 6, lane = tid & 63, n_waves = NW;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n = lane & 31, half = lane >> 5;
     const int b = blockIdx.x / A.n_split, sp = blockIdx.x - b * A.n_split;
     const int head = wave * 32 + n;
@@ -126,20 +188,17 @@ void mla_decode_kernel(const DecodeArgs A) {
     const int nblk_seq = (len + kBlk - 1) / kBlk;
     const int blk0 = sp * A.blocks_per_split;
     const int nb = max(0, min(A.blocks_per_split, nblk_seq - blk0));
+    // stages holding at least one token of the sequence
+    const int n_st = nb > 0 ? min(2 * nb, (len - blk0 * kBlk + kStage - 1) / kStage) : 0;
 
-    // ---- per-split tables: block ids and (cos, sin) of every pending shift --
+    // ---- per-split tables: block ids and pending shifts ---------------------
     for (int e = tid; e < nb; e += nthr) {
         int id = A.bt[(int64_t)b * A.bt_stride + blk0 + e];
         if ((unsigned)id >= (unsigned)A.n_blocks) { raise_error(KVR_DEV_BAD_BLOCK); id = -1; }
         s_blk[e] = id;
+        s_pend[e] = A.pend[(int64_t)b * A.bt_stride + blk0 + e];
     }
-    for (int e = tid; e < nb * 32; e += nthr) {
-        const int d = A.pend[(int64_t)b * A.bt_stride + blk0 + (e >> 5)];
-        const double u = (double)d * A.omega[e & 31];
-        float s, c;
-        sincosf((float)((u - rint(u)) * 6.283185307179586476925), &s, &c);
-        cs_s[e] = make_float2(c, s);
-    }
+    if (tid < 32) s_omega[tid] = A.omega[tid];
 
     // ---- q for this lane's head: B operand of S^T = K Q^T, 36 K-steps -------
     v8bf q[36];
@@ -152,165 +211,235 @@ void mla_decode_kernel(const DecodeArgs A) {
         for (int s = 0; s < 4; ++s)
             q[32 + s] = as_bf(*reinterpret_cast<const v4u*>(A.q_rope + qh * 64 + 16 * s + 8 * half));
     }
+    // all loads so far have landed (a wait the compiler also accounts for, so
+    // it adds none later that would drain the direct loads)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+
+    // a stage is live if it exists and its block id is valid (uniform)
+    auto live = [&](int j) __attribute__((always_inline)) -> bool {
+        return __builtin_amdgcn_readfirstlane((int)(j < n_st && s_blk[j >> 1] >= 0)) != 0;
+    };
+    // (cos, sin) of block i's shift into ring slot i % 4: threads 0..31.
+    // The angle is reduced in float64 to f in [-1/2, 1/2] revolution; the
+    // hardware sine and cosine take revolutions, so f goes in directly.
+    auto angles = [&](int i) __attribute__((always_inline)) {
+        if (tid < 32) {
+            const double u = (double)s_pend[i] * s_omega[tid];
+            const float f = (float)(u - rint(u));
+            cs_s[(i & 3) * 32 + tid] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+        }
+    };
+    // Direct loads of stage j, as items of this wave: cKV rows r = wave + k NW
+    // (k < nc), then k_r row groups g = wave + (k - nc) NW (8 rows of 128
+    // bytes per instruction).  With NW dividing both counts every wave has
+    // the same items and their kinds are known at compile time.  Stages past
+    // the split reload its last stage (into a buffer nobody reads again, from
+    // L2) and a bad block id loads block 0 (its rows are zeroed once landed),
+    // so every iteration issues the same loads and no branch splits the
+    // matrix-core loop.
+    constexpr bool kEven = (kStage % NW == 0) && ((kStage / 8) % NW == 0);
+    const int nc = kEven ? kStage / NW : (kStage - wave + NW - 1) / NW;
+    const int n_items = kEven ? kStage / NW + (kStage / 8) / NW : nc + (kStage / 8 - wave + NW - 1) / NW;
+    auto issue_item = [&](int jj, int k) __attribute__((always_inline)) {
+        const int j = min(jj, n_st - 1);
+        const int id = max(0, __builtin_amdgcn_readfirstlane(s_blk[j >> 1]));
+        const int64_t row0 = 32 * (j & 1);
+        if (k < nc) {
+            const int r = wave + NW * k;
+            dma16(A.ckv + (int64_t)id * A.ckv_b + (row0 + r) * A.ckv_r, 16u * (lane ^ swz(r)),
+                  lds0 + (jj & 3) * kCkvStageB + r * kCkvRow);
+        } else {
+            const int g = wave + NW * (k - nc);
+            const int r = 8 * g + (lane >> 3);
+            dma16(A.kr + (int64_t)id * A.kr_b + (row0 + 8 * g) * A.kr_r,
+                  (uint32_t)(lane >> 3) * (uint32_t)A.kr_r + 16u * ((lane & 7) ^ swz_kr(r)),
+                  lds0 + kKrOff + (jj & 3) * kKrStageB + g * 1024);
+        }
+    };
+    auto issue_all = [&](int j) __attribute__((always_inline)) {
+        for (int k = 0; k < n_items; ++k) issue_item(j, k);
+    };
+    // rotate stage j's k_r in place: item e = (row e/8, 8-byte unit e%8 of
+    // the lo half and its partner in the hi half)
+    auto rotate_kr = [&](int j) __attribute__((always_inline)) {
+        const uint32_t kb = lds0 + kKrOff + (j & 3) * kKrStageB;
+        const float2* cs = cs_s + ((j >> 1) & 3) * 32;
+        for (int e = tid; e < kStage * 8; e += nthr) {
+            const int r = e >> 3, u = e & 7;
+            const uint32_t rb = kb + r * kKrRow + 8 * (u & 1);
+            const uint32_t plo = rb + 16 * ((uint32_t)(u >> 1) ^ swz_kr(r));
+            const uint32_t phi = rb + 16 * ((uint32_t)((u >> 1) + 4) ^ swz_kr(r));
+            v2u lo = lds8_at(plo), hi = lds8_at(phi);
+            rot_bf16x4(lo, hi, cs + 4 * u);
+            lds8_put(plo, lo);
+            lds8_put(phi, hi);
+        }
+    };
+    // cKV rows of stage j at or past the sequence end (all rows if the block
+    // id is bad) are zeroed: their P is 0, and 0 * (NaN left in an unused
+    // cache row) would still poison O.
+    auto zero_tail = [&](int j) __attribute__((always_inline)) {
+        const int valid = __builtin_amdgcn_readfirstlane((int)(s_blk[j >> 1] >= 0));
+        const int first = valid ? max(0, len - (blk0 * kBlk + kStage * j)) : 0;
+        if (first >= kStage) return;
+        const uint32_t cb = lds0 + (j & 3) * kCkvStageB;
+        for (int e = first * 64 + tid; e < kStage * 64; e += nthr)
+            *(lds_v4u*)(size_t)(cb + 16 * e) = v4u{0, 0, 0, 0};
+    };
+    // loads per stage and wave: the fewest any wave issues
+    constexpr int kPerStage = kStage / NW + (kStage / 8) / NW;
+    constexpr int kItemsMax = (kStage + NW - 1) / NW + (kStage / 8 + NW - 1) / NW;
+    constexpr int kSlot = 36 / kItemsMax;                 // S^T steps per load issued
+    constexpr int kW2 = 2 * kPerStage < 63 ? 2 * kPerStage : 63;
 
     v16f acc[16];
     float m_run = kNegInf, l_run = 0.f;
     float m_hint = kNegInf;                 // references carried into a restarted pass
 
-    __syncthreads();
-
-    // k_r staging: item e < 256 is (token e/4, 16-byte chunk e%4) of the lo
-    // half plus its partner chunk in the hi half; thread tid owns items
-    // tid + k * nthr (k < 4).
-    constexpr int KRI = (4 + NW - 1) / NW;
-    auto load_kr = [&](int i, v4u* lo, v4u* hi) -> bool {
-        const int id = s_blk[i];
-        if (id < 0) return false;
+    // softmax of stage j from its S^T: P (bf16) and the running statistics
+    auto softmax = [&](int j, const v16f& sacc, bool last_pass, v8bf* pb) __attribute__((always_inline)) {
+        const bool valid = __builtin_amdgcn_readfirstlane((int)(s_blk[j >> 1] >= 0)) != 0;
+        const int tok_base = blk0 * kBlk + kStage * j;
+        // a stage wholly inside the sequence needs no mask (uniform)
+        const bool full = valid && tok_base + kStage <= len;
+        float x[16];
 #pragma unroll
-        for (int k = 0; k < KRI; ++k) {
-            const int e = tid + k * nthr;
-            if (e < kBlk * 4) {
-                const char* p = A.kr + (int64_t)id * A.kr_b + (int64_t)(e >> 2) * A.kr_r + (e & 3) * 16;
-                lo[k] = *reinterpret_cast<const v4u*>(p);
-                hi[k] = *reinterpret_cast<const v4u*>(p + 64);
+        for (int r = 0; r < 16; ++r) x[r] = sacc[r] * A.scale_log2;
+        if (!full) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int t = 8 * (r >> 2) + 4 * half + (r & 3);
+                if (!valid || tok_base + t >= len) x[r] = kNegInf;
             }
         }
-        return true;
-    };
-    auto store_kr = [&](int i, v4u* lo, v4u* hi, char* dst) {
+        float mt = x[0];
 #pragma unroll
-        for (int k = 0; k < KRI; ++k) {
-            const int e = tid + k * nthr;
-            if (e < kBlk * 4) {
-                rot_bf16x8(lo[k], hi[k], cs_s + i * 32 + (e & 3) * 8);
-                char* p = dst + (e >> 2) * kKrStride + (e & 3) * 16;
-                *reinterpret_cast<v4u*>(p) = lo[k];
-                *reinterpret_cast<v4u*>(p + 64) = hi[k];
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
+        mt = max_halves(mt);
+        // the first live stage of a head fixes its reference; an overshoot
+        // beyond the headroom abandons this pass (decided per workgroup at
+        // the end of the stage)
+        if (m_run == kNegInf) m_run = mt;
+        if (mt > m_run + kHeadroom) {
+            m_hint = fmaxf(m_hint, mt);
+            if (!last_pass) s_overshoot = 1;
+            else raise_error(KVR_DEV_RANGE);
+        }
+        m_hint = fmaxf(m_hint, m_run);
+        // P in bf16, summed from the same bf16 values so that numerator and
+        // denominator agree.  P <= 2^48 and exp2 of anything below -126 may
+        // flush to zero, so the bare hardware exp2 is exact enough.  A head
+        // with no live token yet has m_run = x = -inf: P = exp2(-inf) = 0.
+        const float mr = m_run == kNegInf ? 0.f : m_run;
+        const v2bf ones = {(__bf16)1.f, (__bf16)1.f};
+        float ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const v2bf pr = {(__bf16)__builtin_amdgcn_exp2f(x[r] - mr), (__bf16)__builtin_amdgcn_exp2f(x[r + 1] - mr)};
+            pb[r >> 3][r & 7] = pr[0];
+            pb[r >> 3][(r & 7) + 1] = pr[1];
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
+        }
+        ls = sum_halves(ls);
+        l_run += ls;
+    };
+
+    // one stage of attention: S^T, softmax, O^T += V^T P^T; the loads of
+    // stage jl are spread over the S^T steps
+    auto compute = [&](int j, int jl, bool last_pass) __attribute__((always_inline)) {
+        const uint32_t ck = lds0 + (j & 3) * kCkvStageB;
+        const uint32_t kq = lds0 + kKrOff + (j & 3) * kKrStageB;
+
+        // S^T: rows = 32 tokens, columns = 32 heads.  Chunk 2s + half of cKV
+        // row n sits at position (2s) ^ (half ^ swz(n)); chunk 2s' + half of
+        // k_r row n at (2s') ^ (half ^ swz_kr(n)).
+        const uint32_t krow = ck + n * kCkvRow + 16 * (half ^ swz(n));
+        const uint32_t rrow = kq + n * kKrRow + 16 * (half ^ swz_kr(n));
+        auto kop = [&](int s) __attribute__((always_inline)) {
+            return s < 32 ? lds16_at((krow ^ (32u * (s & 7))) + 256u * (s >> 3)) : lds16_at(rrow ^ (32u * (s - 32)));
+        };
+        v16f sacc = v16f{};
+        constexpr int kWin = 3;             // K-row reads in flight ahead of the MFMAs
+        v4u kw[kWin];
+#pragma unroll
+        for (int s = 0; s < kWin; ++s) kw[s] = kop(s);
+#pragma unroll
+        for (int s = 0; s < 36; ++s) {
+            const v4u cur = kw[s % kWin];
+            if (s + kWin < 36) kw[s % kWin] = kop(s + kWin);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(cur), q[s], sacc, 0, 0, 0);
+            if (s % kSlot == 0 && s / kSlot < kItemsMax && (kEven || s / kSlot < n_items)) issue_item(jl, s / kSlot);
+        }
+
+        v8bf pb[2];
+        softmax(j, sacc, last_pass, pb);
+
+        // O^T += V^T P^T over two 16-token steps; transpose reads run 4
+        // feature tiles ahead of the matrix core
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            // this lane's 8 bytes of feature tile f (64 bytes per row) start
+            // at byte 64f + 16cl + 8(sl&1) of rows ka and ka + 8
+            const int sl = lane & 15;
+            const int ka = 16 * s + 4 * half + (sl >> 2);
+            const uint32_t cl = 2 * ((lane >> 4) & 1) + ((sl & 3) >> 1);
+            const uint32_t ra = ck + ka * kCkvRow + 16 * (cl ^ swz(ka)) + 8 * (sl & 1);
+            const uint32_t rb = ck + (ka + 8) * kCkvRow + 16 * (cl ^ swz(ka + 8)) + 8 * (sl & 1);
+            auto tr = [&](uint32_t base, int f) __attribute__((always_inline)) {
+                return lds_tr_at((base ^ (64u * (f & 3))) + 256u * (f >> 2));
+            };
+            v4s wa[4], wb[4];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) { wa[f] = tr(ra, f); wb[f] = tr(rb, f); }
+#pragma unroll
+            for (int f = 0; f < 16; ++f) {
+                const v4s ta = wa[f & 3], tb = wb[f & 3];
+                if (f + 4 < 16) { wa[f & 3] = tr(ra, f + 4); wb[f & 3] = tr(rb, f + 4); }
+                const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[f], 0, 0, 0);
             }
         }
     };
 
     for (int pass = 0; pass < kPasses; ++pass) {
 #pragma unroll
-    for (int f = 0; f < 16; ++f) acc[f] = v16f{};
-    m_run = m_hint;
-    l_run = 0.f;
-    if (tid == 0) s_overshoot = 0;
-    if (nb > 0) {
-        v4u lo[KRI], hi[KRI];
-        if (s_blk[0] >= 0) stage_ckv(A, s_blk[0], ckv_s, wave, n_waves, lane);
-        if (load_kr(0, lo, hi)) store_kr(0, lo, hi, kr_s);
-    }
-    wait_loads();
-    __syncthreads();
-    const bool last_pass = pass + 1 == kPasses;
-    bool restart = false;
-
-    for (int i = 0; i < nb; ++i) {
-        const int cur = i & 1;
-        const uint32_t ck = ckv_off + cur * kCkvBuf;
-        const char* kq = kr_s + cur * kKrBuf;
-        v4u nlo[KRI], nhi[KRI];
-        bool nkr = false;
-        if (i + 1 < nb) {
-            if (s_blk[i + 1] >= 0) stage_ckv(A, s_blk[i + 1], ckv_s + (cur ^ 1) * kCkvBuf, wave, n_waves, lane);
-            nkr = load_kr(i + 1, nlo, nhi);
-        }
-        const bool valid = s_blk[i] >= 0;
-        const int tok_base = (blk0 + i) * kBlk;
-
-#pragma unroll
-        for (int tile = 0; tile < 2; ++tile) {
-            const int t0 = tile * 32;
-            // S^T tile: rows = 32 tokens, columns = 32 heads
-            v16f sacc = v16f{};
-            // chunk 2s + half of row t0 + n sits at position (2s) ^ (half ^ swz(n))
-            const uint32_t krow = ck + (t0 + n) * kCkvStride + 16 * (half ^ swz(n));
-            const char* rrow = kq + (t0 + n) * kKrStride + 16 * half;
-            // K-row operands stream from LDS through a 4-deep window so the
-            // matrix core never waits for a read it could have issued earlier
-            auto kop = [&](int s) {
-                return s < 32 ? lds16_at((krow ^ (32u * (s & 7))) + 256u * (s >> 3)) : lds16(rrow + 32 * (s - 32));
-            };
-            v4u kw[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) kw[s] = kop(s);
-#pragma unroll
-            for (int s = 0; s < 36; ++s) {
-                const v4u cur = kw[s & 3];
-                if (s + 4 < 36) kw[s & 3] = kop(s + 4);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(cur), q[s], sacc, 0, 0, 0);
-            }
-
-            // scores (base 2), masking, tile maximum over the head's 32 tokens
-            float x[16];
-            float mt = kNegInf;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
-                x[r] = (valid && tok_base + t < len) ? sacc[r] * A.scale_log2 : kNegInf;
-                mt = fmaxf(mt, x[r]);
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            // first valid tile of a head fixes its reference; an overshoot
-            // beyond the headroom abandons this pass (decided per workgroup
-            // at the end of the block)
-            if (m_run == kNegInf) m_run = mt;
-            if (mt > m_run + kHeadroom) {
-                m_hint = fmaxf(m_hint, mt);
-                if (!last_pass) s_overshoot = 1;
-                else raise_error(KVR_DEV_RANGE);
-            }
-            m_hint = fmaxf(m_hint, m_run);
-            // P in bf16 (also summed in bf16 so numerator and denominator agree)
-            v8bf pb[2];
-            float ls = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = (m_run == kNegInf) ? 0.f : exp2f(x[r] - m_run);
-                const __bf16 pr = (__bf16)p;
-                pb[r >> 3][r & 7] = pr;
-                ls += (float)pr;
-            }
-            ls += __shfl_xor(ls, 32);
-            l_run += ls;
-
-            // O^T += V^T P^T over two 16-token steps; transpose reads run
-            // 4 feature tiles ahead of the matrix core
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                // this lane's 8 bytes of feature tile f (64 bytes per row)
-                // start at byte 64f + 16cl + 8(sl&1) of rows ka and ka + 8
-                const int sl = lane & 15;
-                const int ka = t0 + 16 * s + 4 * half + (sl >> 2);
-                const uint32_t cl = 2 * ((lane >> 4) & 1) + ((sl & 3) >> 1);
-                const uint32_t ra = ck + ka * kCkvStride + 16 * (cl ^ swz(ka)) + 8 * (sl & 1);
-                const uint32_t rb = ck + (ka + 8) * kCkvStride + 16 * (cl ^ swz(ka + 8)) + 8 * (sl & 1);
-                auto tr = [&](uint32_t base, int f) { return lds_tr_at((base ^ (64u * (f & 3))) + 256u * (f >> 2)); };
-                v4s wa[4], wb[4];
-#pragma unroll
-                for (int f = 0; f < 4; ++f) { wa[f] = tr(ra, f); wb[f] = tr(rb, f); }
-#pragma unroll
-                for (int f = 0; f < 16; ++f) {
-                    const v4s ta = wa[f & 3], tb = wb[f & 3];
-                    if (f + 4 < 16) { wa[f & 3] = tr(ra, f + 4); wb[f & 3] = tr(rb, f + 4); }
-                    const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
-                    acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[f], 0, 0, 0);
-                }
-            }
-        }
-
-        if (nkr) store_kr(i + 1, nlo, nhi, kr_s + (cur ^ 1) * kKrBuf);
-        wait_loads();
+        for (int f = 0; f < 16; ++f) acc[f] = v16f{};
+        m_run = m_hint;
+        l_run = 0.f;
+        const bool last_pass = pass + 1 == kPasses;
+        __syncthreads();                    // everyone has read the previous flag
+        if (tid == 0) s_overshoot = 0;
+        // prologue: angles of blocks 0 and 1, loads of stages 0..2, stage 0
+        // ready (landed, tail zeroed, k_r rotated)
+        if (nb > 0) angles(0);
+        if (nb > 1) angles(1);
+        if (n_st > 0) { issue_all(0); issue_all(1); issue_all(2); }
+        wait_vmcnt<kW2>();
         __syncthreads();
-        if (s_overshoot) { restart = true; break; }
-    }
-    if (!restart) break;
-    __syncthreads();                        // everyone has read the flag before it is cleared
+        if (0 < n_st) { zero_tail(0); if (live(0)) rotate_kr(0); }
+        __syncthreads();
+
+        // Iteration j: attention over stage j while stage j+3 loads; at the
+        // end stage j+1 is made ready.
+        bool restart = false;
+        for (int j = 0; !restart && j < n_st; ++j) {
+            // the angles of a block are in the ring two barriers before its
+            // first stage is rotated
+            if (((j + 3) & 1) == 0 && ((j + 3) >> 1) < nb) angles((j + 3) >> 1);
+            compute(j, j + 3, last_pass);
+            wait_vmcnt<kW2>();              // stage j+1 landed
+            __syncthreads();                // ... for every wave; stage j fully read
+            if (j + 1 < n_st) { zero_tail(j + 1); if (live(j + 1)) rotate_kr(j + 1); }
+            __syncthreads();                // stage j+1 ready
+            restart = __builtin_amdgcn_readfirstlane(s_overshoot) != 0;
+        }
+        wait_vmcnt<0>();                    // no load may land in LDS after this
+        if (!restart) break;
     }
 
     // ---- unnormalized partials in the lane-native layout ---------------------
-    float* po = A.part_o + (((int64_t)b * A.n_split + sp) * n_waves + wave) * (16 * 16 * 64);
+    float* po = A.part_o + (((int64_t)b * A.n_split + sp) * NW + wave) * (16 * 16 * 64);
 #pragma unroll
     for (int f = 0; f < 16; ++f)
 #pragma unroll

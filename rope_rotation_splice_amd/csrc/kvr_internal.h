@@ -97,7 +97,7 @@ static_assert(sizeof(PatchArgs) <= 4000, "patch kernel arguments too large");
 
 // Rotate-on-read MLA decode (decode.hip).
 constexpr int kDecBlockTokens = 64;  // paged block size the decode kernel reads
-constexpr int kDecMaxBlocks = 32;    // KV blocks per split (angle table in LDS)
+constexpr int kDecMaxBlocks = 64;    // KV blocks per split (block and shift tables in LDS)
 
 struct DecodeArgs {
     const char* ckv; int64_t ckv_b, ckv_r;     // layer applied; bytes
