@@ -223,12 +223,12 @@ void mla_decode_kernel(const DecodeArgs A) {
     // (cos, sin) of block i's shift into ring slot i % 4: threads 0..31.
     // The angle is reduced in float64 to f in [-1/2, 1/2] revolution; the
     // hardware sine and cosine take revolutions, so f goes in directly.
+    // Every wave computes them (lanes share pairs); threads 0..31 store.
     auto angles = [&](int i) __attribute__((always_inline)) {
-        if (tid < 32) {
-            const double u = (double)s_pend[i] * s_omega[tid];
-            const float f = (float)(u - rint(u));
-            cs_s[(i & 3) * 32 + tid] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
-        }
+        const double u = (double)s_pend[i] * s_omega[tid & 31];
+        const float f = (float)(u - rint(u));
+        const float2 v = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+        if (tid < 32) cs_s[(i & 3) * 32 + tid] = v;
     };
     // Direct loads of stage j, as items of this wave: cKV rows r = wave + k NW
     // (k < nc), then k_r row groups g = wave + (k - nc) NW (8 rows of 128
@@ -265,7 +265,10 @@ void mla_decode_kernel(const DecodeArgs A) {
     auto rotate_kr = [&](int j) __attribute__((always_inline)) {
         const uint32_t kb = lds0 + kKrOff + (j & 3) * kKrStageB;
         const float2* cs = cs_s + ((j >> 1) & 3) * 32;
-        for (int e = tid; e < kStage * 8; e += nthr) {
+#pragma unroll
+        for (int k = 0; k < (kStage * 8 + nthr - 1) / nthr; ++k) {
+            const int e = tid + k * nthr;
+            if ((kStage * 8) % nthr != 0 && e >= kStage * 8) break;
             const int r = e >> 3, u = e & 7;
             const uint32_t rb = kb + r * kKrRow + 8 * (u & 1);
             const uint32_t plo = rb + 16 * ((uint32_t)(u >> 1) ^ swz_kr(r));
@@ -291,7 +294,7 @@ void mla_decode_kernel(const DecodeArgs A) {
     constexpr int kPerStage = kStage / NW + (kStage / 8) / NW;
     constexpr int kItemsMax = (kStage + NW - 1) / NW + (kStage / 8 + NW - 1) / NW;
     constexpr int kSlot = 36 / kItemsMax;                 // S^T steps per load issued
-    constexpr int kW2 = 2 * kPerStage < 63 ? 2 * kPerStage : 63;
+    constexpr int kW1 = kPerStage < 63 ? kPerStage : 63;
 
     v16f acc[16];
     float m_run = kNegInf, l_run = 0.f;
@@ -345,9 +348,12 @@ void mla_decode_kernel(const DecodeArgs A) {
         l_run += ls;
     };
 
-    // one stage of attention: S^T, softmax, O^T += V^T P^T; the loads of
-    // stage jl are spread over the S^T steps
-    auto compute = [&](int j, int jl, bool last_pass) __attribute__((always_inline)) {
+    // One stage of attention: S^T, softmax, O^T += V^T P^T.  The loads of
+    // stage j+3 are spread over the S^T steps; between the two O^T steps
+    // stage j+1's k_r is rotated and block (j+3)/2's angles are computed.
+    // Stage j+1's k_r landed before the last barrier; stages beyond the
+    // split only touch buffers and ring slots nobody reads again.
+    auto compute = [&](int j, bool last_pass) __attribute__((always_inline)) {
         const uint32_t ck = lds0 + (j & 3) * kCkvStageB;
         const uint32_t kq = lds0 + kKrOff + (j & 3) * kKrStageB;
 
@@ -360,7 +366,7 @@ void mla_decode_kernel(const DecodeArgs A) {
             return s < 32 ? lds16_at((krow ^ (32u * (s & 7))) + 256u * (s >> 3)) : lds16_at(rrow ^ (32u * (s - 32)));
         };
         v16f sacc = v16f{};
-        constexpr int kWin = 3;             // K-row reads in flight ahead of the MFMAs
+        constexpr int kWin = 4;             // K-row reads in flight ahead of the MFMAs
         v4u kw[kWin];
 #pragma unroll
         for (int s = 0; s < kWin; ++s) kw[s] = kop(s);
@@ -369,7 +375,7 @@ void mla_decode_kernel(const DecodeArgs A) {
             const v4u cur = kw[s % kWin];
             if (s + kWin < 36) kw[s % kWin] = kop(s + kWin);
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(cur), q[s], sacc, 0, 0, 0);
-            if (s % kSlot == 0 && s / kSlot < kItemsMax && (kEven || s / kSlot < n_items)) issue_item(jl, s / kSlot);
+            if (s % kSlot == 0 && s / kSlot < kItemsMax && (kEven || s / kSlot < n_items)) issue_item(j + 3, s / kSlot);
         }
 
         v8bf pb[2];
@@ -379,6 +385,11 @@ void mla_decode_kernel(const DecodeArgs A) {
         // feature tiles ahead of the matrix core
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
+            if (s == 1) {
+                // between the two steps no read window is live
+                rotate_kr(j + 1);
+                angles(min((j + 3) >> 1, nb - 1));
+            }
             // this lane's 8 bytes of feature tile f (64 bytes per row) start
             // at byte 64f + 16cl + 8(sl&1) of rows ka and ka + 8
             const int sl = lane & 15;
@@ -410,28 +421,25 @@ void mla_decode_kernel(const DecodeArgs A) {
         const bool last_pass = pass + 1 == kPasses;
         __syncthreads();                    // everyone has read the previous flag
         if (tid == 0) s_overshoot = 0;
-        // prologue: angles of blocks 0 and 1, loads of stages 0..2, stage 0
-        // ready (landed, tail zeroed, k_r rotated)
+        // prologue: angles of blocks 0 and 1, loads of stages 0..2; stage 0
+        // ready (landed, tail zeroed, k_r rotated) and stage 1 landed
         if (nb > 0) angles(0);
         if (nb > 1) angles(1);
         if (n_st > 0) { issue_all(0); issue_all(1); issue_all(2); }
-        wait_vmcnt<kW2>();
+        wait_vmcnt<kW1>();
         __syncthreads();
-        if (0 < n_st) { zero_tail(0); if (live(0)) rotate_kr(0); }
+        if (0 < n_st) { zero_tail(0); rotate_kr(0); }
         __syncthreads();
 
-        // Iteration j: attention over stage j while stage j+3 loads; at the
-        // end stage j+1 is made ready.
+        // Iteration j: attention over stage j, with stage j+1's k_r rotated
+        // and stage j+3's loads issued on the way; at the end stage j+2 has
+        // landed and one barrier makes stages j+1 and j+2 visible.
         bool restart = false;
         for (int j = 0; !restart && j < n_st; ++j) {
-            // the angles of a block are in the ring two barriers before its
-            // first stage is rotated
-            if (((j + 3) & 1) == 0 && ((j + 3) >> 1) < nb) angles((j + 3) >> 1);
-            compute(j, j + 3, last_pass);
-            wait_vmcnt<kW2>();              // stage j+1 landed
-            __syncthreads();                // ... for every wave; stage j fully read
-            if (j + 1 < n_st) { zero_tail(j + 1); if (live(j + 1)) rotate_kr(j + 1); }
-            __syncthreads();                // stage j+1 ready
+            if (j + 1 < n_st) zero_tail(j + 1);
+            compute(j, last_pass);
+            wait_vmcnt<kW1>();              // stage j+2 landed
+            __syncthreads();
             restart = __builtin_amdgcn_readfirstlane(s_overshoot) != 0;
         }
         wait_vmcnt<0>();                    // no load may land in LDS after this

@@ -183,3 +183,24 @@ def test_decode_workload_sampled():
         eps = odec.score_bound(ob.to_f64(qr_h[b]), kr, d, w.scale, TH)
         ok = tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps)
         assert ok.all(), f"seq {b}: {(~ok).sum()} heads outside tolerance"
+
+
+def test_decode_nan_rows_past_length():
+    """Cache rows past a sequence's length (same block, and whole blocks the
+    table still names) may hold anything, NaN included: masked tokens get
+    P = 0 and must not contribute 0 * NaN to O."""
+    import torch
+    lens = [100, 64 * 3 + 5, 1]
+    host, devs = _setup(3, 128, lens, bt_stride=8, keys=(7,))
+    nan = np.uint16(0x7FC0)
+    for b, n in enumerate(lens):
+        for t in range(n, 8 * 64):
+            phys = int(osplice.physical_rows([t], host["bt"][b], 64)[0])
+            devs["pool"].view(-1, 576)[phys] = torch.from_numpy(
+                np.full(576, nan, np.uint16).view(np.int16)).view(torch.bfloat16).cuda()
+    scale = 1.0 / math.sqrt(576.0)
+    o, lse = _run(devs, scale, max_len=8 * 64)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    for b in range(len(lens)):
+        o_ref, l_ref, eps = _oracle(host, b, scale)
+        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps).all(), f"seq {b}"
