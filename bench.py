@@ -39,12 +39,31 @@ METRIC = "KV slots relocated/sec (δ-rotate + splice) and achieved HBM GB/s vs p
 MLA_ROW_BYTES = 1152
 
 
-def kernel_source_hash():
+# sources each kernel is built from: a change to any of them makes the stored
+# HBM counters stale (the shared headers and the host side count for all)
+KERNEL_SOURCES = {
+    "reloc_kernel": ["relocate.hip"],
+    "patch_kernel": ["patch.hip"],
+    "mla_decode_kernel": ["decode.hip"],
+}
+SHARED_SOURCES = ["kvr_device.h", "kvr_internal.h", "api.cpp"]
+
+
+def kernel_source_hash(kernel=None):
+    """Hash of the sources of ``kernel`` (key prefix as in KERNEL_SOURCES),
+    or of every source when ``kernel`` is None."""
     p = os.path.join(ROOT, "rope_rotation_splice_amd", "csrc")
+    if kernel is None:
+        files = sorted(f for f in os.listdir(p) if f.endswith((".hip", ".h", ".cpp")))
+    else:
+        own = next((v for k, v in KERNEL_SOURCES.items() if kernel.startswith(k)), None)
+        files = sorted(SHARED_SOURCES + own) if own else sorted(
+            f for f in os.listdir(p) if f.endswith((".hip", ".h", ".cpp")))
     h = hashlib.sha256()
-    for f in sorted(os.listdir(p)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(p, f), "rb").read())
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(p, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "kvreloc.h"), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -58,7 +77,7 @@ def stored_traffic(kernel, workload):
         rec = json.load(open(path)).get(f"{kernel}/{workload}")
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("traffic_bytes_per_launch")
 
