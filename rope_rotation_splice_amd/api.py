@@ -115,9 +115,11 @@ class LowRank:
 _workspaces = {}
 
 
-def _workspace(nbytes, device):
-    """A zero-filled workspace per (device, stream); every call leaves it zeroed."""
-    key = (device.index if device.index is not None else torch.cuda.current_device(),
+def _workspace(nbytes, device, kind):
+    """A workspace per (kind, device, stream).  Kinds never share memory: the
+    splice's must stay zero-filled between calls (each call leaves it so),
+    the decode's holds split partials."""
+    key = (kind, device.index if device.index is not None else torch.cuda.current_device(),
            torch.cuda.current_stream().cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -161,7 +163,7 @@ def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, worksp
             if s is not None:
                 stub_arr[i] = s.c()
     need = lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens, dirs)
-    ws = workspace if workspace is not None else _workspace(need, cache.pf.device)
+    ws = workspace if workspace is not None else _workspace(need, cache.pf.device, "splice")
     st = lib.leyline_splice(ctypes.byref(cache.c), block_tables.data_ptr(), int(block_tables.stride(0)), n,
                             lens, dirs, stub_arr, out, ws.data_ptr(), ws.numel() * ws.element_size(),
                             _stream_handle())
@@ -220,7 +222,7 @@ def mla_decode_rotate_on_read(q_nope, q_rope, cache, layer, block_tables, pendin
     if lse is None:
         lse = torch.empty((b, h), dtype=torch.float32, device=q_nope.device)
     need = int(lib.kvr_decode_workspace_bytes(b, h, int(max_seq_len)))
-    ws = workspace if workspace is not None else _workspace(need, q_nope.device)
+    ws = workspace if workspace is not None else _workspace(need, q_nope.device, "decode")
     st = lib.mla_decode_rotate_on_read(q_nope.data_ptr(), q_rope.data_ptr(), b, h, ctypes.byref(cache.c), int(layer),
                                        block_tables.data_ptr(), pending_delta.data_ptr(), int(block_tables.stride(0)),
                                        seq_lens.data_ptr(), int(max_seq_len), float(scale), out.data_ptr(),

@@ -102,13 +102,22 @@ __device__ __forceinline__ void rot_patch(v4u& lo, v4u& hi, const float2* cs, bo
     }
 }
 
+// Workgroups reach the 8 XCDs round-robin (workgroup b runs on XCD b % 8,
+// each with its own L2).  Every tile of an (item, layer) re-reads that
+// layer's feature-side factors, so each XCD is given a contiguous range of
+// logical workgroups: the tiles of one (item, layer) then share one L2.
+__device__ __forceinline__ int xcd_contiguous(int b, int n) {
+    const int x = b & 7, k = b >> 3, q = n >> 3, r = n & 7;
+    return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
 template <bool INPLACE>
 __global__ __launch_bounds__(kThreads) void patch_kernel(const PatchArgs A) {
     __shared__ float2 s_cs[kPatchMaxPairs];
     __shared__ int32_t s_blk[kMaxTileRows], s_row[kMaxTileRows];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bid = blockIdx.x;
+    const int bid = xcd_contiguous(blockIdx.x, gridDim.x);
     const Pool& P = A.pool;
 
     int it = 0;

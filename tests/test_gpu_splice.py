@@ -144,3 +144,69 @@ def test_single_sequence_workload_with_drift():
     scratch = orope.rotate(k_raw[1800:4096], np.arange(1016, 3312), 1, 64, th)
     rel = np.linalg.norm(got - scratch) / np.linalg.norm(scratch)
     assert rel <= 4.7e-3, rel
+
+
+def test_batched_splice_full_workload_sampled():
+    """The batched-splice workload at full size (64 sequences x 32768 slots x
+    61 layers, 64-row blocks, 147 GB resident), in the launch configuration
+    the benchmark times.  Four (sequence, layer) slabs are compared with the
+    oracle over the whole new length: moved rows, stub rows, untouched prefix."""
+    import torch
+    import rope_rotation_splice_amd as rrs
+    from oracle import splice as osplice, tolerance
+    w = kvsynth.batched_splice()
+    L = w.shape.n_layers
+    pool = torch.empty((L, w.n_blocks, w.block_size, 576), dtype=torch.bfloat16, device="cuda")
+    kvsynth.fill_normal_(pool, 3, 1)
+    cache = rrs.KVCache.mla(pool)
+    bt = torch.from_numpy(w.block_tables).cuda()
+    stubs_t, stubs = [], []
+    for b in range(w.n_seq):
+        st = torch.empty((L, int(w.directives[b, 2]), 576), dtype=torch.bfloat16, device="cuda")
+        kvsynth.fill_normal_(st, 3, 2, b)
+        stubs_t.append(st)
+        stubs.append(rrs.Rows(st[..., :512], st[..., 512:]))
+    samples = [(0, 0), (29, 30), (63, 60), (13, 7)]
+    h16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def rows(b, l):
+        n = int(w.seq_lens[b])
+        phys = osplice.physical_rows(np.arange(n), w.block_tables[b], w.block_size)
+        return h16(pool[l].reshape(-1, 576)[torch.from_numpy(phys).cuda()])
+
+    before = {s: rows(*s) for s in samples}
+    new_lens, st = rrs.leyline_splice(cache, bt, w.seq_lens.tolist(),
+                                      [tuple(int(x) for x in d) for d in w.directives], stubs)
+    torch.cuda.synchronize()
+    assert st == 0 and rrs.device_errors() == 0
+    th = orope.inv_freq(64, 10000.0)
+    for (b, l) in samples:
+        d = w.directives[b]
+        p = osplice.plan(int(w.seq_lens[b]), int(d[0]), int(d[1]), int(d[2]), int(d[3]))
+        assert new_lens[b] == p.new_len
+        r0 = before[(b, l)]
+        stub = h16(stubs_t[b][l])
+        ex = osplice.splice_sequence(p, r0[:, :512], r0[:, 512:], stub[:, :512], stub[:, 512:], 1, 64, th,
+                                     rope_is_bf16=True)
+        phys = osplice.physical_rows(np.arange(p.new_len), w.block_tables[b], w.block_size)
+        got = h16(pool[l].reshape(-1, 576)[torch.from_numpy(phys).cuda()])
+        assert (got[:, :512] == ex.pf_bits).all(), f"seq {b} layer {l}: position-free words differ"
+        plain = ~ex.rotated
+        assert (got[plain, 512:] == ex.rope_bits[plain]).all(), f"seq {b} layer {l}: unrotated rotary words differ"
+        ok = tolerance.bf16_close(got[ex.rotated, 512:], ex.rope_ref[ex.rotated], ex.pair_norm[ex.rotated])
+        assert ok.all(), f"seq {b} layer {l}: {(~ok).sum()} rotated words outside tolerance"
+
+
+def test_splice_after_decode_on_the_same_stream():
+    """A decode's split partials must not land in the splice's workspace,
+    whose ticket counters are expected to be zero at every call."""
+    import math
+    import torch
+    import rope_rotation_splice_amd as rrs
+    from tests.test_gpu_decode import _setup
+    host, devs = _setup(2, 128, [3000, 4000], bt_stride=64, keys=(11,))
+    rrs.mla_decode_rotate_on_read(devs["qn"], devs["qr"], devs["cache"], 0, devs["bt"], devs["pend"],
+                                  devs["lens"], 1.0 / math.sqrt(576.0), max_seq_len=64 * 64)
+    torch.cuda.synchronize()
+    assert rrs.device_errors() == 0
+    _run(rc.MLA, 2, 4, 16, [(64, 10, 30, 5, 0), (60, 0, 2, 4, 0)], keys=(12,))
