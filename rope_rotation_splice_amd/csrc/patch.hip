@@ -157,13 +157,13 @@ __global__ __launch_bounds__(kThreads) void patch_kernel(const PatchArgs A) {
     // Work of a wave: whole rotary heads (every 32-feature group of the head,
     // so the two 64-byte halves of each 128-byte line are read and written by
     // the same wave in consecutive instructions) and pairs of position-free
-    // groups (128 bytes).  Sub-tiles of 16 tokens are taken two at a time:
+    // groups (128 bytes).  The tile's four sub-tiles of 16 tokens are taken at once:
     // all their loads are issued before the matrix cores run.  For rank <= 16
     // (one K block) the U rows of this lane's token stay in registers for the
     // whole tile and each group's factor rows are loaded once per unit; larger
     // ranks walk the K blocks with operand reloads (group_patch).
     constexpr int NS = kPatchTileRows / 16;
-    constexpr int NB = 2;                      // sub-tiles per batch
+    constexpr int NB = 4;                      // sub-tiles per batch
     constexpr int MAXG = 4;                    // groups per unit (a 128-dim head)
 
     auto load_u = [&](const float* Ul, int rank, v4f* ub) {
