@@ -32,6 +32,8 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
                    figures of the single-sequence splice workload.
 * ``gather``    -- pinned: brute-force paged maps, O(n^2) overlap check.
 * ``patch``     -- pinned: textbook GEMM on asymmetric shapes; memory fractions.
+* ``lazy``      -- pinned: slot map equal to the eager splice's, block
+                   conservation, one-rotation composition.
 * ``decode``    -- pinned: textbook softmax attention on explicitly rotated keys,
                    needle retrieval, brute-force per-key loop on tiny inputs.
 * FORGET mode   -- status and truncated length only; parity unpinned beyond that
@@ -40,4 +42,4 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
                    reuse operator is written; parity unpinned beyond that formula.
 """
 
-from . import bf16, rope, splice, gather, patch, decode, tolerance  # noqa: F401
+from . import bf16, rope, splice, gather, patch, decode, lazy, tolerance  # noqa: F401
