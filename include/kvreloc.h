@@ -257,6 +257,50 @@ kvr_status mla_decode_rotate_on_read(const void* q_nope, const void* q_rope,
                                      hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * leyline_splice_lazy -- a block-aligned AMORTIZE splice done as an edit of
+ * the block table and of the per-block pending shifts; no KV byte moves.
+ * (Leyline, sections 2.2-2.3: the downstream slots are re-indexed and owe
+ * R(Delta); rotations compose, so Delta is added to each moved block's
+ * pending shift and applied once, on read, by mla_decode_rotate_on_read --
+ * Irminsul, sections 2.2 and 4.)  Repeated splices then round the keys once
+ * instead of once per splice.
+ *
+ * Per sequence b with directive (s_start, s_end, r_len, mode), B = block_size,
+ * Delta = r_len - (s_end - s_start), all of s_start, s_end, r_len multiples
+ * of B, N = seq_lens[b]:
+ *   - logical blocks below s_start/B keep their entries;
+ *   - blocks s_start/B .. s_start/B + r_len/B - 1 take the next r_len/B ids
+ *     of d_stub_blocks (blocks the caller has prefilled with R at its final
+ *     positions) with pending shift 0;
+ *   - blocks up to ceil((N + Delta)/B) - 1 take the entry of old block
+ *     k - Delta/B, its pending shift increased by Delta;
+ *   - entries from ceil((N + Delta)/B) up to ceil(N/B) - 1 become -1 with
+ *     shift 0; entries past both counts are left alone;
+ *   - the ids of old blocks s_start/B .. s_end/B - 1 are written to
+ *     d_freed_blocks, sequences concatenated in order; the caller owns them.
+ * FORGET changes nothing: KVR_FORGET_NEEDS_PREFILL, new_lens[b] = s_start.
+ *   block_size      : slots per block, > 0
+ *   d_block_tables  : device int32 [n_seq][bt_stride], edited in place
+ *   d_pending_delta : device int32 [n_seq][bt_stride], edited in place
+ *   bt_stride       : 1 .. 8192 blocks; capacity = bt_stride * block_size
+ *   seq_lens, dirs  : host [n_seq]
+ *   d_stub_blocks   : device int32 [sum of r_len/B]; NULL when that sum is 0
+ *   d_freed_blocks  : device int32 out [sum of (s_end - s_start)/B]; NULL when 0
+ *   new_lens        : host out [n_seq]
+ * A shift that would leave the int32 range raises KVR_DEV_RANGE (see
+ * kvr_device_errors) and that entry keeps its unshifted value.
+ * Errors: KVR_E_ARG (null pointer, block_size <= 0, bt_stride outside
+ * 1..8192, a range not on block boundaries, unknown mode), KVR_E_RANGE
+ * (0 <= s_start <= s_end <= N <= capacity violated, r_len < 0),
+ * KVR_E_CAPACITY (N + Delta > capacity), KVR_E_HIP.  Nothing is enqueued
+ * unless every sequence validates.
+ * ---------------------------------------------------------------------- */
+kvr_status leyline_splice_lazy(int32_t block_size, int32_t* d_block_tables, int32_t* d_pending_delta,
+                               int32_t bt_stride, int32_t n_seq, const int64_t* seq_lens,
+                               const kvr_directive* dirs, const int32_t* d_stub_blocks,
+                               int32_t* d_freed_blocks, int64_t* new_lens, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Utilities.
  * ---------------------------------------------------------------------- */
 int32_t     kvr_abi_version(void);

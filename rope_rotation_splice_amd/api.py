@@ -171,6 +171,39 @@ def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, worksp
     return np.array(out[:n], dtype=np.int64), st
 
 
+def leyline_splice_lazy(block_tables, pending_delta, block_size, seq_lens, directives, stub_blocks=None):
+    """Block-aligned AMORTIZE splices done as edits of the block table and of
+    the per-block pending shifts (no KV bytes move); decode with
+    mla_decode_rotate_on_read applies the composed shift on read.
+
+    block_tables, pending_delta: int32 device tensors [n_seq, bt_stride],
+    edited in place.  stub_blocks: int32 device tensor with the r_len /
+    block_size prefilled block ids of every sequence, concatenated in order.
+    Returns (new_lens int64 array, freed int32 device tensor, status).
+    """
+    lib = _abi.load()
+    dirs, n = _directives(directives)
+    for t in (block_tables, pending_delta):
+        if t.dtype != torch.int32 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("block_tables and pending_delta must be int32 [n_seq, blocks] with unit last stride")
+    if pending_delta.shape != block_tables.shape or pending_delta.stride(0) != block_tables.stride(0):
+        raise ValueError("pending_delta must match block_tables in shape and row stride")
+    d = np.asarray(directives, dtype=np.int64).reshape(-1, 4)
+    amort = d[:, 3] == 0
+    n_free = int(((d[:, 1] - d[:, 0]) // block_size)[amort].sum()) if n else 0
+    if stub_blocks is not None and (stub_blocks.dtype != torch.int32 or not stub_blocks.is_contiguous()):
+        raise ValueError("stub_blocks must be a contiguous int32 tensor")
+    freed = torch.empty(max(1, n_free), dtype=torch.int32, device=block_tables.device)
+    lens = (ctypes.c_int64 * max(1, n))(*[int(x) for x in seq_lens])
+    out = (ctypes.c_int64 * max(1, n))()
+    st = lib.leyline_splice_lazy(int(block_size), block_tables.data_ptr(), pending_delta.data_ptr(),
+                                 int(block_tables.stride(0)), n, lens, dirs,
+                                 stub_blocks.data_ptr() if stub_blocks is not None and stub_blocks.numel() else None,
+                                 freed.data_ptr() if n_free else None, out, _stream_handle())
+    _check("leyline_splice_lazy", st)
+    return np.array(out[:n], dtype=np.int64), freed[:n_free], st
+
+
 def kv_relocate_gather(cache, block_table, entries, p_targets, patch_rope=None, patch_pf=None):
     """Gather registry entries (list of Rows) into one paged destination
     sequence at logical slots p_targets[i] + t; optional rank-m patches

@@ -308,8 +308,10 @@ kvr_status kvr_device_errors(uint32_t* flags) {
     const uint32_t v = read_and_clear_errors_relocate();
     const uint32_t w = read_and_clear_errors_patch();
     const uint32_t x = read_and_clear_errors_decode();
-    if (v == 0xffffffffu || w == 0xffffffffu || x == 0xffffffffu) return hip_fail(hipErrorUnknown);
-    *flags = v | w | x;
+    const uint32_t y = read_and_clear_errors_lazy();
+    if (v == 0xffffffffu || w == 0xffffffffu || x == 0xffffffffu || y == 0xffffffffu)
+        return hip_fail(hipErrorUnknown);
+    *flags = v | w | x | y;
     return KVR_OK;
 }
 
@@ -589,6 +591,82 @@ kvr_status mla_decode_rotate_on_read(const void* q_nope, const void* q_rope, int
     std::memcpy(a.omega, omega, sizeof(a.omega));
     hipError_t e = launch_decode(a, (uint16_t*)out, lse, stream);
     return e == hipSuccess ? KVR_OK : hip_fail(e);
+}
+
+kvr_status leyline_splice_lazy(int32_t block_size, int32_t* d_block_tables, int32_t* d_pending_delta,
+                               int32_t bt_stride, int32_t n_seq, const int64_t* seq_lens,
+                               const kvr_directive* dirs, const int32_t* d_stub_blocks,
+                               int32_t* d_freed_blocks, int64_t* new_lens, hipStream_t stream) {
+    if (block_size <= 0 || bt_stride <= 0 || bt_stride > kLazyMaxBlocks || n_seq < 0) return KVR_E_ARG;
+    if (n_seq > 0 && (!d_block_tables || !d_pending_delta || !seq_lens || !dirs || !new_lens)) return KVR_E_ARG;
+    const int64_t B = block_size, cap = (int64_t)bt_stride * B;
+    // validate everything first: no table is touched unless all sequences pass
+    int64_t n_stub = 0, n_free = 0;
+    bool forget = false;
+    std::vector<int64_t> out(n_seq);
+    for (int32_t b = 0; b < n_seq; ++b) {
+        const kvr_directive& d = dirs[b];
+        const int64_t N = seq_lens[b];
+        if (d.mode != KVR_AMORTIZE && d.mode != KVR_FORGET) return KVR_E_ARG;
+        if (N < 0 || N > cap || d.s_start < 0 || d.s_start > d.s_end || d.s_end > N || d.r_len < 0)
+            return KVR_E_RANGE;
+        if (d.mode == KVR_FORGET) {
+            out[b] = d.s_start;
+            forget = true;
+            continue;
+        }
+        if (d.s_start % B || d.s_end % B || d.r_len % B) return KVR_E_ARG;
+        const int64_t delta = d.r_len - (d.s_end - d.s_start);
+        if (N + delta > cap) return KVR_E_CAPACITY;
+        out[b] = N + delta;
+        n_stub += d.r_len / B;
+        n_free += (d.s_end - d.s_start) / B;
+    }
+    if ((n_stub > 0 && !d_stub_blocks) || (n_free > 0 && !d_freed_blocks)) return KVR_E_ARG;
+    if (n_stub >= ((int64_t)1 << 31) || n_free >= ((int64_t)1 << 31)) return KVR_E_RANGE;
+
+    LazyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.bt = d_block_tables;
+    a.pend = d_pending_delta;
+    a.stubs = d_stub_blocks;
+    a.freed = d_freed_blocks;
+    a.bt_stride = bt_stride;
+    a.block_size = block_size;
+    int32_t stub_off = 0, free_off = 0;
+    auto flush = [&]() -> kvr_status {
+        hipError_t e = launch_lazy(a, stream);
+        a.n_seq = 0;
+        return e == hipSuccess ? KVR_OK : hip_fail(e);
+    };
+    for (int32_t b = 0; b < n_seq; ++b) {
+        const kvr_directive& d = dirs[b];
+        if (d.mode == KVR_FORGET) continue;
+        const int64_t N = seq_lens[b];
+        LazySeq s;
+        s.row = b;
+        s.n_old = (int32_t)((N + B - 1) / B);
+        s.n_new = (int32_t)((out[b] + B - 1) / B);
+        s.s0b = (int32_t)(d.s_start / B);
+        s.s1b = (int32_t)(d.s_end / B);
+        s.rb = (int32_t)(d.r_len / B);
+        s.delta = (int32_t)(out[b] - N);
+        s.stub_off = stub_off;
+        s.free_off = free_off;
+        stub_off += s.rb;
+        free_off += s.s1b - s.s0b;
+        a.seqs[a.n_seq++] = s;
+        if (a.n_seq == kLazyMaxSeq) {
+            kvr_status st = flush();
+            if (st != KVR_OK) return st;
+        }
+    }
+    if (a.n_seq > 0) {
+        kvr_status st = flush();
+        if (st != KVR_OK) return st;
+    }
+    for (int32_t b = 0; b < n_seq; ++b) new_lens[b] = out[b];
+    return forget ? KVR_FORGET_NEEDS_PREFILL : KVR_OK;
 }
 
 }  // extern "C"

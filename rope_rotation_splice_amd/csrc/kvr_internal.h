@@ -116,6 +116,28 @@ struct DecodeArgs {
     double omega[32];
 };
 
+// Block-table splice (lazy.hip): one workgroup per sequence.
+constexpr int kLazyMaxBlocks = 8192;  // table entries a workgroup stages in LDS
+constexpr int kLazyMaxSeq = 96;       // sequences per launch
+
+struct LazySeq {
+    int32_t row;                      // sequence index (row of the tables)
+    int32_t n_old, n_new;             // blocks before / after
+    int32_t s0b, s1b, rb;             // replaced range and stub count, in blocks
+    int32_t delta;                    // slots (a multiple of the block size)
+    int32_t stub_off, free_off;       // offsets into the stub / freed id lists
+};
+
+struct LazyArgs {
+    int32_t* bt;
+    int32_t* pend;
+    const int32_t* stubs;
+    int32_t* freed;
+    int32_t bt_stride, block_size, n_seq;
+    LazySeq seqs[kLazyMaxSeq];
+};
+static_assert(sizeof(LazyArgs) <= 4000, "lazy splice arguments too large");
+
 // Kernel arguments must stay within the 4 KB kernarg budget.
 static_assert(sizeof(RelocArgs) <= 4000, "relocation kernel arguments too large");
 
@@ -132,5 +154,8 @@ uint32_t read_and_clear_errors_patch();
 // Decode (decode.hip): split kernel + combine kernel.
 hipError_t launch_decode(const DecodeArgs& a, uint16_t* out, float* lse, hipStream_t s);
 uint32_t read_and_clear_errors_decode();
+// Block-table splice (lazy.hip).
+hipError_t launch_lazy(const LazyArgs& a, hipStream_t s);
+uint32_t read_and_clear_errors_lazy();
 
 }  // namespace kvr

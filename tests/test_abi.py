@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_functions_exported():
     lib = _abi.load()
     names = declared_functions()
-    assert {"leyline_splice", "kv_relocate_gather", "kv_patch_lowrank", "mla_decode_rotate_on_read"} <= set(names)
+    assert {"leyline_splice", "kv_relocate_gather", "kv_patch_lowrank", "mla_decode_rotate_on_read",
+            "leyline_splice_lazy"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_abi.SIGNATURES), "binding and header disagree"
@@ -131,3 +132,38 @@ def test_gather_validation_errors():
     bad.pf = FAKE + 4
     assert gather(c, [bad], [0]) == -1
     assert gather(c, [rows(10, base=-(1 << 40))], [0]) == -2       # shift does not fit 32 bits
+
+
+def lazy(dirs, lens, B=64, bt_stride=512, stubs=FAKE, freed=FAKE):
+    lib = _abi.load()
+    n = len(dirs)
+    D = (_abi.kvr_directive * max(1, n))(*[_abi.kvr_directive(*d, 0) for d in dirs])
+    Ls = (ctypes.c_int64 * max(1, n))(*lens)
+    out = (ctypes.c_int64 * max(1, n))()
+    st = lib.leyline_splice_lazy(B, FAKE, FAKE, bt_stride, n, Ls, D, stubs, freed, out, None)
+    return st, out
+
+
+@pytest.mark.parametrize("d, n, kw, code", [
+    ((65, 128, 64, 0), 4096, {}, -1),                        # s_start off the block grid
+    ((64, 130, 64, 0), 4096, {}, -1),                        # s_end off the grid
+    ((64, 128, 65, 0), 4096, {}, -1),                        # r_len off the grid
+    ((64, 128, 64, 0), 4096, {"B": 0}, -1),
+    ((64, 128, 64, 0), 4096, {"bt_stride": 8193}, -1),
+    ((64, 128, 64, 0), 4096, {"stubs": None}, -1),           # stubs needed
+    ((64, 128, 64, 0), 4096, {"freed": None}, -1),           # freed list needed
+    ((64, 128, 64, 2), 4096, {}, -1),                        # unknown mode
+    ((128, 64, 64, 0), 4096, {}, -2),                        # s_start > s_end
+    ((64, 128, 64, 0), 40000, {}, -2),                       # N beyond capacity 512 * 64
+    ((0, 0, 128, 0), 512 * 64, {}, -3),                      # growth beyond capacity
+])
+def test_lazy_validation_errors(d, n, kw, code):
+    st, _ = lazy([d], [n], **kw)
+    assert st == code
+
+
+def test_lazy_forget_and_empty_need_no_launch():
+    st, out = lazy([(128, 256, 64, 1)], [4096])
+    assert st == 1 and out[0] == 128
+    st, _ = lazy([], [])
+    assert st == 0

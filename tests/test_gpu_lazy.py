@@ -1,0 +1,151 @@
+"""Parity of leyline_splice_lazy (HIP, through the C ABI): the edited block
+tables and pending shifts are compared integer for integer with the oracle,
+and a rotate-on-read decode over the lazily spliced cache with the fp64
+oracle on the composed keys."""
+
+import math
+
+import numpy as np
+import pytest
+
+import kvsynth
+from oracle import bf16 as ob, decode as odec, lazy as olazy, rope as orope, splice as osplice, tolerance
+
+pytestmark = pytest.mark.gpu
+
+TH = orope.inv_freq(64, 10000.0)
+
+
+def _tables(seqs, bt_stride, B, n_blocks, keys):
+    r = kvsynth.rng(21, *keys)
+    perm = r.permutation(n_blocks).astype(np.int32)
+    n = len(seqs)
+    bt = perm[: n * bt_stride].reshape(n, bt_stride).copy()
+    pend = r.integers(-100000, 100000, size=(n, bt_stride), endpoint=True).astype(np.int32)
+    spare = perm[n * bt_stride:]
+    return bt, pend, spare
+
+
+def _apply(bt_d, pd_d, B, lens, dirs, stubs):
+    import torch
+    import rope_rotation_splice_amd as rrs
+    st_t = torch.from_numpy(np.asarray(stubs, np.int32)).cuda() if len(stubs) else None
+    new_lens, freed, st = rrs.leyline_splice_lazy(bt_d, pd_d, B, lens, dirs, st_t)
+    torch.cuda.synchronize()
+    assert rrs.device_errors() == 0
+    return new_lens, freed.cpu().numpy(), st
+
+
+def _oracle_all(bt, pend, B, lens, dirs, stubs):
+    bt2, pd2, freed, out = bt.astype(np.int64).copy(), pend.astype(np.int64).copy(), [], []
+    off = 0
+    for b, (n, d) in enumerate(zip(lens, dirs)):
+        if d[3] == osplice.FORGET:
+            out.append(d[0])
+            continue
+        k = d[2] // B
+        nb, npd, fr, nl = olazy.lazy_splice_tables(bt[b], pend[b], n, d[0], d[1], d[2], B, stubs[off:off + k])
+        off += k
+        bt2[b], pd2[b] = nb, npd
+        freed += list(fr)
+        out.append(nl)
+    return bt2, pd2, np.array(freed, np.int64), np.array(out)
+
+
+@pytest.mark.parametrize("B", [4, 64])
+def test_lazy_tables_bit_exact(B):
+    import torch
+    bt_stride = 40
+    seqs = [  # (N, s_start, s_end, r_len, mode) in blocks * B, plus tails
+        (30 * B + (3 if B > 4 else 1), 5 * B, 9 * B, 2 * B, 0),      # shrink, partial last block
+        (25 * B, 3 * B, 4 * B, 3 * B, 0),                           # growth
+        (20 * B, 0, 20 * B, 0, 0),                                  # everything replaced by nothing
+        (18 * B, 7 * B, 12 * B, B, 1),                              # FORGET: unchanged
+        (10 * B, 10 * B, 10 * B, 30 * B, 0),                        # append at the end, fills capacity
+        (12 * B, 4 * B, 4 * B, 0, 0),                               # empty range, no stub: identity
+    ]
+    bt, pend, spare = _tables(seqs, bt_stride, B, 6 * bt_stride + 64, keys=(B,))
+    lens = [s[0] for s in seqs]
+    dirs = [s[1:] for s in seqs]
+    n_stub = sum(d[2] // B for d in dirs if d[3] == 0)
+    stubs = spare[:n_stub]
+    bt_d, pd_d = torch.from_numpy(bt.copy()).cuda(), torch.from_numpy(pend.copy()).cuda()
+    new_lens, freed, st = _apply(bt_d, pd_d, B, lens, dirs, stubs)
+    bt2, pd2, fr2, nl2 = _oracle_all(bt, pend, B, lens, dirs, stubs)
+    assert st == 1                                                  # one FORGET in the batch
+    assert list(new_lens) == list(nl2)
+    assert (bt_d.cpu().numpy() == bt2).all()
+    assert (pd_d.cpu().numpy() == pd2).all()
+    assert list(freed) == list(fr2)
+
+
+def test_lazy_shift_overflow_flagged():
+    import torch
+    import rope_rotation_splice_amd as rrs
+    B = 64
+    bt = np.arange(8, dtype=np.int32).reshape(1, 8)
+    pend = np.full((1, 8), 2 ** 31 - 10, np.int32)
+    bt_d, pd_d = torch.from_numpy(bt).cuda(), torch.from_numpy(pend).cuda()
+    st_t = torch.tensor([100], dtype=torch.int32).cuda()
+    rrs.leyline_splice_lazy(bt_d, pd_d, B, [4 * B], [(0, 0, B, 0)], st_t)   # +64 overflows int32
+    torch.cuda.synchronize()
+    assert rrs.device_errors() & 8
+    assert (pd_d.cpu().numpy()[0, 1:5] == 2 ** 31 - 10).all()
+
+
+def _decode_check(pool_h, pool_d, bt_d, pd_d, lens, qn, qr, scale):
+    import torch
+    import rope_rotation_splice_amd as rrs
+    cache = rrs.KVCache.mla(pool_d)
+    out, lse = rrs.mla_decode_rotate_on_read(qn[1], qr[1], cache, 0, bt_d, pd_d,
+                                             torch.tensor(lens, dtype=torch.int32).cuda(), scale,
+                                             max_seq_len=bt_d.shape[1] * 64)
+    torch.cuda.synchronize()
+    assert rrs.device_errors() == 0
+    o = ob.to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    lse = lse.cpu().numpy().astype(np.float64)
+    bt, pd = bt_d.cpu().numpy(), pd_d.cpu().numpy()
+    for b, n in enumerate(lens):
+        phys = osplice.physical_rows(np.arange(n), bt[b], 64)
+        rows = pool_h[phys]
+        kr = ob.to_f64(rows[:, 512:])
+        d = odec.token_deltas(pd[b], n, 64)
+        qrb = ob.to_f64(qr[0][b])
+        o_ref, l_ref = odec.mla_decode(ob.to_f64(qn[0][b]), qrb, ob.to_f64(rows[:, :512]), kr, d, scale, TH,
+                                       round_keys=True)
+        eps = odec.score_bound(qrb, kr, d, scale, TH)
+        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps).all(), f"sequence {b}"
+
+
+def test_lazy_splice_then_decode_composes():
+    """Two successive lazy splices, each followed by a rotate-on-read decode
+    checked against the oracle: the pending shift carries both splices'
+    Deltas and the key is rotated once, on read."""
+    import torch
+    B, bt_stride, heads = 64, 48, 128
+    seqs = [(30 * B + 17, 5 * B, 9 * B, 2 * B, 0), (25 * B, 3 * B, 4 * B, 3 * B, 0)]
+    n_blocks = 2 * bt_stride + 32
+    bt, pend, spare = _tables(seqs, bt_stride, B, n_blocks, keys=(3,))
+    r = kvsynth.rng(21, 4)
+    pool_h = kvsynth.bf16_normal(r, (n_blocks * 64, 576))
+    qn_h = kvsynth.bf16_normal(r, (2, heads, 512))
+    qr_h = kvsynth.bf16_normal(r, (2, heads, 64))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    pool_d = dev(pool_h).reshape(1, n_blocks, 64, 576)
+    qn, qr = (qn_h, dev(qn_h)), (qr_h, dev(qr_h))
+    bt_d, pd_d = torch.from_numpy(bt.copy()).cuda(), torch.from_numpy(pend.copy()).cuda()
+    scale = 1.0 / math.sqrt(576.0)
+    lens = [s[0] for s in seqs]
+    _decode_check(pool_h, pool_d, bt_d, pd_d, lens, qn, qr, scale)
+    used = 0
+    for step_dirs in ([s[1:] for s in seqs], [(2 * B, 6 * B, B, 0), (10 * B, 11 * B, 2 * B, 0)]):
+        n_stub = sum(d[2] // B for d in step_dirs)
+        stubs = spare[used:used + n_stub]
+        used += n_stub
+        bt_h, pd_h = bt_d.cpu().numpy(), pd_d.cpu().numpy()
+        new_lens, freed, st = _apply(bt_d, pd_d, B, lens, step_dirs, stubs)
+        bt2, pd2, fr2, nl2 = _oracle_all(bt_h, pd_h, B, lens, step_dirs, stubs)
+        assert st == 0 and list(new_lens) == list(nl2)
+        assert (bt_d.cpu().numpy() == bt2).all() and (pd_d.cpu().numpy() == pd2).all()
+        lens = [int(x) for x in new_lens]
+        _decode_check(pool_h, pool_d, bt_d, pd_d, lens, qn, qr, scale)
