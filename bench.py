@@ -279,6 +279,70 @@ class SpliceBatched:
                           f"generation excluded, numpy fp64, one process"}
 
 
+class SpliceLazy:
+    """The batched-splice shape (64 sequences x 32768 slots, 64-row blocks)
+    with each directive widened to block boundaries (s_start down, s_end and
+    |R| up), done as block-table and pending-shift edits: no KV byte moves.
+    Slots counted are the downstream slots re-indexed per step."""
+    name = "lazy_splice"
+    kernel = "lazy_kernel"
+
+    def __init__(self):
+        import kvsynth
+        self.w = kvsynth.batched_splice()
+        B = self.w.block_size
+        d = self.w.directives
+        s0 = d[:, 0] // B * B
+        s1 = -(-d[:, 1] // B) * B
+        rl = -(-d[:, 2] // B) * B
+        self.dirs = [(int(a), int(b), int(c), 0) for a, b, c in zip(s0, s1, rl)]
+        n = self.w.seq_lens.astype(np.int64)
+        self.slots = int((n - s1).sum())
+        nb_old = -(-n // B)
+        nb_new = -(-(n + rl - (s1 - s0)) // B)
+        # tables: both rows read up to the old count, written from s_start on;
+        # stub ids read, freed ids written
+        self.bytes = int((8 * nb_old + 8 * (np.maximum(nb_old, nb_new) - s0 // B) + 4 * (rl // B)
+                          + 4 * ((s1 - s0) // B)).sum())
+        self.launches = 1
+        self.config = {"workload": "leyline_lazy_splices", "sequences": self.w.n_seq, "slots": self.w.capacity,
+                       "block_size": B, "directives": "batched-splice draws widened to block boundaries",
+                       "slots_per_step": self.slots, "kv_bytes_moved": 0}
+
+    def setup(self):
+        import torch
+        import rope_rotation_splice_amd as rrs
+        w = self.w
+        self.bt = torch.from_numpy(w.block_tables.copy()).cuda()
+        self.pend = torch.zeros_like(self.bt)
+        n_stub = sum(d[2] // w.block_size for d in self.dirs)
+        self.stubs = torch.arange(w.n_blocks, w.n_blocks + n_stub, dtype=torch.int32, device="cuda")
+        self.lens = w.seq_lens.tolist()
+        self.rrs = rrs
+
+    def step(self):
+        # the same directives on the same lengths each step: same table work
+        self.rrs.leyline_splice_lazy(self.bt, self.pend, self.w.block_size, self.lens, self.dirs, self.stubs)
+
+    def cpu_baseline(self, budget_s):
+        from oracle import lazy as olazy
+        w = self.w
+        B = w.block_size
+        pend = np.zeros(w.block_tables.shape[1], np.int64)
+        rows, spent, units = 0, 0.0, 0
+        stub = np.arange(64)
+        while spent < budget_s:
+            for b, d in enumerate(self.dirs):
+                t0 = time.perf_counter()
+                olazy.lazy_splice_tables(w.block_tables[b], pend, int(w.seq_lens[b]), d[0], d[1], d[2], B,
+                                         stub[: d[2] // B])
+                spent += time.perf_counter() - t0
+                rows += int(w.seq_lens[b]) - d[1]
+                units += 1
+        return {"value": rows / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
+                "sample": f"{units} sequence table edits (the step's 64, repeated), numpy, one process"}
+
+
 class GqaPatch:
     """Kamera GQA relocation with its rank-16 patch, fused into one gather:
     16 chunks x 1024 tokens, 32 layers, K and V of 8 x 128 bf16, delta ~
@@ -473,7 +537,8 @@ class Copy:
         return None
 
 
-WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "gqa_patch": GqaPatch,
+WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "splice_lazy": SpliceLazy,
+             "gqa_patch": GqaPatch,
              "decode": Decode, "decode_zero_delta": lambda: Decode(zero_delta=True), "copy": Copy}
 
 
