@@ -70,6 +70,7 @@ __device__ uint32_t g_errors_decode;
 namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -458,41 +459,91 @@ void mla_decode_kernel(const DecodeArgs A) {
     }
 }
 
-// Merge the splits of one (sequence, head group): O = sum_s 2^(m_s - M) O_s / L,
-// L = sum_s 2^(m_s - M) l_s, LSE = ln 2 * (M + log2 L).  One thread per
-// (lane-native position) of a wave's 32 heads x 512 features.
-__global__ __launch_bounds__(256) void mla_decode_combine(const DecodeArgs A, uint16_t* out, float* lse) {
-    const int n_waves = A.heads / 32;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;     // over b, wave, f, r, lane
-    const int64_t per_b = (int64_t)n_waves * 16 * 16 * 64;
-    if (idx >= (int64_t)gridDim.x * 256 || idx >= per_b * A.batch) return;
-    const int b = (int)(idx / per_b);
-    int64_t rem = idx - b * per_b;
-    const int wave = (int)(rem / (16 * 16 * 64));
-    rem -= (int64_t)wave * (16 * 16 * 64);
-    const int f = (int)(rem / (16 * 64));
-    const int r = (int)((rem / 64) % 16);
-    const int lane = (int)(rem % 64);
-    const int head = wave * 32 + (lane & 31);
-    const int feat = 32 * f + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+// Merge the splits: O = sum_s 2^(m_s - M) O_s / L, L = sum_s 2^(m_s - M) l_s,
+// LSE = ln 2 * (M + log2 L).  One workgroup per (sequence, wave's 32 heads,
+// quarter of the 512 features = 4 feature tiles).  Partials are read in
+// their lane-native order as float4 (coalesced), the merged values go
+// through LDS as [head][feature] bf16, and leave as 256-byte row segments.
+constexpr int kCombineSplitChunk = 256;     // split weights staged in LDS at a time
 
-    const float2* pm = reinterpret_cast<const float2*>(A.part_ml);
-    float M = kNegInf;
-    for (int s = 0; s < A.n_split; ++s) M = fmaxf(M, pm[((int64_t)b * A.n_split + s) * A.heads + head].x);
-    float L = 0.f, o = 0.f;
-    if (M != kNegInf) {
-        for (int s = 0; s < A.n_split; ++s) {
-            const float2 ml = pm[((int64_t)b * A.n_split + s) * A.heads + head];
-            if (ml.x == kNegInf) continue;
-            const float w = exp2f(ml.x - M);
-            L += w * ml.y;
-            o += w * A.part_o[(((int64_t)b * A.n_split + s) * n_waves + wave) * (16 * 16 * 64) + rem];
+__global__ __launch_bounds__(256) void mla_decode_combine(const DecodeArgs A, uint16_t* out, float* lse) {
+    __shared__ float s_w[kCombineSplitChunk][32];
+    __shared__ float s_M[32], s_L[32];
+    __shared__ uint16_t s_o[32][128 + 8];
+    const int tid = threadIdx.x;
+    const int n_waves = A.heads / 32;
+    const int q = blockIdx.x & 3;                        // feature quarter: tiles 4q .. 4q+3
+    const int bw = blockIdx.x >> 2;
+    const int b = bw / n_waves, wave = bw - b * n_waves;
+    const float2* pm = reinterpret_cast<const float2*>(A.part_ml) + (int64_t)b * A.n_split * A.heads + wave * 32;
+
+    if (tid < 32) {
+        float M = kNegInf;
+        for (int s = 0; s < A.n_split; ++s) M = fmaxf(M, pm[(int64_t)s * A.heads + tid].x);
+        float L = 0.f;
+        if (M != kNegInf)
+            for (int s = 0; s < A.n_split; ++s) {
+                const float2 ml = pm[(int64_t)s * A.heads + tid];
+                if (ml.x != kNegInf) L += exp2f(ml.x - M) * ml.y;
+            }
+        s_M[tid] = M;
+        s_L[tid] = L;
+    }
+    // this thread's float4 units u = tid + 256 k (k < 4) of the quarter's
+    // 4 x 16 x 64 lane-native floats: element e = 4u + i has tile f = e / 1024,
+    // row r = (e / 64) % 16, lane (e % 64)
+    v4f acc[4] = {};
+    const int64_t base0 = (((int64_t)b * A.n_split) * n_waves + wave) * (16 * 16 * 64) + (int64_t)q * 4 * 1024;
+    const int64_t split_stride = (int64_t)n_waves * 16 * 16 * 64;
+    for (int c0 = 0; c0 < A.n_split; c0 += kCombineSplitChunk) {
+        const int nc = min(kCombineSplitChunk, A.n_split - c0);
+        __syncthreads();                                   // s_M ready; previous chunk consumed
+        for (int e = tid; e < nc * 32; e += 256) {
+            const int s = e >> 5, h = e & 31;
+            const float m = pm[(int64_t)(c0 + s) * A.heads + h].x;
+            s_w[s][h] = (m == kNegInf || s_M[h] == kNegInf) ? 0.f : exp2f(m - s_M[h]);
+        }
+        __syncthreads();
+        for (int s = 0; s < nc; ++s) {
+            const v4f* src = reinterpret_cast<const v4f*>(A.part_o + base0 + (int64_t)(c0 + s) * split_stride);
+            v4f x[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x[k] = src[tid + 256 * k];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int lane0 = (4 * (tid + 256 * k)) & 63;   // 4 consecutive lanes, same half
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[k][i] += s_w[s][(lane0 + i) & 31] * x[k][i];
+            }
         }
     }
-    const float v = L > 0.f ? o / L : 0.f;
-    out[((int64_t)b * A.heads + head) * 512 + feat] = __builtin_bit_cast(uint16_t, (__bf16)v);
-    if (f == 0 && r == 0 && (lane >> 5) == 0)
-        lse[(int64_t)b * A.heads + head] = L > 0.f ? 0.6931471805599453f * (M + log2f(L)) : kNegInf;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e0 = 4 * (tid + 256 * k);
+        const int f = e0 >> 10, r = (e0 >> 6) & 15;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int lane = (e0 + i) & 63, h = lane & 31;
+            const int feat = 32 * f + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);   // within the quarter
+            const float v = s_L[h] > 0.f ? acc[k][i] / s_L[h] : 0.f;
+            s_o[h][feat] = __builtin_bit_cast(uint16_t, (__bf16)v);
+        }
+    }
+    __syncthreads();
+    // 32 heads x 128 features = 512 runs of 8 bf16 (16 bytes); 2 per thread
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int unit = tid + 256 * k, h = unit >> 4, c = (unit & 15) * 8;
+        uint4 v;
+        v.x = s_o[h][c] | ((uint32_t)s_o[h][c + 1] << 16);
+        v.y = s_o[h][c + 2] | ((uint32_t)s_o[h][c + 3] << 16);
+        v.z = s_o[h][c + 4] | ((uint32_t)s_o[h][c + 5] << 16);
+        v.w = s_o[h][c + 6] | ((uint32_t)s_o[h][c + 7] << 16);
+        *reinterpret_cast<uint4*>(out + ((int64_t)b * A.heads + wave * 32 + h) * 512 + 128 * q + c) = v;
+    }
+    if (q == 0 && tid < 32)
+        lse[(int64_t)b * A.heads + wave * 32 + tid] =
+            s_L[tid] > 0.f ? 0.6931471805599453f * (s_M[tid] + log2f(s_L[tid])) : kNegInf;
 }
 
 }  // namespace
@@ -508,8 +559,7 @@ hipError_t launch_decode(const DecodeArgs& a, uint16_t* out, float* lse, hipStre
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t total = (int64_t)a.batch * (a.heads / 32) * 16 * 16 * 64;
-    hipLaunchKernelGGL(mla_decode_combine, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, out, lse);
+    hipLaunchKernelGGL(mla_decode_combine, dim3((unsigned)(a.batch * (a.heads / 32) * 4)), dim3(256), 0, s, a, out, lse);
     return hipGetLastError();
 }
 
