@@ -14,5 +14,6 @@ GPU with torch's seeded generator instead (see ``fill_normal_``).
 from .workloads import (  # noqa: F401
     BASE_SEED, rng, bf16_normal, f32_normal, fill_normal_,
     MLA, GQA, SpliceWorkload, GatherWorkload, PatchWorkload, DecodeWorkload,
-    single_splice, batched_splice, registry_gather, gqa_patch, rotate_on_read_decode,
+    KeyingWorkload, single_splice, batched_splice, registry_gather, gqa_patch, rotate_on_read_decode,
+    registry_streams,
 )

@@ -277,3 +277,43 @@ def rotate_on_read_decode(batch=32, ctx=32768, heads=128, block_size=64, delta_m
         heads=heads, block_size=block_size, n_blocks=n_blocks, block_tables=bt,
         pending_delta=pend, seq_lens=np.asarray(seq_lens, np.int32),
         scale=1.0 / math.sqrt(576.0), seed_keys=(cfg,))
+
+
+# ---------------------------------------------------------------- keying ---
+
+@dataclass
+class KeyingWorkload:
+    name: str
+    tokens: np.ndarray            # int32 [n_streams, stream_len]
+    gear: np.ndarray              # uint64 [vocab]
+    threshold: int                # boundary when the Gear hash is below it
+    min_len: int
+    max_len: int
+    s1_window: int
+    seed: int = 0
+
+
+def registry_streams(n_streams=64, stream_len=32768, vocab=131072, n_docs=48, doc_range=(512, 4096),
+                     threshold=1 << 56, min_len=64, max_len=2048, s1_window=128, cfg=6):
+    """Token-id streams for registry keying.  Each stream is a random prefix
+    of U{0..2047} tokens followed by documents drawn from a shared library of
+    n_docs (lengths U{doc_range}), each preceded by a random run of U{0..63}
+    tokens, cut at stream_len: the same content recurs at different offsets.
+    Token ids are uniform over the vocabulary; the Gear table is 64-bit
+    uniform per token id."""
+    r = rng(cfg, 0)
+    gear = r.integers(0, 2 ** 64, size=vocab, dtype=np.uint64)
+    docs = [r.integers(0, vocab, size=int(r.integers(doc_range[0], doc_range[1], endpoint=True)))
+            for _ in range(n_docs)]
+    out = np.empty((n_streams, stream_len), np.int32)
+    for s in range(n_streams):
+        parts = [r.integers(0, vocab, size=int(r.integers(0, 2047, endpoint=True)))]
+        n = len(parts[0])
+        while n < stream_len:
+            sep = r.integers(0, vocab, size=int(r.integers(0, 63, endpoint=True)))
+            d = docs[int(r.integers(0, n_docs))]
+            parts += [sep, d]
+            n += len(sep) + len(d)
+        out[s] = np.concatenate(parts)[:stream_len]
+    return KeyingWorkload(name=f"registry_keying_{n_streams}x{stream_len}", tokens=out, gear=gear,
+                          threshold=threshold, min_len=min_len, max_len=max_len, s1_window=s1_window)
