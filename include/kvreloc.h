@@ -71,7 +71,9 @@ typedef int32_t kvr_status;
 #define KVR_DEV_BAD_BLOCK   1u  /* a block-table entry was outside [0, n_blocks) */
 #define KVR_DEV_SPIN_LIMIT  2u  /* a splice ordering wait hit its bound (workspace misuse) */
 #define KVR_DEV_BAD_TICKET  4u  /* a splice ticket was out of range (workspace not zeroed) */
-#define KVR_DEV_RANGE       8u  /* decode: scores kept outgrowing the softmax headroom (2^48) */
+#define KVR_DEV_RANGE       8u  /* decode: scores kept outgrowing the softmax headroom (2^48);
+                                    lazy splice: a shift left int32; keying: chunk list overflow */
+#define KVR_DEV_BAD_TOKEN  16u  /* keying: a token id outside [0, vocab) */
 
 /* Directive modes m (Leyline 2.1). */
 #define KVR_AMORTIZE 0
@@ -154,6 +156,16 @@ typedef struct kvr_lowrank {
     int32_t      rank;       /* 0 or 1..64 */
     int32_t      reserved;
 } kvr_lowrank;
+
+/* Content-defined chunking parameters (registry_chunk_keys). */
+typedef struct kvr_cdc_params {
+    uint64_t threshold;  /* a candidate boundary follows token i when its Gear hash < threshold */
+    int32_t  min_len;    /* chunk length bounds in tokens, 1 <= min_len <= max_len */
+    int32_t  max_len;
+    int32_t  s1_window;  /* S1 fallback window in tokens (>= 1) */
+    int32_t  reserved;
+    uint64_t seed;       /* xxHash64 seed */
+} kvr_cdc_params;
 
 /* ------------------------------------------------------------------------
  * leyline_splice -- in-place AMORTIZE splice of n_seq sequences (Leyline
@@ -299,6 +311,47 @@ kvr_status leyline_splice_lazy(int32_t block_size, int32_t* d_block_tables, int3
                                int32_t bt_stride, int32_t n_seq, const int64_t* seq_lens,
                                const kvr_directive* dirs, const int32_t* d_stub_blocks,
                                int32_t* d_freed_blocks, int64_t* new_lens, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * registry_chunk_keys -- registry keying of token streams (Irminsul, section
+ * 2.2): content-defined chunks cut by a Gear rolling hash over 64-token
+ * windows, each fingerprinted with xxHash64, plus the S1 fallback's fixed
+ * windows inside every chunk.
+ *
+ * Per stream s = tokens [offsets[s], offsets[s+1]) of d_tokens:
+ *   h_i = (2 h_{i-1} + gear[tok_i]) mod 2^64, h = 0 before the stream start
+ *         (= sum over the last 64 tokens of gear[tok] * 2^age);
+ *   the chunk starting at p ends after the first i in
+ *   [p + min_len - 1, p + max_len - 1] with h_i < threshold, else after
+ *   p + max_len - 1; the last chunk ends at the stream end;
+ *   fingerprint = xxHash64(token ids as little-endian int32 bytes, seed);
+ *   S1 window w of a chunk [a, b) = [a + w s1, min(a + (w+1) s1, b)).
+ *   d_tokens     : device int32 [offsets[n_streams]]
+ *   offsets      : host int64 [n_streams + 1], non-decreasing, offsets[0] >= 0;
+ *                  each stream shorter than 2^31 tokens
+ *   n_streams    : 0 .. 240
+ *   d_gear       : device uint64 [vocab] (the Gear table, caller-drawn)
+ *   d_hash       : device uint64 out [total] (h_i per token) or NULL
+ *   d_chunk_end  : device int32 out [n_streams][chunk_cap]: chunk ends
+ *                  relative to the stream start, in order
+ *   chunk_cap    : >= ceil(len / min_len) for every stream
+ *   d_n_chunks   : device int32 out [n_streams]
+ *   d_chunk_fp   : device uint64 out [n_streams][chunk_cap]
+ *   d_s1_fp      : device uint64 out [n_streams][chunk_cap][ceil(max_len / s1_window)]
+ *                  (unused windows 0) or NULL
+ *   d_workspace  : kvr_keys_workspace_bytes(total) bytes, 256-byte aligned
+ * Device errors: KVR_DEV_BAD_TOKEN for an id outside [0, vocab) (its Gear
+ * value counts as 0).
+ * Errors: KVR_E_ARG (null pointer, bad parameters, chunk_cap too small),
+ * KVR_E_RANGE (offsets), KVR_E_UNSUPPORTED (n_streams > 240),
+ * KVR_E_WORKSPACE, KVR_E_HIP.
+ * ---------------------------------------------------------------------- */
+size_t kvr_keys_workspace_bytes(int64_t total_tokens);
+kvr_status registry_chunk_keys(const int32_t* d_tokens, const int64_t* offsets, int32_t n_streams,
+                               const uint64_t* d_gear, int32_t vocab, const kvr_cdc_params* params,
+                               uint64_t* d_hash, int32_t* d_chunk_end, int32_t chunk_cap, int32_t* d_n_chunks,
+                               uint64_t* d_chunk_fp, uint64_t* d_s1_fp, void* d_workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Utilities.

@@ -13,7 +13,7 @@ KVR_OK = 0
 KVR_FORGET_NEEDS_PREFILL = 1
 KVR_AMORTIZE, KVR_FORGET = 0, 1
 KVR_BF16, KVR_F32 = 0, 1
-KVR_DEV_BAD_BLOCK, KVR_DEV_SPIN_LIMIT, KVR_DEV_BAD_TICKET = 1, 2, 4
+KVR_DEV_BAD_BLOCK, KVR_DEV_SPIN_LIMIT, KVR_DEV_BAD_TICKET, KVR_DEV_RANGE, KVR_DEV_BAD_TOKEN = 1, 2, 4, 8, 16
 
 
 class kvr_part(ctypes.Structure):
@@ -41,6 +41,11 @@ class kvr_lowrank(ctypes.Structure):
                 ("rank", c_i32), ("reserved", c_i32)]
 
 
+class kvr_cdc_params(ctypes.Structure):
+    _fields_ = [("threshold", ctypes.c_uint64), ("min_len", c_i32), ("max_len", c_i32), ("s1_window", c_i32),
+                ("reserved", c_i32), ("seed", ctypes.c_uint64)]
+
+
 P = ctypes.POINTER
 
 # name -> (restype, argtypes); the names and order follow include/kvreloc.h
@@ -62,6 +67,9 @@ SIGNATURES = {
                                           c_vp, c_i32, c_f32, c_vp, c_vp, c_vp, c_size, c_vp]),
     "leyline_splice_lazy": (c_i32, [c_i32, c_vp, c_vp, c_i32, c_i32, P(c_i64), P(kvr_directive), c_vp, c_vp,
                                     P(c_i64), c_vp]),
+    "kvr_keys_workspace_bytes": (c_size, [c_i64]),
+    "registry_chunk_keys": (c_i32, [c_vp, P(c_i64), c_i32, c_vp, c_i32, P(kvr_cdc_params), c_vp, c_vp, c_i32, c_vp,
+                                    c_vp, c_vp, c_vp, c_size, c_vp]),
 }
 
 _lib = None

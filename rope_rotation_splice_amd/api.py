@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import _abi
-from ._abi import (KVR_AMORTIZE, KVR_BF16, KVR_F32, KVR_FORGET, KVR_FORGET_NEEDS_PREFILL,  # noqa: F401
+from ._abi import (kvr_cdc_params, KVR_AMORTIZE, KVR_BF16, KVR_F32, KVR_FORGET, KVR_FORGET_NEEDS_PREFILL,  # noqa: F401
                    KVR_OK, kvr_cache, kvr_directive, kvr_lowrank, kvr_part, kvr_rows)
 
 
@@ -202,6 +202,45 @@ def leyline_splice_lazy(block_tables, pending_delta, block_size, seq_lens, direc
                                  freed.data_ptr() if n_free else None, out, _stream_handle())
     _check("leyline_splice_lazy", st)
     return np.array(out[:n], dtype=np.int64), freed[:n_free], st
+
+
+def registry_chunk_keys(tokens, offsets, gear, threshold, min_len, max_len, s1_window, seed=0,
+                        with_hash=False, with_s1=True):
+    """Content-defined chunking of token streams with a Gear rolling hash and
+    xxHash64 fingerprints, plus S1 fixed windows per chunk.
+
+    tokens: int32 device tensor (streams concatenated); offsets: host list of
+    n_streams + 1 token offsets; gear: device tensor of 64-bit values per token
+    id (int64 or uint64 storage).  Returns a dict with chunk_end [n, cap],
+    n_chunks [n], chunk_fp [n, cap] (int64 storage of uint64), s1_fp
+    [n, cap, slots] and, on request, hash [total].
+    """
+    lib = _abi.load()
+    if tokens.dtype != torch.int32 or not tokens.is_contiguous():
+        raise ValueError("tokens must be a contiguous int32 tensor")
+    if gear.element_size() != 8 or not gear.is_contiguous():
+        raise ValueError("gear must be a contiguous tensor of 64-bit values")
+    off = [int(x) for x in offsets]
+    n = len(off) - 1
+    lens = [off[i + 1] - off[i] for i in range(n)]
+    cap = max([1] + [-(-ln // int(min_len)) for ln in lens])
+    slots = -(-int(max_len) // int(s1_window))
+    dev = tokens.device
+    out = {"chunk_end": torch.zeros((max(n, 1), cap), dtype=torch.int32, device=dev)[:n],
+           "n_chunks": torch.zeros(max(n, 1), dtype=torch.int32, device=dev)[:n],
+           "chunk_fp": torch.zeros((max(n, 1), cap), dtype=torch.int64, device=dev)[:n]}
+    out["s1_fp"] = torch.zeros((max(n, 1), cap, slots), dtype=torch.int64, device=dev)[:n] if with_s1 else None
+    out["hash"] = torch.zeros(max(1, off[-1] if n else 1), dtype=torch.int64, device=dev) if with_hash else None
+    p = kvr_cdc_params(int(threshold), int(min_len), int(max_len), int(s1_window), 0, int(seed))
+    offs = (ctypes.c_int64 * max(1, n + 1))(*off)
+    need = lib.kvr_keys_workspace_bytes(off[-1] - off[0] if n else 0)
+    ws = _workspace(need, dev, "keys")
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    st = lib.registry_chunk_keys(tokens.data_ptr(), offs, n, gear.data_ptr(), int(gear.numel()), ctypes.byref(p),
+                                 ptr(out["hash"]), ptr(out["chunk_end"]), cap, ptr(out["n_chunks"]),
+                                 ptr(out["chunk_fp"]), ptr(out["s1_fp"]), ws.data_ptr(), ws.numel(), _stream_handle())
+    _check("registry_chunk_keys", st)
+    return out
 
 
 def kv_relocate_gather(cache, block_table, entries, p_targets, patch_rope=None, patch_pf=None):

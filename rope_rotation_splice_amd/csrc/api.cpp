@@ -309,9 +309,10 @@ kvr_status kvr_device_errors(uint32_t* flags) {
     const uint32_t w = read_and_clear_errors_patch();
     const uint32_t x = read_and_clear_errors_decode();
     const uint32_t y = read_and_clear_errors_lazy();
-    if (v == 0xffffffffu || w == 0xffffffffu || x == 0xffffffffu || y == 0xffffffffu)
+    const uint32_t z = read_and_clear_errors_keys();
+    if (v == 0xffffffffu || w == 0xffffffffu || x == 0xffffffffu || y == 0xffffffffu || z == 0xffffffffu)
         return hip_fail(hipErrorUnknown);
-    *flags = v | w | x | y;
+    *flags = v | w | x | y | z;
     return KVR_OK;
 }
 
@@ -667,6 +668,58 @@ kvr_status leyline_splice_lazy(int32_t block_size, int32_t* d_block_tables, int3
     }
     for (int32_t b = 0; b < n_seq; ++b) new_lens[b] = out[b];
     return forget ? KVR_FORGET_NEEDS_PREFILL : KVR_OK;
+}
+
+size_t kvr_keys_workspace_bytes(int64_t total_tokens) {
+    if (total_tokens <= 0) return kAlign;
+    return round_up((size_t)((total_tokens + 63) / 64) * 8);
+}
+
+kvr_status registry_chunk_keys(const int32_t* d_tokens, const int64_t* offsets, int32_t n_streams,
+                               const uint64_t* d_gear, int32_t vocab, const kvr_cdc_params* params,
+                               uint64_t* d_hash, int32_t* d_chunk_end, int32_t chunk_cap, int32_t* d_n_chunks,
+                               uint64_t* d_chunk_fp, uint64_t* d_s1_fp, void* d_ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    if (n_streams < 0 || !params) return KVR_E_ARG;
+    if (n_streams > kKeyMaxStreams) return KVR_E_UNSUPPORTED;
+    if (n_streams == 0) return KVR_OK;
+    if (!offsets || !d_tokens || !d_gear || vocab <= 0 || !d_chunk_end || !d_n_chunks || !d_chunk_fp)
+        return KVR_E_ARG;
+    const kvr_cdc_params& P = *params;
+    if (P.min_len < 1 || P.max_len < P.min_len || P.s1_window < 1) return KVR_E_ARG;
+    if (offsets[0] < 0) return KVR_E_RANGE;
+    for (int32_t s = 0; s < n_streams; ++s) {
+        const int64_t len = offsets[s + 1] - offsets[s];
+        if (len < 0 || len >= ((int64_t)1 << 31)) return KVR_E_RANGE;
+        if (chunk_cap < (len + P.min_len - 1) / P.min_len) return KVR_E_ARG;
+    }
+    if (chunk_cap < 1 || (int64_t)chunk_cap * n_streams >= ((int64_t)1 << 31)) return KVR_E_ARG;
+    const int64_t n_tok = offsets[n_streams] - offsets[0];
+    const size_t need = kvr_keys_workspace_bytes(n_tok);
+    if (!d_ws || (reinterpret_cast<uintptr_t>(d_ws) % kAlign) || ws_bytes < need) return KVR_E_WORKSPACE;
+    KeyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.tokens = d_tokens;
+    a.gear = d_gear;
+    a.hash = d_hash;
+    a.cand = (uint64_t*)d_ws;
+    a.chunk_end = d_chunk_end;
+    a.n_chunks = d_n_chunks;
+    a.chunk_fp = d_chunk_fp;
+    a.s1_fp = d_s1_fp;
+    a.threshold = P.threshold;
+    a.seed = P.seed;
+    a.total = offsets[n_streams];
+    a.vocab = vocab;
+    a.min_len = P.min_len;
+    a.max_len = P.max_len;
+    a.s1_window = P.s1_window;
+    a.s1_slots = (P.max_len + P.s1_window - 1) / P.s1_window;
+    a.cap = chunk_cap;
+    a.n_streams = n_streams;
+    for (int32_t s = 0; s <= n_streams; ++s) a.offsets[s] = offsets[s];
+    hipError_t e = launch_keys(a, stream);
+    return e == hipSuccess ? KVR_OK : hip_fail(e);
 }
 
 }  // extern "C"

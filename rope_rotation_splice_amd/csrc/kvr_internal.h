@@ -138,6 +138,25 @@ struct LazyArgs {
 };
 static_assert(sizeof(LazyArgs) <= 4000, "lazy splice arguments too large");
 
+// Registry keying (keying.hip).
+constexpr int kKeyMaxStreams = 240;
+
+struct KeyArgs {
+    const int32_t* tokens;
+    const uint64_t* gear;
+    uint64_t* hash;                   // optional Gear hash per token
+    uint64_t* cand;                   // candidate bitmask, one bit per token
+    int32_t* chunk_end;
+    int32_t* n_chunks;
+    uint64_t* chunk_fp;
+    uint64_t* s1_fp;                  // optional
+    uint64_t threshold, seed;
+    int64_t total;
+    int32_t vocab, min_len, max_len, s1_window, s1_slots, cap, n_streams;
+    int64_t offsets[kKeyMaxStreams + 1];
+};
+static_assert(sizeof(KeyArgs) <= 4000, "keying arguments too large");
+
 // Kernel arguments must stay within the 4 KB kernarg budget.
 static_assert(sizeof(RelocArgs) <= 4000, "relocation kernel arguments too large");
 
@@ -157,5 +176,8 @@ uint32_t read_and_clear_errors_decode();
 // Block-table splice (lazy.hip).
 hipError_t launch_lazy(const LazyArgs& a, hipStream_t s);
 uint32_t read_and_clear_errors_lazy();
+// Registry keying (keying.hip): Gear hashes and candidates, cuts, fingerprints.
+hipError_t launch_keys(const KeyArgs& a, hipStream_t s);
+uint32_t read_and_clear_errors_keys();
 
 }  // namespace kvr

@@ -26,7 +26,7 @@ def test_header_functions_exported():
     lib = _abi.load()
     names = declared_functions()
     assert {"leyline_splice", "kv_relocate_gather", "kv_patch_lowrank", "mla_decode_rotate_on_read",
-            "leyline_splice_lazy"} <= set(names)
+            "leyline_splice_lazy", "registry_chunk_keys"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_abi.SIGNATURES), "binding and header disagree"
@@ -167,3 +167,32 @@ def test_lazy_forget_and_empty_need_no_launch():
     assert st == 1 and out[0] == 128
     st, _ = lazy([], [])
     assert st == 0
+
+
+def keys(n_streams=2, lens=(1000, 500), cap=None, p=None, ws_bytes=1 << 20, gear=FAKE, toks=FAKE):
+    lib = _abi.load()
+    off = [0]
+    for ln in lens:
+        off.append(off[-1] + ln)
+    offs = (ctypes.c_int64 * len(off))(*off)
+    p = p or _abi.kvr_cdc_params(1 << 56, 64, 2048, 128, 0, 0)
+    cap = cap if cap is not None else max([1] + [-(-ln // max(1, p.min_len)) for ln in lens])
+    return lib.registry_chunk_keys(toks, offs, n_streams, gear, 1000, ctypes.byref(p), None, FAKE, cap, FAKE,
+                                   FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def test_keys_validation_errors():
+    P = _abi.kvr_cdc_params
+    assert keys(cap=10) == -1                                       # stream 0 needs 16 chunks
+    assert keys(p=P(1, 0, 10, 128, 0, 0)) == -1                     # min_len 0
+    assert keys(p=P(1, 64, 32, 128, 0, 0)) == -1                    # max_len < min_len
+    assert keys(p=P(1, 64, 2048, 0, 0, 0)) == -1                    # s1 window 0
+    assert keys(gear=None) == -1
+    assert keys(toks=None) == -1
+    assert keys(lens=(1000, -5)) == -2                              # offsets decrease
+    assert keys(ws_bytes=64) == -6                                  # bitmask does not fit
+    assert keys(n_streams=241, lens=tuple([10] * 241)) == -7
+    assert keys(n_streams=0, lens=()) == 0
+    lib = _abi.load()
+    assert lib.kvr_keys_workspace_bytes(1500) == 256
+    assert lib.kvr_keys_workspace_bytes(64 * 32 * 3) == 3 * 256

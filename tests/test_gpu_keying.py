@@ -1,0 +1,95 @@
+"""Parity of registry_chunk_keys (HIP, through the C ABI) with the oracle:
+Gear hashes, chunk cuts, xxHash64 fingerprints and S1 windows, bit for bit."""
+
+import numpy as np
+import pytest
+
+import kvsynth
+from oracle import keying as ok
+
+pytestmark = pytest.mark.gpu
+
+U64 = (1 << 64) - 1
+
+
+def _u(t):
+    return [int(x) & U64 for x in t.reshape(-1).cpu().numpy().astype(np.int64)]
+
+
+def _run(streams, gear, thr, lo, hi, s1, seed=0, with_hash=True):
+    import torch
+    import rope_rotation_splice_amd as rrs
+    off = np.concatenate([[0], np.cumsum([len(s) for s in streams])]).tolist()
+    flat = np.concatenate([np.asarray(s, np.int32) for s in streams]) if off[-1] else np.zeros(0, np.int32)
+    tok = torch.from_numpy(flat).cuda() if len(flat) else torch.zeros(0, dtype=torch.int32, device="cuda")
+    g = torch.from_numpy(np.asarray(gear, np.uint64).view(np.int64)).cuda()
+    out = rrs.registry_chunk_keys(tok, off, g, thr, lo, hi, s1, seed=seed, with_hash=with_hash)
+    torch.cuda.synchronize()
+    return off, out
+
+
+def _check(streams, gear, thr, lo, hi, s1, seed, off, out, check_hash=True):
+    slots = -(-hi // s1)
+    for s, toks in enumerate(streams):
+        toks = np.asarray(toks)
+        if check_hash and len(toks):
+            h = ok.gear_hashes(toks, gear)
+            assert _u(out["hash"][off[s]:off[s + 1]]) == h, f"stream {s}: Gear hashes"
+        ends, fps, s1fp = ok.chunk_keys(toks, gear, thr, lo, hi, s1, seed)
+        n = int(out["n_chunks"][s])
+        assert n == len(ends), f"stream {s}: {n} chunks, oracle {len(ends)}"
+        assert out["chunk_end"][s][:n].cpu().numpy().tolist() == ends, f"stream {s}: cuts"
+        assert _u(out["chunk_fp"][s][:n]) == fps, f"stream {s}: fingerprints"
+        got = _u(out["s1_fp"][s][:n])
+        want = [w + [0] * (slots - len(w)) for w in s1fp]
+        assert got == [x for w in want for x in w], f"stream {s}: S1 windows"
+
+
+def test_keys_small_streams():
+    import rope_rotation_splice_amd as rrs
+    r = kvsynth.rng(31, 1)
+    vocab = 5000
+    gear = r.integers(0, 2 ** 64, size=vocab, dtype=np.uint64)
+    lens = [0, 1, 63, 64, 65, 130, 1000, 5000, 257, 3]
+    streams = [r.integers(0, vocab, size=n) for n in lens]
+    for thr, lo, hi, s1, seed in [(1 << 58, 16, 200, 32, 0), (1 << 56, 64, 2048, 128, 7), (1 << 62, 1, 5, 3, 2 ** 64 - 1)]:
+        off, out = _run(streams, gear, thr, lo, hi, s1, seed)
+        assert rrs.device_errors() == 0
+        _check(streams, gear, thr, lo, hi, s1, seed, off, out)
+
+
+def test_keys_shared_content_aligns():
+    """The same document behind two prefixes yields shared fingerprints on
+    the device as in the oracle (content-defined cuts)."""
+    r = kvsynth.rng(31, 2)
+    gear = r.integers(0, 2 ** 64, size=50000, dtype=np.uint64)
+    doc = r.integers(0, 50000, size=6000)
+    streams = [np.concatenate([r.integers(0, 50000, size=333), doc]),
+               np.concatenate([r.integers(0, 50000, size=1017), doc])]
+    off, out = _run(streams, gear, 1 << 56, 64, 2048, 128)
+    _check(streams, gear, 1 << 56, 64, 2048, 128, 0, off, out)
+    fa = set(_u(out["chunk_fp"][0][:int(out["n_chunks"][0])]))
+    fb = set(_u(out["chunk_fp"][1][:int(out["n_chunks"][1])]))
+    assert len(fa & fb) >= len(fa) - 3
+
+
+def test_keys_bad_token_flagged():
+    import rope_rotation_splice_amd as rrs
+    gear = np.arange(100, dtype=np.uint64)
+    _run([np.array([1, 2, 300, 4] * 20)], gear, 1 << 60, 4, 64, 16)
+    assert rrs.device_errors() & 16
+
+
+def test_keys_full_workload_sampled():
+    """The keying workload at full size (64 streams x 32768 tokens, vocab
+    131072, threshold 2^56, chunks 64..2048, S1 windows of 128), streams 0,
+    31 and 63 compared with the oracle."""
+    import rope_rotation_splice_amd as rrs
+    w = kvsynth.registry_streams()
+    streams = list(w.tokens)
+    off, out = _run(streams, w.gear, w.threshold, w.min_len, w.max_len, w.s1_window, with_hash=False)
+    assert rrs.device_errors() == 0
+    for s in (0, 31, 63):
+        sub = {k: (v[s:s + 1] if v is not None else None) for k, v in out.items()}
+        _check([streams[s]], w.gear, w.threshold, w.min_len, w.max_len, w.s1_window, w.seed, [0, len(streams[s])],
+               sub, check_hash=False)
