@@ -343,6 +343,55 @@ class SpliceLazy:
                 "sample": f"{units} sequence table edits (the step's 64, repeated), numpy, one process"}
 
 
+class Keys:
+    """Registry keying of 64 token streams x 32768 tokens (vocab 131072): Gear
+    CDC (threshold 2^56, chunks 64..2048 tokens), xxHash64 per chunk and per
+    S1 128-token window.  Slots counted are tokens keyed."""
+    name = "registry_keying"
+    kernel = "gear_kernel + cut_kernel + fp_kernel"
+
+    def __init__(self):
+        import kvsynth
+        self.w = kvsynth.registry_streams()
+        n = self.w.tokens.size
+        self.slots = n
+        # tokens read by the hash pass and by the chunk and S1 fingerprint
+        # passes, one Gear value per token, one candidate bit per token
+        self.bytes = int(n * (4 * 3 + 8) + n / 8)
+        self.launches = 1
+        self.config = {"workload": "irminsul_registry_keying", "streams": self.w.tokens.shape[0],
+                       "stream_len": self.w.tokens.shape[1], "vocab": len(self.w.gear), "threshold": "2^56",
+                       "chunk_len": [self.w.min_len, self.w.max_len], "s1_window": self.w.s1_window,
+                       "slots_per_step": n}
+
+    def setup(self):
+        import torch
+        import rope_rotation_splice_amd as rrs
+        w = self.w
+        self.tok = torch.from_numpy(w.tokens.reshape(-1).copy()).cuda()
+        self.gear = torch.from_numpy(w.gear.view(np.int64)).cuda()
+        self.off = [int(x) for x in range(0, w.tokens.size + 1, w.tokens.shape[1])]
+        self.rrs = rrs
+
+    def step(self):
+        w = self.w
+        self.rrs.registry_chunk_keys(self.tok, self.off, self.gear, w.threshold, w.min_len, w.max_len, w.s1_window)
+
+    def cpu_baseline(self, budget_s):
+        from oracle import keying as ok
+        w = self.w
+        toks, spent = 0, 0.0
+        for s in range(w.tokens.shape[0]):
+            t0 = time.perf_counter()
+            ok.chunk_keys(w.tokens[s], w.gear, w.threshold, w.min_len, w.max_len, w.s1_window, w.seed)
+            spent += time.perf_counter() - t0
+            toks += w.tokens.shape[1]
+            if spent >= budget_s:
+                break
+        return {"value": toks / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
+                "sample": f"{toks // w.tokens.shape[1]} whole streams of the same draw, pure Python, one process"}
+
+
 class GqaPatch:
     """Kamera GQA relocation with its rank-16 patch, fused into one gather:
     16 chunks x 1024 tokens, 32 layers, K and V of 8 x 128 bf16, delta ~
@@ -538,7 +587,7 @@ class Copy:
 
 
 WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "splice_lazy": SpliceLazy,
-             "gqa_patch": GqaPatch,
+             "gqa_patch": GqaPatch, "keys": Keys,
              "decode": Decode, "decode_zero_delta": lambda: Decode(zero_delta=True), "copy": Copy}
 
 
