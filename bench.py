@@ -286,6 +286,8 @@ class SpliceLazy:
     Slots counted are the downstream slots re-indexed per step."""
     name = "lazy_splice"
     kernel = "lazy_kernel"
+    dtype = "int32"
+    data = "synthetic (seeded block tables, pending shifts and directives of the batched-splice draw)"
 
     def __init__(self):
         import kvsynth
@@ -349,6 +351,8 @@ class Keys:
     S1 128-token window.  Slots counted are tokens keyed."""
     name = "registry_keying"
     kernel = "gear_kernel + cut_kernel + fp_kernel"
+    dtype = "u64"
+    data = "synthetic (seeded token-id streams over shared documents, seeded 64-bit Gear table)"
 
     def __init__(self):
         import kvsynth
@@ -657,8 +661,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 cache rows, integer draws as stated in config)",
+        "dtype": getattr(wl, "dtype", "bf16"),
+        "data": getattr(wl, "data", "synthetic (seeded N(0,1) bf16 cache rows, integer draws as stated in config)"),
         "config": wl.config,
         "hbm_GBps_per_step": wl.bytes * args.steps / wall / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

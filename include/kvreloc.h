@@ -338,7 +338,9 @@ kvr_status leyline_splice_lazy(int32_t block_size, int32_t* d_block_tables, int3
  *   d_n_chunks   : device int32 out [n_streams]
  *   d_chunk_fp   : device uint64 out [n_streams][chunk_cap]
  *   d_s1_fp      : device uint64 out [n_streams][chunk_cap][ceil(max_len / s1_window)]
- *                  (unused windows 0) or NULL
+ *                  (a chunk's unused windows 0) or NULL
+ *   Entries of d_chunk_end, d_chunk_fp and d_s1_fp at chunk k >= n_chunks[s]
+ *   are not written; d_hash is written at [offsets[0], total) only.
  *   d_workspace  : kvr_keys_workspace_bytes(total) bytes, 256-byte aligned
  * Device errors: KVR_DEV_BAD_TOKEN for an id outside [0, vocab) (its Gear
  * value counts as 0).

@@ -213,7 +213,8 @@ def registry_chunk_keys(tokens, offsets, gear, threshold, min_len, max_len, s1_w
     n_streams + 1 token offsets; gear: device tensor of 64-bit values per token
     id (int64 or uint64 storage).  Returns a dict with chunk_end [n, cap],
     n_chunks [n], chunk_fp [n, cap] (int64 storage of uint64), s1_fp
-    [n, cap, slots] and, on request, hash [total].
+    [n, cap, slots] and, on request, hash [total].  Rows of chunk_end,
+    chunk_fp and s1_fp past n_chunks[s] are left unwritten (unspecified).
     """
     lib = _abi.load()
     if tokens.dtype != torch.int32 or not tokens.is_contiguous():
@@ -226,10 +227,10 @@ def registry_chunk_keys(tokens, offsets, gear, threshold, min_len, max_len, s1_w
     cap = max([1] + [-(-ln // int(min_len)) for ln in lens])
     slots = -(-int(max_len) // int(s1_window))
     dev = tokens.device
-    out = {"chunk_end": torch.zeros((max(n, 1), cap), dtype=torch.int32, device=dev)[:n],
-           "n_chunks": torch.zeros(max(n, 1), dtype=torch.int32, device=dev)[:n],
-           "chunk_fp": torch.zeros((max(n, 1), cap), dtype=torch.int64, device=dev)[:n]}
-    out["s1_fp"] = torch.zeros((max(n, 1), cap, slots), dtype=torch.int64, device=dev)[:n] if with_s1 else None
+    out = {"chunk_end": torch.empty((max(n, 1), cap), dtype=torch.int32, device=dev)[:n],
+           "n_chunks": torch.empty(max(n, 1), dtype=torch.int32, device=dev)[:n],
+           "chunk_fp": torch.empty((max(n, 1), cap), dtype=torch.int64, device=dev)[:n]}
+    out["s1_fp"] = torch.empty((max(n, 1), cap, slots), dtype=torch.int64, device=dev)[:n] if with_s1 else None
     out["hash"] = torch.zeros(max(1, off[-1] if n else 1), dtype=torch.int64, device=dev) if with_hash else None
     p = kvr_cdc_params(int(threshold), int(min_len), int(max_len), int(s1_window), 0, int(seed))
     offs = (ctypes.c_int64 * max(1, n + 1))(*off)

@@ -2,17 +2,21 @@
 // chunks cut by a Gear rolling hash over 64-token windows, fingerprinted with
 // xxHash64, plus the S1 fallback's fixed windows inside each chunk.
 //
-// 1. gear_kernel: one thread per token.  The 64-bit Gear state shifts a
+// 1. gear_kernel: one lane per token.  The 64-bit Gear state shifts a
 //    token's contribution out after 64 steps, so h_i is the sum over the
-//    last 64 tokens of gear[tok] * 2^age: every position is computed
-//    independently from a window of Gear values staged in LDS (Horner order,
-//    oldest first, clipped at the stream start).  Candidates (h_i below the
-//    threshold) become a bitmask, one wave ballot per 64 tokens.
+//    last 64 tokens of gear[tok] * 2^age (clipped at the stream start).  A
+//    64-token tile is a segmented scan under (a, b) -> (a << d) + b, six
+//    shift-add steps across the wave that restart at stream starts, plus the
+//    previous tile's last h shifted by lane + 1 where no start intervenes.
+//    Candidates (h_i below the threshold) become a bitmask, one wave ballot
+//    per 64 tokens.
 // 2. cut_kernel: one wave per stream walks the chunk rule; the first
 //    candidate in [p + min_len - 1, p + max_len - 1] is found by scanning 64
-//    bitmask words (4096 tokens) per step.
-// 3. fp_kernel: one thread per chunk computes xxHash64 of the chunk's token
-//    ids (little-endian int32 bytes) and of its S1 windows.  xxHash64 follows
+//    bitmask words (4096 tokens) per step, from a window of the bitmask
+//    staged in LDS.
+// 3. fp_kernel: one wave per chunk computes xxHash64 of its tokens' ids
+//    (little-endian int32 bytes) and of its S1 windows, four lanes (the four
+//    stripe accumulators) per hash, 16 hashes side by side.  xxHash64 follows
 //    its published specification (XXH64: four lanes over 32-byte stripes,
 //    merge, 8- and 4-byte tail steps, avalanche).
 #include "kvr_device.h"
@@ -45,32 +49,28 @@ __device__ __forceinline__ uint64_t two_tokens(const int32_t* t) {
     return (uint64_t)(uint32_t)t[0] | ((uint64_t)(uint32_t)t[1] << 32);
 }
 
-// xxHash64 of n token ids (4 n bytes)
-__device__ uint64_t xxh64_tokens(const int32_t* t, int n, uint64_t seed) {
-    int i = 0;
-    uint64_t h;
-    if (n >= 8) {
-        uint64_t v1 = seed + P1 + P2, v2 = seed + P2, v3 = seed, v4 = seed - P1;
-        for (; i + 8 <= n; i += 8) {
-            v1 = xround(v1, two_tokens(t + i));
-            v2 = xround(v2, two_tokens(t + i + 2));
-            v3 = xround(v3, two_tokens(t + i + 4));
-            v4 = xround(v4, two_tokens(t + i + 6));
-        }
-        h = rotl64(v1, 1) + rotl64(v2, 7) + rotl64(v3, 12) + rotl64(v4, 18);
-        h = xmerge(h, v1);
-        h = xmerge(h, v2);
-        h = xmerge(h, v3);
-        h = xmerge(h, v4);
-    } else {
-        h = seed + P5;
-    }
+// Starting value of stripe accumulator a (0..3).
+__device__ __forceinline__ uint64_t xxh_init(int a, uint64_t seed) {
+    return a == 0 ? seed + P1 + P2 : a == 1 ? seed + P2 : a == 2 ? seed : seed - P1;
+}
+
+__device__ __forceinline__ uint64_t xxh_converge(uint64_t v1, uint64_t v2, uint64_t v3, uint64_t v4) {
+    uint64_t h = rotl64(v1, 1) + rotl64(v2, 7) + rotl64(v3, 12) + rotl64(v4, 18);
+    h = xmerge(h, v1);
+    h = xmerge(h, v2);
+    h = xmerge(h, v3);
+    return xmerge(h, v4);
+}
+
+// Length, the rem (< 8 after the stripes) trailing token ids at t, avalanche.
+__device__ __forceinline__ uint64_t xxh_tail(uint64_t h, const int32_t* t, int rem, int n) {
     h += 4ull * (uint64_t)n;
-    for (; i + 2 <= n; i += 2) {
+    int i = 0;
+    for (; i + 2 <= rem; i += 2) {
         h ^= xround(0, two_tokens(t + i));
         h = rotl64(h, 27) * P1 + P4;
     }
-    if (i < n) {
+    if (i < rem) {
         h ^= (uint64_t)(uint32_t)t[i] * P1;
         h = rotl64(h, 23) * P2 + P3;
     }
@@ -82,70 +82,147 @@ __device__ uint64_t xxh64_tokens(const int32_t* t, int n, uint64_t seed) {
     return h;
 }
 
-__device__ __forceinline__ int64_t stream_start(const KeyArgs& A, int64_t i) {
-    int lo = 0, hi = A.n_streams - 1;        // last stream whose start <= i
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (A.offsets[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    return A.offsets[lo];
+// Each wave takes kGearTiles consecutive 64-token tiles (one position per
+// lane), after one warm-up tile that only supplies the carry-in.  All the
+// span's token ids and Gear values are loaded before the scans.
+constexpr int kGearTiles = 8;
+
+__device__ __forceinline__ uint64_t shfl_up64(uint64_t v, int d) {
+    const uint32_t lo = __shfl_up((uint32_t)v, d), hi = __shfl_up((uint32_t)(v >> 32), d);
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return (uint64_t)lo | ((uint64_t)hi << 32);
 }
 
 __global__ __launch_bounds__(256) void gear_kernel(const KeyArgs A) {
-    __shared__ uint64_t g[256 + 64];
-    const int tid = threadIdx.x;
-    const int64_t base = A.offsets[0] + (int64_t)blockIdx.x * 256;
-    for (int j = tid; j < 320; j += 256) {
-        const int64_t p = base - 64 + j;
-        uint64_t v = 0;
-        if (p >= A.offsets[0] && p < A.total) {
-            const int32_t t = A.tokens[p];
-            if ((uint32_t)t < (uint32_t)A.vocab) v = A.gear[t];
-            else if (j >= 64) raise_error(KVR_DEV_BAD_TOKEN);      // reported once, by its own tile
+    const int lane = threadIdx.x & 63;
+    const int64_t O = A.offsets[0];
+    const int64_t ntiles = (A.total - O + 63) >> 6;
+    const int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kGearTiles;
+    if (t0 >= ntiles) return;
+    const int64_t tw = t0 > 0 ? t0 - 1 : 0;  // first tile scanned (the warm-up one unless t0 == 0)
+    const int nt = (int)(min<int64_t>(t0 + kGearTiles, ntiles) - tw);
+    // Loads are unconditional (addresses clamped into range, values masked
+    // afterwards) so that all of them are in flight together.
+    int32_t tk[kGearTiles + 1];
+    uint64_t gv[kGearTiles + 1];
+#pragma unroll
+    for (int j = 0; j < kGearTiles + 1; ++j) {
+        const int64_t i = O + ((tw + j) << 6) + lane;
+        tk[j] = A.tokens[min(i, A.total - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kGearTiles + 1; ++j)
+        gv[j] = A.gear[(uint32_t)tk[j] < (uint32_t)A.vocab ? tk[j] : 0];
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kGearTiles + 1; ++j) {
+        const int64_t i = O + ((tw + j) << 6) + lane;
+        const bool in = j < nt && i < A.total;
+        const bool ok = (uint32_t)tk[j] < (uint32_t)A.vocab;
+        if (!(in && ok)) gv[j] = 0;
+        bad |= in && !ok && tw + j >= t0;    // reported by the span that owns the tile
+    }
+    if (bad) raise_error(KVR_DEV_BAD_TOKEN);
+    // first stream start at or after the first scanned tile
+    const int64_t first = O + (tw << 6);
+    int sidx = 0, shi = A.n_streams;
+    while (sidx < shi) {
+        const int mid = (sidx + shi) >> 1;
+        if (A.offsets[mid] < first) sidx = mid + 1; else shi = mid;
+    }
+    uint64_t carry = 0;                      // h just before the tile
+#pragma unroll
+    for (int j = 0; j < kGearTiles + 1; ++j) {
+        if (j < nt) {
+            const int64_t tile0 = O + ((tw + j) << 6);
+            uint64_t F = 0;                      // stream starts inside the tile
+            while (sidx < A.n_streams && A.offsets[sidx] < tile0 + 64) {
+                F |= 1ull << (A.offsets[sidx] - tile0);
+                ++sidx;
+            }
+            const uint64_t m = lane == 63 ? F : F & ((2ull << lane) - 1);
+            const int hd = m ? 63 - __clzll((long long)m) : -1;    // this position's stream start in the tile
+            // segmented scan: v = sum over [max(hd, 0), lane] of g_j 2^(lane - j)
+            uint64_t v = gv[j];
+#pragma unroll
+            for (int dd = 1; dd < 64; dd <<= 1) {
+                const uint64_t u = shfl_up64(v, dd);
+                if (lane >= dd && lane - dd >= hd) v += u << dd;
+            }
+            if (hd < 0 && lane < 63) v += carry << (lane + 1);
+            carry = readlane64(v, 63);
+            if (tw + j >= t0) {
+                const int64_t i = tile0 + lane;
+                const bool ok = i < A.total;
+                if (A.hash && ok) A.hash[i] = v;
+                const uint64_t bm = __ballot(ok && v < A.threshold);
+                if (lane == 0) A.cand[(tile0 - O) >> 6] = bm;
+            }
         }
-        g[j] = v;
     }
-    __syncthreads();
-    const int64_t i = base + tid;
-    bool cand = false;
-    if (i < A.total) {
-        const int kmax = (int)min<int64_t>(63, i - stream_start(A, i));
-        uint64_t h = 0;
-        for (int k = kmax; k >= 0; --k) h = (h << 1) + g[tid + 64 - k];
-        if (A.hash) A.hash[i] = h;
-        cand = h < A.threshold;
-    }
-    const uint64_t m = __ballot(cand);
-    const int64_t w0 = base + (tid & ~63);
-    if ((tid & 63) == 0 && w0 < A.total) A.cand[(w0 - A.offsets[0]) >> 6] = m;
 }
 
+// The walk reads the stream's bitmask from an LDS window of kCutWords words,
+// refilled (coalesced) whenever the scan needs words past it.  Positions are
+// 32-bit and relative to the stream start (a stream is shorter than 2^31
+// tokens); the word found by the ballot is read with readlane, so the walk's
+// state stays wave-uniform (scalar).
+constexpr int kCutWords = 4096;
+
 __global__ __launch_bounds__(64) void cut_kernel(const KeyArgs A) {
+    __shared__ uint64_t win[kCutWords];
     const int s = blockIdx.x, lane = threadIdx.x;
-    const int64_t S = A.offsets[s], E = A.offsets[s + 1], O = A.offsets[0];
-    int64_t p = S;
-    int k = 0;
-    while (p < E) {
-        const int64_t lo = p + A.min_len - 1, hi = min(p + A.max_len, E) - 1;
-        int64_t end = hi + 1;
+    const int64_t O = A.offsets[0], S = A.offsets[s];
+    const int L = (int)(A.offsets[s + 1] - S);
+    const int64_t ws = (S - O) >> 6;         // first bitmask word of the stream
+    const int sh = (int)((S - O) & 63);      // bit of the stream's first token in it
+    const int wlast = L > 0 ? (sh + L - 1) >> 6 : -1;    // last word, stream-relative
+    int wb = -kCutWords;                     // first word held in win (none yet)
+    int32_t* ce = A.chunk_end + (int64_t)s * A.cap;
+    int p = 0, k = 0;
+    while (p < L) {
+        const int lo = p + A.min_len - 1, hi = min(p + A.max_len, L) - 1;
+        int end = hi + 1;
         if (lo <= hi) {
-            // bitmask words hold tokens O + 64 w .. O + 64 w + 63
-            const int64_t wlo = (lo - O) >> 6, whi = (hi - O) >> 6;
-            for (int64_t w0 = wlo; w0 <= whi; w0 += 64) {
-                const int64_t w = w0 + lane;
+            const int wlo = (sh + lo) >> 6, whi = (sh + hi) >> 6;
+            const int blo = (sh + lo) & 63, bhi = (sh + hi) & 63;
+            for (int w0 = wlo; w0 <= whi; w0 += 64) {
+                if (w0 < wb || w0 + 64 > wb + kCutWords) {
+                    __syncthreads();
+                    // 16 loads in flight per lane; batches past the stream's end are skipped
+                    for (int j0 = 0; j0 < kCutWords && w0 + j0 <= wlast; j0 += 64 * 16) {
+                        uint64_t r[16];
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {   // clamped: unconditional loads
+                            const int j = j0 + 64 * i + lane;
+                            r[i] = A.cand[ws + min(w0 + j, wlast)];
+                            if (w0 + j > wlast) r[i] = 0;
+                        }
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) win[j0 + 64 * i + lane] = r[i];
+                    }
+                    __syncthreads();
+                    wb = w0;
+                }
+                const int w = w0 + lane;
                 uint64_t bits = 0;
                 if (w <= whi) {
-                    bits = A.cand[w];
-                    if (w == wlo) bits &= ~0ull << ((lo - O) & 63);
-                    const int top = (int)((hi - O) & 63);
-                    if (w == whi && top < 63) bits &= (2ull << top) - 1;
+                    bits = win[w - wb];
+                    if (w == wlo) bits &= ~0ull << blo;
+                    if (w == whi && bhi < 63) bits &= (2ull << bhi) - 1;
                 }
                 const uint64_t any = __ballot(bits != 0);
                 if (any) {
                     const int first = __ffsll((unsigned long long)any) - 1;
-                    const uint32_t blo = __shfl((uint32_t)bits, first), bhi = __shfl((uint32_t)(bits >> 32), first);
-                    const uint64_t fb = (uint64_t)blo | ((uint64_t)bhi << 32);
-                    end = O + ((w0 + first) << 6) + (__ffsll((unsigned long long)fb) - 1) + 1;
+                    const uint32_t flo = __builtin_amdgcn_readlane((int)(uint32_t)bits, first);
+                    const uint32_t fhi = __builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), first);
+                    const int bit = flo ? __ffs(flo) - 1 : 31 + __ffs(fhi);
+                    end = ((w0 + first) << 6) + bit - sh + 1;
                     break;
                 }
             }
@@ -154,28 +231,104 @@ __global__ __launch_bounds__(64) void cut_kernel(const KeyArgs A) {
             if (lane == 0) raise_error(KVR_DEV_RANGE);
             break;
         }
-        if (lane == 0) A.chunk_end[(int64_t)s * A.cap + k] = (int32_t)(end - S);
+        if (lane == 0) ce[k] = end;
         ++k;
         p = end;
     }
     if (lane == 0) A.n_chunks[s] = k;
 }
 
-__global__ __launch_bounds__(256) void fp_kernel(const KeyArgs A) {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t s = gid / A.cap;
-    const int k = (int)(gid - s * A.cap);
-    if (s >= A.n_streams || k >= A.n_chunks[s]) return;
-    const int32_t* ce = A.chunk_end + s * A.cap;
-    const int start = k == 0 ? 0 : ce[k - 1], end = ce[k];
-    const int32_t* t = A.tokens + A.offsets[s];
-    A.chunk_fp[s * A.cap + k] = xxh64_tokens(t + start, end - start, A.seed);
-    if (A.s1_fp) {
-        uint64_t* o = A.s1_fp + (s * A.cap + k) * A.s1_slots;
-        for (int w = 0; w < A.s1_slots; ++w) {
-            const int a = start + w * A.s1_window;
-            o[w] = a < end ? xxh64_tokens(t + a, min(A.s1_window, end - a), A.seed) : 0;
+// One wave per chunk.  Each workgroup first scans n_chunks into a prefix in
+// LDS, then takes chunks g = blockIdx.x, blockIdx.x + gridDim.x, ... of the
+// concatenated chunk list, so the work is spread evenly whatever the chunk
+// counts per stream.  A chunk's hashes are items: item 0 the chunk, item
+// 1 + w its S1 window w.  Each item takes four lanes, one per stripe
+// accumulator, so a pass runs 16 items side by side.  The pass's token range
+// is staged in LDS kFpPiece tokens at a time, with kFpHalo tokens on either
+// side so that a stripe starting in the piece, and a tail ending in it, read
+// only staged tokens.  An item is finished (accumulators merged, tail,
+// avalanche) in the piece that holds its last token.
+constexpr int kFpPiece = 2048;
+constexpr int kFpHalo = 8;
+constexpr int kFpGrid = 4096;
+
+__global__ __launch_bounds__(64) void fp_kernel(const KeyArgs A) {
+    __shared__ int32_t buf[kFpPiece + 2 * kFpHalo];
+    __shared__ int pre[kKeyMaxStreams + 1];
+    const int lane = threadIdx.x, acc = lane & 3, grp = lane >> 2;
+    int carry = 0;
+    for (int s0 = 0; s0 < A.n_streams; s0 += 64) {
+        int v = s0 + lane < A.n_streams ? A.n_chunks[s0 + lane] : 0;
+        for (int dd = 1; dd < 64; dd <<= 1) {
+            const int u = __shfl_up(v, dd);
+            if (lane >= dd) v += u;
         }
+        if (s0 + lane < A.n_streams) pre[s0 + lane + 1] = carry + v;
+        carry += __shfl(v, 63);
+    }
+    if (lane == 0) pre[0] = 0;
+    __syncthreads();
+    const int total = pre[A.n_streams];
+    const int W = A.s1_window;
+    for (int g = blockIdx.x; g < total; g += gridDim.x) {
+        int s = 0, hi = A.n_streams - 1;        // last stream with pre[s] <= g
+        while (s < hi) {
+            const int mid = (s + hi + 1) >> 1;
+            if (pre[mid] <= g) s = mid; else hi = mid - 1;
+        }
+        const int k = g - pre[s];
+        const int64_t c = (int64_t)s * A.cap + k;
+        const int32_t* ce = A.chunk_end + (int64_t)s * A.cap;
+        const int start = k == 0 ? 0 : ce[k - 1];
+        const int len = ce[k] - start;
+        const int32_t* t = A.tokens + A.offsets[s] + start;
+        const int nw = A.s1_fp ? min(A.s1_slots, (len + W - 1) / W) : 0;
+        const int items = 1 + nw;
+        for (int i0 = 0; i0 < items; i0 += 16) {
+            const int it = i0 + grp;
+            const bool act = it < items;
+            const int st = !act || it == 0 ? 0 : (it - 1) * W;            // item's first token
+            const int nt = !act ? 0 : it == 0 ? len : min(W, len - st);   // and its length
+            const int ns = nt >> 3;                                       // whole stripes
+            const int last = st + nt - 1;
+            const int ilast = min(items, i0 + 16) - 1;
+            const int r0 = i0 == 0 ? 0 : (i0 - 1) * W;                    // the pass's token range
+            const int r1 = i0 == 0 ? len : min(len, ilast * W);
+            uint64_t v = xxh_init(acc, A.seed);
+            for (int base = r0; base < r1; base += kFpPiece) {
+                const int lo = max(0, base - kFpHalo), hi2 = min(len, base + kFpPiece + kFpHalo);
+                int32_t* b0 = buf + kFpHalo - base;                       // b0[x] holds token x
+                __syncthreads();
+                for (int j0 = 0; j0 < hi2 - lo; j0 += 64 * 8) {          // 8 loads in flight per lane
+                    int32_t r[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) r[i] = t[min(lo + j0 + 64 * i + lane, hi2 - 1)];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int x = lo + j0 + 64 * i + lane;
+                        if (x < hi2) b0[x] = r[i];
+                    }
+                }
+                __syncthreads();
+                const int d0 = base - st, d1 = base + kFpPiece - st;
+                const int q0 = d0 <= 0 ? 0 : (d0 + 7) >> 3;
+                const int q1 = d1 <= 0 ? 0 : min(ns, (d1 + 7) >> 3);
+                for (int q = q0; q < q1; ++q) v = xround(v, two_tokens(b0 + st + 8 * q + 2 * acc));
+                const uint32_t vlo = (uint32_t)v, vhi = (uint32_t)(v >> 32);
+                uint64_t va[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    va[b] = (uint64_t)__shfl(vlo, (lane & ~3) + b) | ((uint64_t)__shfl(vhi, (lane & ~3) + b) << 32);
+                if (act && acc == 0 && last >= base && last < base + kFpPiece) {
+                    uint64_t h = ns > 0 ? xxh_converge(va[0], va[1], va[2], va[3]) : A.seed + P5;
+                    h = xxh_tail(h, b0 + st + 8 * ns, nt - 8 * ns, nt);
+                    if (it == 0) A.chunk_fp[c] = h;
+                    else A.s1_fp[c * A.s1_slots + (it - 1)] = h;
+                }
+            }
+        }
+        if (A.s1_fp)
+            for (int w = nw + lane; w < A.s1_slots; w += 64) A.s1_fp[c * A.s1_slots + w] = 0;
     }
 }
 
@@ -185,7 +338,8 @@ hipError_t launch_keys(const KeyArgs& a, hipStream_t s) {
     if (a.n_streams <= 0) return hipSuccess;
     const int64_t n = a.total - a.offsets[0];
     if (n > 0) {
-        hipLaunchKernelGGL(gear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+        const int64_t waves = ((n + 63) / 64 + kGearTiles - 1) / kGearTiles;
+        hipLaunchKernelGGL(gear_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -193,7 +347,7 @@ hipError_t launch_keys(const KeyArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t slots = (int64_t)a.n_streams * a.cap;
-    hipLaunchKernelGGL(fp_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(fp_kernel, dim3((unsigned)std::min<int64_t>(slots, kFpGrid)), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

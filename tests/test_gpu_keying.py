@@ -93,3 +93,41 @@ def test_keys_full_workload_sampled():
         sub = {k: (v[s:s + 1] if v is not None else None) for k, v in out.items()}
         _check([streams[s]], w.gear, w.threshold, w.min_len, w.max_len, w.s1_window, w.seed, [0, len(streams[s])],
                sub, check_hash=False)
+
+
+def test_keys_long_chunks_and_offset_base():
+    """Chunks longer than one LDS piece (forced cuts at max_len 5000 with
+    hardly any candidates) and streams that start past token 0 of the
+    buffer: the leading tokens, out-of-range ids among them, are not read."""
+    import torch
+    import rope_rotation_splice_amd as rrs
+    r = kvsynth.rng(31, 3)
+    vocab = 3000
+    gear = r.integers(0, 2 ** 64, size=vocab, dtype=np.uint64)
+    streams = [r.integers(0, vocab, size=n) for n in (12001, 4999, 5000, 7)]
+    base = 37
+    lead = np.full(base, vocab + 5, dtype=np.int32)
+    flat = np.concatenate([lead] + [np.asarray(s, np.int32) for s in streams])
+    off = (base + np.concatenate([[0], np.cumsum([len(s) for s in streams])])).tolist()
+    tok = torch.from_numpy(flat).cuda()
+    g = torch.from_numpy(gear.view(np.int64)).cuda()
+    for thr, lo, hi, s1 in [(1 << 50, 64, 5000, 128), (1 << 57, 100, 3000, 1000), (1 << 50, 3000, 4100, 77)]:
+        out = rrs.registry_chunk_keys(tok, off, g, thr, lo, hi, s1, seed=11, with_hash=True)
+        torch.cuda.synchronize()
+        assert rrs.device_errors() == 0
+        _check(streams, gear, thr, lo, hi, s1, 11, off, out)
+        if lo > 2048 or thr == 1 << 50:
+            ends = out["chunk_end"][0][:int(out["n_chunks"][0])].tolist()
+            assert max(e - b for b, e in zip([0] + ends[:-1], ends)) > 2048
+
+
+def test_keys_long_stream_window_refill():
+    """A stream of 300000 tokens: its candidate bitmask (4688 words) is
+    longer than the cut walk's on-chip window, so the walk refills it."""
+    import rope_rotation_splice_amd as rrs
+    r = kvsynth.rng(31, 4)
+    gear = r.integers(0, 2 ** 64, size=20000, dtype=np.uint64)
+    streams = [r.integers(0, 20000, size=300000), r.integers(0, 20000, size=999)]
+    off, out = _run(streams, gear, 1 << 56, 64, 2048, 128, with_hash=False)
+    assert rrs.device_errors() == 0
+    _check(streams, gear, 1 << 56, 64, 2048, 128, 0, off, out, check_hash=False)
