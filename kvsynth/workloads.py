@@ -279,6 +279,42 @@ def rotate_on_read_decode(batch=32, ctx=32768, heads=128, block_size=64, delta_m
         scale=1.0 / math.sqrt(576.0), seed_keys=(cfg,))
 
 
+@dataclass
+class GqaDecodeWorkload:
+    name: str
+    batch: int
+    ctx: int
+    q_heads: int
+    block_size: int
+    n_blocks: int
+    block_tables: np.ndarray      # int32 [batch, ctx // block_size]
+    pending_delta: np.ndarray     # int32 [batch, ctx // block_size]
+    seq_lens: np.ndarray          # int32 [batch]
+    scale: float
+    shape: GQA = GQA(n_layers=1)
+    seed_keys: tuple = field(default_factory=tuple)
+
+
+def gqa_rotate_on_read_decode(batch=32, ctx=32768, q_heads=32, kv_heads=8, head_dim=128, block_size=64,
+                              delta_max=30000, cfg=7, seq_lens=None, spare_blocks=0):
+    """Decode over a paged GQA cache (K and V of kv_heads x head_dim bf16,
+    RoPE base 500000, separate pools) whose blocks carry a pending shift
+    delta ~ U{-delta_max..delta_max}; q_heads / kv_heads query heads share
+    each KV head; softmax scale 1/sqrt(head_dim)."""
+    r = rng(cfg, 0)
+    bps = ctx // block_size
+    n_blocks = batch * bps + spare_blocks
+    bt = r.permutation(n_blocks)[: batch * bps].astype(np.int32).reshape(batch, bps)
+    pend = r.integers(-delta_max, delta_max, size=(batch, bps), endpoint=True).astype(np.int32)
+    if seq_lens is None:
+        seq_lens = np.full(batch, ctx, np.int32)
+    return GqaDecodeWorkload(
+        name=f"gqa_decode_rotate_on_read_b{batch}_ctx{ctx}_h{q_heads}_kv{kv_heads}", batch=batch, ctx=ctx,
+        q_heads=q_heads, block_size=block_size, n_blocks=n_blocks, block_tables=bt, pending_delta=pend,
+        seq_lens=np.asarray(seq_lens, np.int32), scale=1.0 / math.sqrt(float(head_dim)),
+        shape=GQA(n_layers=1, heads=kv_heads, head_dim=head_dim), seed_keys=(cfg,))
+
+
 # ---------------------------------------------------------------- keying ---
 
 @dataclass

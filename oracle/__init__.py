@@ -35,11 +35,16 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
 * ``lazy``      -- pinned: slot map equal to the eager splice's, block
                    conservation, one-rotation composition.
 * ``decode``    -- pinned: textbook softmax attention on explicitly rotated keys,
-                   needle retrieval, brute-force per-key loop on tiny inputs.
+                   needle retrieval, brute-force per-key loop on tiny inputs;
+                   the GQA form against torch's scaled_dot_product_attention on
+                   independently rotated keys, a needle, and a grouping mutant.
+* ``keying``    -- pinned: xxHash64 against the xxhash library and its published
+                   empty-input value, the Gear recurrence against its window
+                   sum, the cut rule by brute force, content alignment.
 * FORGET mode   -- status and truncated length only; parity unpinned beyond that
                    (truly forgetting needs a model re-prefill).
 * patch frame   -- the patch is added after rotation, in the target frame, as the
                    reuse operator is written; parity unpinned beyond that formula.
 """
 
-from . import bf16, rope, splice, gather, patch, decode, lazy, tolerance  # noqa: F401
+from . import bf16, rope, splice, gather, patch, decode, lazy, keying, tolerance  # noqa: F401

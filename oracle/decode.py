@@ -68,3 +68,69 @@ def token_deltas(block_deltas, seq_len, block_size):
     """Pending shift of every token t < seq_len from the per-block table."""
     t = np.arange(seq_len)
     return np.asarray(block_deltas)[t // block_size]
+
+
+# ------------------------------------------------------------- GQA decode ---
+#
+# Kamera §2 re-rotates the whole GQA key and hooks its correction into the
+# attention kernel; Irminsul §2.2 and §4 apply the pending rotation inside
+# attention, on the load path, without writing a rotated copy back.  Taken
+# together for a GQA cache (Kamera's shape: KV heads of dimension d, all of K
+# rotary, V position-free):
+#
+#   s_t = scale * q_h . (R(delta_blk(t)) k_{t, g(h)}),   g(h) = h // (H / G)
+#   O_h = sum_t softmax(s)_t v_{t, g(h)},   LSE_h = ln sum_t exp(s_t)
+#
+# Readings: query head h reads KV head h // (H / G) (consecutive query heads
+# share a KV head); the attended key is the exact rotation of the stored key
+# (no rounding: the rotation is applied in attention, not stored); one decode
+# query attends to every cached token.
+
+
+def gqa_decode(q, k, v, delta_tok, scale, theta, kv_heads):
+    """GQA decode attention for one sequence, float64.
+
+    q [H, d]; k, v [T, G*d] (stored rows, G = kv_heads); delta_tok [T].
+    Returns (O [H, d], LSE [H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    H, d = q.shape
+    G = int(kv_heads)
+    if H % G:
+        raise ValueError("query heads must be a multiple of KV heads")
+    grp = H // G
+    k_hat = rope.rotate(np.asarray(k, dtype=np.float64), np.asarray(delta_tok), G, d, theta)
+    v = np.asarray(v, dtype=np.float64)
+    o = np.empty((H, d))
+    lse = np.empty(H)
+    for h in range(H):
+        g = h // grp
+        s = scale * (k_hat[:, g * d:(g + 1) * d] @ q[h])          # [T]
+        m = s.max()
+        e = np.exp(s - m)
+        z = e.sum()
+        o[h] = (e / z) @ v[:, g * d:(g + 1) * d]
+        lse[h] = m + np.log(z)
+    return o, lse
+
+
+def gqa_score_bound(q, k, delta_tok, scale, theta, kv_heads):
+    """Per-head bound on the score error of attending with bf16 operands.
+
+    A kernel may apply R(-delta) to q instead of R(delta) to k (the same
+    product, since R is orthogonal) and round that rotated query to bf16:
+    each element moves by at most 2^-8 of its magnitude, so a score moves by
+    at most scale * 2^-8 * max_t sum_i |(R(-delta_t) q_h)_i| |k_{t,i}|.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    H, d = q.shape
+    G = int(kv_heads)
+    grp = H // G
+    k = np.asarray(k, dtype=np.float64)
+    dt = np.asarray(delta_tok)
+    out = np.empty(H)
+    for h in range(H):
+        g = h // grp
+        qr = rope.rotate(np.broadcast_to(q[h], (len(dt), d)), -dt, 1, d, theta)   # [T, d]
+        out[h] = scale * 2.0 ** -8 * (np.abs(qr) * np.abs(k[:, g * d:(g + 1) * d])).sum(axis=1).max()
+    return out
