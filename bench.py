@@ -44,7 +44,8 @@ MLA_ROW_BYTES = 1152
 KERNEL_SOURCES = {
     "reloc_kernel": ["relocate.hip"],
     "patch_kernel": ["patch.hip"],
-    "mla_decode_kernel": ["decode.hip"],
+    "mla_decode_kernel": ["decode.hip", "kvr_lds.h"],
+    "gqa_decode_kernel": ["gqa_decode.hip", "kvr_lds.h"],
 }
 SHARED_SOURCES = ["kvr_device.h", "kvr_internal.h", "api.cpp"]
 

@@ -269,6 +269,44 @@ kvr_status mla_decode_rotate_on_read(const void* q_nope, const void* q_rope,
                                      hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * gqa_decode_rotate_on_read -- one decode step of GQA attention over a paged
+ * cache whose blocks carry a pending rotary shift (Kamera, section 2: in GQA
+ * all of K is rotary and is re-rotated, V is position-free; Irminsul,
+ * sections 2.2 and 4: the shift is applied inside attention, on the load
+ * path, and never written back).  For sequence b and query head h, with G =
+ * cache->rope_heads KV heads and g = h / (q_heads / G):
+ *   s_t = scale * q[b][h] . (R(delta_blk(t)) K_t[g])
+ *   out[b][h] = sum_t softmax(s)_t V_t[g],   lse[b][h] = ln sum_t exp(s_t)
+ * over t < seq_lens[b]; delta_blk(t) = d_pending_delta[b][t / block_size].
+ * The kernel applies R(-delta) to the query once per block (the same scores,
+ * R being orthogonal) and keeps the rotated query to about 16 bits.
+ *   q              : device bf16 [batch][q_heads][128], 16-byte aligned
+ *   cache          : GQA layout: rope = K with rope_heads = G and rope_dim 128,
+ *                    pf = V with pf_width = G * 128, both bf16; block_size 64
+ *   q_heads        : a multiple of G, at most 16 query heads per KV head
+ *   d_block_tables, d_pending_delta : device int32 [batch][bt_stride]
+ *   d_seq_lens     : device int32 [batch]; max_seq_len (host) bounds them
+ *   out            : device bf16 [batch][q_heads][128]; lse : device f32 [batch][q_heads]
+ *                    (a sequence of length 0 gives out 0 and lse -inf)
+ *   d_workspace    : kvr_gqa_decode_workspace_bytes() bytes, 256-byte aligned
+ * Device errors: KVR_DEV_BAD_BLOCK for a block id outside [0, n_blocks) (its
+ * tokens are skipped).
+ * Errors: KVR_E_ARG, KVR_E_RANGE (layer, max_seq_len past the table),
+ * KVR_E_WORKSPACE, KVR_E_UNSUPPORTED (other layouts, dtypes, head counts,
+ * row strides above 16 MiB), KVR_E_HIP.
+ * ---------------------------------------------------------------------- */
+size_t kvr_gqa_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t max_seq_len);
+
+kvr_status gqa_decode_rotate_on_read(const void* q, int32_t batch, int32_t q_heads,
+                                     const kvr_cache* cache, int32_t layer,
+                                     const int32_t* d_block_tables,
+                                     const int32_t* d_pending_delta, int32_t bt_stride,
+                                     const int32_t* d_seq_lens, int32_t max_seq_len,
+                                     float scale, void* out, float* lse,
+                                     void* d_workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * leyline_splice_lazy -- a block-aligned AMORTIZE splice done as an edit of
  * the block table and of the per-block pending shifts; no KV byte moves.
  * (Leyline, sections 2.2-2.3: the downstream slots are re-indexed and owe

@@ -305,6 +305,33 @@ def mla_decode_rotate_on_read(q_nope, q_rope, cache, layer, block_tables, pendin
     return out, lse
 
 
+def gqa_decode_rotate_on_read(q, cache, layer, block_tables, pending_delta, seq_lens, scale,
+                              max_seq_len=None, out=None, lse=None, workspace=None):
+    """One GQA decode step over a paged cache (K = rope part, V = position-free
+    part) with per-block pending shifts applied in attention.
+    q: bf16 [b, q_heads, 128].  Returns (out bf16 [b, q_heads, 128], lse f32 [b, q_heads])."""
+    lib = _abi.load()
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [batch, heads, dim] tensor")
+    b, h = int(q.shape[0]), int(q.shape[1])
+    kv = int(cache.c.rope_heads)
+    if max_seq_len is None:
+        max_seq_len = int(block_tables.shape[1]) * cache.block_size
+    if out is None:
+        out = torch.empty((b, h, int(q.shape[2])), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, h), dtype=torch.float32, device=q.device)
+    need = int(lib.kvr_gqa_decode_workspace_bytes(b, h, kv, int(max_seq_len)))
+    ws = workspace if workspace is not None else _workspace(need, q.device, "gqa_decode")
+    st = lib.gqa_decode_rotate_on_read(q.data_ptr(), b, h, ctypes.byref(cache.c), int(layer),
+                                       block_tables.data_ptr(), pending_delta.data_ptr(), int(block_tables.stride(0)),
+                                       seq_lens.data_ptr(), int(max_seq_len), float(scale), out.data_ptr(),
+                                       lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                       _stream_handle())
+    _check("gqa_decode_rotate_on_read", st)
+    return out, lse
+
+
 def device_errors():
     """Synchronize and return (then clear) the library's device error bits."""
     lib = _abi.load()

@@ -310,9 +310,11 @@ kvr_status kvr_device_errors(uint32_t* flags) {
     const uint32_t x = read_and_clear_errors_decode();
     const uint32_t y = read_and_clear_errors_lazy();
     const uint32_t z = read_and_clear_errors_keys();
-    if (v == 0xffffffffu || w == 0xffffffffu || x == 0xffffffffu || y == 0xffffffffu || z == 0xffffffffu)
+    const uint32_t u = read_and_clear_errors_gqa_decode();
+    if (v == 0xffffffffu || w == 0xffffffffu || x == 0xffffffffu || y == 0xffffffffu || z == 0xffffffffu ||
+        u == 0xffffffffu)
         return hip_fail(hipErrorUnknown);
-    *flags = v | w | x | y | z;
+    *flags = v | w | x | y | z | u;
     return KVR_OK;
 }
 
@@ -591,6 +593,83 @@ kvr_status mla_decode_rotate_on_read(const void* q_nope, const void* q_rope, int
     a.part_ml = (float*)((char*)d_ws + round_up((size_t)batch * a.n_split  * heads * 512 * 4));
     std::memcpy(a.omega, omega, sizeof(a.omega));
     hipError_t e = launch_decode(a, (uint16_t*)out, lse, stream);
+    return e == hipSuccess ? KVR_OK : hip_fail(e);
+}
+
+// Splits of the GQA decode: about 2048 single-wave workgroups in all, at most
+// kGqaMaxBlocks blocks per split.
+static void gqa_split(int32_t batch, int32_t kv_heads, int32_t max_seq_len, int32_t& n_split, int32_t& bps) {
+    const int32_t blocks = std::max(1, (max_seq_len + kDecBlockTokens - 1) / kDecBlockTokens);
+    const int32_t pairs = std::max(1, batch * kv_heads);
+    n_split = std::max<int32_t>(1, (2048 + pairs - 1) / pairs);
+    n_split = std::max(n_split, (blocks + kGqaMaxBlocks - 1) / kGqaMaxBlocks);
+    n_split = std::min(n_split, blocks);
+    bps = (blocks + n_split - 1) / n_split;
+    n_split = (blocks + bps - 1) / bps;
+}
+
+size_t kvr_gqa_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t max_seq_len) {
+    if (batch < 1 || kv_heads < 1 || q_heads < kv_heads || q_heads % kv_heads ||
+        q_heads / kv_heads > kGqaMaxGroup || max_seq_len < 0)
+        return 0;
+    int32_t n_split, bps;
+    gqa_split(batch, kv_heads, max_seq_len, n_split, bps);
+    const size_t rows = (size_t)batch * n_split * q_heads;
+    return round_up(rows * kGqaDim * 4) + round_up(rows * 8);
+}
+
+kvr_status gqa_decode_rotate_on_read(const void* q, int32_t batch, int32_t q_heads, const kvr_cache* cache,
+                                     int32_t layer, const int32_t* d_block_tables, const int32_t* d_pending_delta,
+                                     int32_t bt_stride, const int32_t* d_seq_lens, int32_t max_seq_len, float scale,
+                                     void* out, float* lse, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    Pool pool;
+    double omega[kMaxPairs];
+    kvr_status st = make_pool(cache, pool, omega);
+    if (st != KVR_OK) return st;
+    const int32_t G = cache->rope_heads;
+    if (cache->pf_dtype != KVR_BF16 || cache->rope_dtype != KVR_BF16 || cache->rope_dim != kGqaDim ||
+        cache->pf_width != G * kGqaDim || cache->block_size != kDecBlockTokens)
+        return KVR_E_UNSUPPORTED;
+    if (batch < 1 || q_heads < G || q_heads % G || q_heads / G > kGqaMaxGroup) return KVR_E_UNSUPPORTED;
+    if (layer < 0 || layer >= cache->n_layers) return KVR_E_RANGE;
+    if (!q || !aligned16(q) || !out || !lse) return KVR_E_ARG;
+    if (!d_block_tables || !d_pending_delta || !d_seq_lens || bt_stride < 1) return KVR_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(d_block_tables) | reinterpret_cast<uintptr_t>(d_pending_delta) |
+         reinterpret_cast<uintptr_t>(d_seq_lens) | reinterpret_cast<uintptr_t>(lse)) & 3u)
+        return KVR_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(out) & 1u) || !std::isfinite(scale)) return KVR_E_ARG;
+    // the direct loads address rows with 32-bit offsets from a block's row
+    if (pool.pf_r > (1 << 24) || pool.rp_r > (1 << 24)) return KVR_E_UNSUPPORTED;
+    if (max_seq_len < 0 || (int64_t)max_seq_len > (int64_t)bt_stride * kDecBlockTokens) return KVR_E_RANGE;
+    const size_t need = kvr_gqa_decode_workspace_bytes(batch, q_heads, G, max_seq_len);
+    if (!d_ws || (reinterpret_cast<uintptr_t>(d_ws) % kAlign) || ws_bytes < need) return KVR_E_WORKSPACE;
+
+    GqaDecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.k = pool.rp + (int64_t)layer * pool.rp_l;
+    a.k_b = pool.rp_b;
+    a.k_r = pool.rp_r;
+    a.v = pool.pf + (int64_t)layer * pool.pf_l;
+    a.v_b = pool.pf_b;
+    a.v_r = pool.pf_r;
+    a.n_blocks = pool.n_blocks;
+    a.q = (const uint16_t*)q;
+    a.bt = d_block_tables;
+    a.pend = d_pending_delta;
+    a.seq_lens = d_seq_lens;
+    a.bt_stride = bt_stride;
+    a.max_len = max_seq_len;
+    a.batch = batch;
+    a.q_heads = q_heads;
+    a.kv_heads = G;
+    a.group = q_heads / G;
+    gqa_split(batch, G, max_seq_len, a.n_split, a.blocks_per_split);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const size_t rows = (size_t)batch * a.n_split * q_heads;
+    a.part_o = (float*)d_ws;
+    a.part_ml = (float*)((char*)d_ws + round_up(rows * kGqaDim * 4));
+    for (int j = 0; j < kGqaDim / 2; ++j) a.omega[j] = omega[j];
+    hipError_t e = launch_gqa_decode(a, (uint16_t*)out, lse, stream);
     return e == hipSuccess ? KVR_OK : hip_fail(e);
 }
 

@@ -116,6 +116,27 @@ struct DecodeArgs {
     double omega[32];
 };
 
+// GQA decode (gqa_decode.hip): one wave per (sequence, KV head, split).
+constexpr int kGqaDim = 128;          // head dimension the GQA decode reads
+constexpr int kGqaMaxGroup = 16;      // query heads per KV head
+constexpr int kGqaMaxBlocks = 64;     // KV blocks per split (tables in LDS)
+
+struct GqaDecodeArgs {
+    const char* k; int64_t k_b, k_r;          // K pool, layer applied; bytes
+    const char* v; int64_t v_b, v_r;          // V pool, layer applied; bytes
+    int32_t n_blocks;
+    const uint16_t* q;                         // bf16 [batch][q_heads][128]
+    const int32_t* bt;                         // [batch][bt_stride]
+    const int32_t* pend;                       // [batch][bt_stride]
+    const int32_t* seq_lens;                   // [batch]
+    int32_t bt_stride, max_len;
+    int32_t batch, q_heads, kv_heads, group, n_split, blocks_per_split;
+    float scale_log2;                          // softmax scale * log2(e)
+    float* part_o;                             // [batch][kv_heads][n_split][group][128]
+    float* part_ml;                            // [batch][kv_heads][n_split][group] x (max, sum)
+    double omega[kGqaDim / 2];
+};
+
 // Block-table splice (lazy.hip): one workgroup per sequence.
 constexpr int kLazyMaxBlocks = 8192;  // table entries a workgroup stages in LDS
 constexpr int kLazyMaxSeq = 96;       // sequences per launch
@@ -137,6 +158,7 @@ struct LazyArgs {
     LazySeq seqs[kLazyMaxSeq];
 };
 static_assert(sizeof(LazyArgs) <= 4000, "lazy splice arguments too large");
+static_assert(sizeof(GqaDecodeArgs) <= 4000, "GQA decode arguments too large");
 
 // Registry keying (keying.hip).
 constexpr int kKeyMaxStreams = 240;
@@ -173,6 +195,9 @@ uint32_t read_and_clear_errors_patch();
 // Decode (decode.hip): split kernel + combine kernel.
 hipError_t launch_decode(const DecodeArgs& a, uint16_t* out, float* lse, hipStream_t s);
 uint32_t read_and_clear_errors_decode();
+// GQA decode (gqa_decode.hip): split kernel + combine kernel.
+hipError_t launch_gqa_decode(const GqaDecodeArgs& a, uint16_t* out, float* lse, hipStream_t s);
+uint32_t read_and_clear_errors_gqa_decode();
 // Block-table splice (lazy.hip).
 hipError_t launch_lazy(const LazyArgs& a, hipStream_t s);
 uint32_t read_and_clear_errors_lazy();
