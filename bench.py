@@ -564,6 +564,86 @@ class Decode:
                           f"(its two matmuls go through numpy's BLAS, which may use up to {thr} threads)"}
 
 
+class GqaDecode:
+    """Rotate-on-read GQA decode: batch 32, 32768 cached tokens per sequence,
+    32 query heads on 8 KV heads of 128 (K and V bf16, separate pools, RoPE
+    base 500000), paged 64-token blocks each carrying a pending shift
+    ~ U{-30000..30000}, scale 1/sqrt(128).  A slot is a key rotated on read
+    (per KV head: 8 per token)."""
+    name = "gqa_decode"
+    kernel = "gqa_decode_kernel + combine"
+
+    def __init__(self):
+        import kvsynth
+        self.w = kvsynth.gqa_rotate_on_read_decode()
+        w = self.w
+        G, D = w.shape.heads, w.shape.head_dim
+        self.slots = w.batch * w.ctx * G
+        cache = w.batch * w.ctx * G * D * 2 * 2
+        q = w.batch * w.q_heads * D * 2
+        o = w.batch * w.q_heads * D * 2 + w.batch * w.q_heads * 4
+        tables = 2 * w.block_tables.nbytes + w.seq_lens.nbytes
+        self.bytes = cache + q + o + tables
+        self.flops = 2 * w.batch * w.ctx * w.q_heads * 2 * D
+        self.launches = 1
+        self.config = {"workload": "gqa_decode_rotate_on_read", "batch": w.batch, "ctx": w.ctx,
+                       "q_heads": w.q_heads, "kv_heads": G, "head_dim": D, "block_size": w.block_size,
+                       "pending_delta": "U{-30000..30000} per block", "scale": "1/sqrt(128)",
+                       "keys_per_step": self.slots, "gflop": self.flops / 1e9}
+
+    def setup(self):
+        import torch
+        import kvsynth
+        import rope_rotation_splice_amd as rrs
+        w = self.w
+        G, D = w.shape.heads, w.shape.head_dim
+        self.kp = torch.empty((1, w.n_blocks, w.block_size, G * D), dtype=torch.bfloat16, device="cuda")
+        self.vp = torch.empty_like(self.kp)
+        self.q = torch.empty((w.batch, w.q_heads, D), dtype=torch.bfloat16, device="cuda")
+        kvsynth.fill_normal_(self.kp, 7, 1)
+        kvsynth.fill_normal_(self.vp, 7, 2)
+        kvsynth.fill_normal_(self.q, 7, 3)
+        self.cache = rrs.KVCache.gqa(self.kp, self.vp, G, D)
+        self.bt = torch.from_numpy(w.block_tables).cuda()
+        self.pend = torch.from_numpy(w.pending_delta).cuda()
+        self.lens = torch.from_numpy(w.seq_lens).cuda()
+        self.out = torch.empty((w.batch, w.q_heads, D), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device="cuda")
+        self.rrs = rrs
+
+    def step(self):
+        w = self.w
+        self.rrs.gqa_decode_rotate_on_read(self.q, self.cache, 0, self.bt, self.pend, self.lens, w.scale,
+                                           max_seq_len=w.ctx, out=self.out, lse=self.lse)
+
+    def cpu_baseline(self, budget_s):
+        import kvsynth
+        from oracle import decode as odec, rope as orope, bf16 as ob
+        w = self.w
+        G, D = w.shape.heads, w.shape.head_dim
+        th = orope.inv_freq(D, 500000.0)
+        keys, spent, seqs = 0, 0.0, 0
+        for b in range(w.batch):
+            r = kvsynth.rng(7, 9, b)
+            k = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, G * D)))
+            v = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, G * D)))
+            q = ob.to_f64(kvsynth.bf16_normal(r, (w.q_heads, D)))
+            d = odec.token_deltas(w.pending_delta[b], w.ctx, 64)
+            t0 = time.perf_counter()
+            odec.gqa_decode(q, k, v, d, w.scale, th, G)
+            spent += time.perf_counter() - t0
+            keys += w.ctx * G
+            seqs += 1
+            if spent >= budget_s:
+                break
+        import os as _os
+        thr = int(_os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(_os.sched_getaffinity(0))
+        return {"value": keys / spent, "unit": "keys/s", "cores": thr, "kind": "oracle",
+                "sample": f"{seqs} whole sequences ({keys} keys over {G} KV heads, {w.q_heads} query heads), "
+                          f"generation excluded, numpy fp64 (its matrix-vector products go through numpy's BLAS, "
+                          f"which may use up to {thr} threads)"}
+
+
 class Copy:
     """A plain device-to-device copy of the registry gather's byte volume
     (torch's copy kernel): the practical read+write ceiling, and the known-size
@@ -593,7 +673,8 @@ class Copy:
 
 WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "splice_lazy": SpliceLazy,
              "gqa_patch": GqaPatch, "keys": Keys,
-             "decode": Decode, "decode_zero_delta": lambda: Decode(zero_delta=True), "copy": Copy}
+             "decode": Decode, "decode_zero_delta": lambda: Decode(zero_delta=True), "gqa_decode": GqaDecode,
+             "copy": Copy}
 
 
 def main():
@@ -611,7 +692,7 @@ def main():
         return 2
 
     wl = WORKLOADS[args.workload]()
-    unit = "keys/s" if isinstance(wl, Decode) else "slots/s"
+    unit = "keys/s" if isinstance(wl, (Decode, GqaDecode)) else "slots/s"
     # the CPU oracle runs before the GPU is touched
     cpu = None if args.no_cpu_baseline else wl.cpu_baseline(args.cpu_budget)
 
@@ -648,7 +729,7 @@ def main():
     traffic = stored_traffic(wl.kernel, wl.name)
     extra = {}
     if getattr(wl, "flops", None):
-        dt, peak = ("bf16", 2500.0) if isinstance(wl, Decode) else ("fp32", 157.3)
+        dt, peak = ("bf16", 2500.0) if isinstance(wl, (Decode, GqaDecode)) else ("fp32", 157.3)
         extra["matrix_core"] = {"dtype": dt, "achieved_TFLOPs": wl.flops * args.steps / gpu_s / 1e12,
                                 "peak_TFLOPs": peak, "frac": wl.flops * args.steps / gpu_s / 1e12 / peak}
     out = {

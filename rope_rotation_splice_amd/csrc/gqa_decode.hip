@@ -318,30 +318,29 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(const GqaDecodeArgs A) {
 }
 
 // Merge the splits: O = sum_s 2^(m_s - M) O_s / L, L = sum_s 2^(m_s - M) l_s,
-// LSE = ln 2 * (M + log2 L).  One workgroup per (sequence, KV head), one
-// thread per feature, the group's heads in turn.
+// LSE = ln 2 * (M + log2 L).  One workgroup per (sequence, query head), one
+// thread per feature; the split loops are unrolled so their loads overlap.
 __global__ __launch_bounds__(kGqaDim) void gqa_decode_combine(const GqaDecodeArgs A, uint16_t* out, float* lse) {
-    const int g = blockIdx.x % A.kv_heads, b = blockIdx.x / A.kv_heads;
+    const int h = blockIdx.x % A.q_heads, b = blockIdx.x / A.q_heads;
+    const int g = h / A.group, i = h - g * A.group;
     const int f = threadIdx.x;
-    const int64_t bg = (int64_t)b * A.kv_heads + g;
+    const int64_t base = ((int64_t)b * A.kv_heads + g) * A.n_split;      // row = (base + s) * group + i
     const float2* pm = reinterpret_cast<const float2*>(A.part_ml);
-    for (int i = 0; i < A.group; ++i) {
-        float M = kNegInf;
-        for (int s = 0; s < A.n_split; ++s) M = fmaxf(M, pm[(bg * A.n_split + s) * A.group + i].x);
-        float L = 0.f, o = 0.f;
-        if (M != kNegInf)
-            for (int s = 0; s < A.n_split; ++s) {
-                const int64_t row = (bg * A.n_split + s) * A.group + i;
-                const float2 ml = pm[row];
-                if (ml.x == kNegInf) continue;
-                const float w = exp2f(ml.x - M);
-                L += w * ml.y;
-                o += w * A.part_o[row * kGqaDim + f];
-            }
-        const int64_t h = (int64_t)b * A.q_heads + g * A.group + i;
-        out[h * kGqaDim + f] = __builtin_bit_cast(uint16_t, (__bf16)(L > 0.f ? o / L : 0.f));
-        if (f == 0) lse[h] = L > 0.f ? 0.6931471805599453f * (M + log2f(L)) : kNegInf;
+    float M = kNegInf;
+#pragma unroll 8
+    for (int s = 0; s < A.n_split; ++s) M = fmaxf(M, pm[(base + s) * A.group + i].x);
+    float L = 0.f, o = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < A.n_split; ++s) {
+        const int64_t row = (base + s) * A.group + i;
+        const float2 ml = pm[row];
+        const float w = ml.x == kNegInf ? 0.f : exp2f(ml.x - M);
+        L += w * ml.y;
+        o += w * A.part_o[row * kGqaDim + f];
     }
+    const int64_t oh = (int64_t)b * A.q_heads + h;
+    out[oh * kGqaDim + f] = __builtin_bit_cast(uint16_t, (__bf16)(L > 0.f ? o / L : 0.f));
+    if (f == 0) lse[oh] = L > 0.f ? 0.6931471805599453f * (M + log2f(L)) : kNegInf;
 }
 
 }  // namespace
@@ -350,7 +349,7 @@ hipError_t launch_gqa_decode(const GqaDecodeArgs& a, uint16_t* out, float* lse, 
     hipLaunchKernelGGL(gqa_decode_kernel, dim3((unsigned)(a.batch * a.n_split * a.kv_heads)), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gqa_decode_combine, dim3((unsigned)(a.batch * a.kv_heads)), dim3(kGqaDim), 0, s, a, out, lse);
+    hipLaunchKernelGGL(gqa_decode_combine, dim3((unsigned)(a.batch * a.q_heads)), dim3(kGqaDim), 0, s, a, out, lse);
     return hipGetLastError();
 }
 
