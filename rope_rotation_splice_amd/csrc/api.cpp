@@ -250,6 +250,16 @@ void set_factors(const kvr_lowrank* f, const float*& U, const float*& V, int64_t
 // Enqueue patch-kernel launches for `items` (at most kPatchMaxItems each).
 kvr_status run_patch(const Pool& pool, const double* omega, const int32_t* d_bt, std::vector<PatchItem>& items,
                      int n_layers, bool inplace, bool do_rope, bool do_pf, hipStream_t stream) {
+    // The streaming kernel takes bf16 rows in 256-byte units (128-dimension
+    // rotary heads), ranks up to 16, power-of-two blocks of at least 16 rows
+    // and items of at most 4 x kPatchDmaMaxStages x 16 rows; anything else
+    // goes to the tiled kernel.
+    bool dma = pool.bs_shift >= 4 && (!do_rope || (pool.head_bytes == 256 && pool.pairs_per_chunk == 8)) &&
+               (!do_pf || pool.pf_chunks % 16 == 0);
+    for (const PatchItem& it : items)
+        if (it.len > 4 * kPatchDmaMaxStages * 16 || it.rank_rp > 16 || it.rank_pf > 16) dma = false;
+    const int n_ru = do_rope ? pool.rope_items / pool.half_chunks : 0;
+    const int n_units = n_ru + (do_pf ? pool.pf_chunks / 16 : 0);
     size_t i = 0;
     while (i < items.size()) {
         PatchArgs a;
@@ -259,12 +269,15 @@ kvr_status run_patch(const Pool& pool, const double* omega, const int32_t* d_bt,
         a.tile_rows = kPatchTileRows;
         a.do_rope = do_rope;
         a.do_pf = do_pf;
+        a.dma = dma;
+        a.n_units = n_units;
+        a.n_rope_units = n_ru;
         std::memcpy(a.omega, omega, sizeof(a.omega));
         int64_t wg = 0;
         int n = 0;
         for (; i < items.size() && n < kPatchMaxItems; ++i) {
             PatchItem it = items[i];
-            const int64_t add = (int64_t)it.tiles * n_layers;
+            const int64_t add = (int64_t)(dma ? n_units : it.tiles) * n_layers;
             if (n > 0 && wg + add >= ((int64_t)1 << 31)) break;
             it.wg_off = (int32_t)wg;
             wg += add;

@@ -85,11 +85,17 @@ struct PatchItem {
     int32_t wg_off;                            // first workgroup of this item
 };
 
+// Streaming form of the patch kernel (patch_dma_kernel): one workgroup per
+// (item, layer, 256-byte unit of the row), each wave streaming 16-row stages.
+constexpr int kPatchDmaMaxStages = 64;   // stages per wave: items of at most 4 x 64 x 16 rows
+
 struct PatchArgs {
     Pool pool;
     const int32_t* bt;
     int32_t n_items, tile_rows, n_wg;
     int32_t do_rope, do_pf;
+    int32_t dma;                               // 1: patch_dma_kernel (items' wg counts are layers x units)
+    int32_t n_units, n_rope_units;             // units per row; the first n_rope_units are rotary heads
     double omega[kPatchMaxPairs];
     PatchItem items[kPatchMaxItems];
 };

@@ -320,11 +320,234 @@ __global__ __launch_bounds__(kThreads) void patch_kernel(const PatchArgs A) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming form.  One workgroup per (item, layer, unit), a unit being 256
+// bytes of the row: a 128-dimension rotary head or 128 position-free
+// features.  The unit's feature-side factor rows are loaded into registers
+// once; each wave then streams its 16-row sub-tiles (wave w takes sub-tiles
+// w, w + 4, ...) global -> LDS directly, data and U rows, 3 stages ahead,
+// from inline assembly (no registers hold data in flight, no barriers: a
+// wave reads only what it loaded itself).  Results are written back to
+// their LDS slots and stored row by row, so every store covers whole
+// 128-byte lines.  Every stage issues exactly 5
+// direct loads and 4 stores, so the vmcnt waits are exact: rows outside the
+// item or behind a bad block id load a clamped in-range row and store into
+// g_patch_sink instead of being skipped.
+constexpr int kDmaRows = 16;                        // rows per stage (one MFMA sub-tile)
+constexpr int kDmaBuf = 4;                          // stage buffers per wave (3 loads ahead)
+constexpr int kDmaDataB = kDmaRows * 256;           // 4 KB of row data per stage
+constexpr int kDmaUB = 1024;                        // U rows of a stage (16 x at most 16 floats)
+constexpr int kDmaStageB = kDmaDataB + kDmaUB;
+constexpr int kDmaWaveB = kDmaBuf * kDmaStageB;     // 20 KB per wave
+
+__device__ v4u g_patch_sink[64];
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Direct global -> LDS load from a per-lane 64-bit address: 16 bytes of lane
+// l land at LDS address lds + 16 l (lds wave-uniform, carried in M0).
+__device__ __forceinline__ void dma16_va(const char* p, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(p), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+typedef __attribute__((address_space(3))) v4u lds_v4u_t;
+typedef __attribute__((address_space(3))) v4f lds_v4f_t;
+
+template <bool INPLACE>
+__global__ __launch_bounds__(kThreads) void patch_dma_kernel(const PatchArgs A) {
+    __shared__ __attribute__((aligned(1024))) char smem[(kThreads / 64) * kDmaWaveB];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bid = xcd_contiguous(blockIdx.x, gridDim.x);
+    const Pool& P = A.pool;
+
+    int it = 0;
+    {
+        int hi = A.n_items - 1;
+        while (it < hi) {
+            const int mid = (it + hi + 1) >> 1;
+            if (bid >= A.items[mid].wg_off) it = mid; else hi = mid - 1;
+        }
+    }
+    const PatchItem& I = A.items[it];
+    const int local = bid - I.wg_off;
+    const int layer = local / A.n_units, unit = local - layer * A.n_units;
+    const bool rope = unit < A.n_rope_units;
+    const int uo = rope ? unit : unit - A.n_rope_units;
+    const char* dst_base = rope ? P.rp + (int64_t)layer * P.rp_l : P.pf + (int64_t)layer * P.pf_l;
+    const int64_t dst_b = rope ? P.rp_b : P.pf_b, dst_r = rope ? P.rp_r : P.pf_r;
+    const int unit_off = uo * 256;
+    const char* src_base = INPLACE ? nullptr
+                                   : (rope ? I.src_rp + (int64_t)layer * I.src_rp_l : I.src_pf + (int64_t)layer * I.src_pf_l);
+    const int64_t src_r = rope ? I.src_rp_r : I.src_pf_r;
+    const int rank = rope ? I.rank_rp : I.rank_pf;
+    const float* U = rank ? (rope ? I.U_rp + (int64_t)layer * I.u_rp_l : I.U_pf + (int64_t)layer * I.u_pf_l) : nullptr;
+    const float* V = rank ? (rope ? I.V_rp + (int64_t)layer * I.v_rp_l : I.V_pf + (int64_t)layer * I.v_pf_l) : nullptr;
+    const bool rotate = rope && !INPLACE && I.shift != 0;
+    const int len = I.len;
+    const int n_sub = (len + kDmaRows - 1) / kDmaRows;
+    const int n_st = n_sub > wave ? (n_sub - wave + 3) / 4 : 0;       // this wave's stages
+    const int bs = P.bs_shift;
+    const int bmask = P.block_size - 1;
+    const int tok = lane & 15, g = lane >> 4;
+
+    // feature-side factor rows of the unit's 4 groups (A operands)
+    v4f fa[4], fb[4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+        fa[gi] = v4f{0, 0, 0, 0};
+        fb[gi] = fa[gi];
+        if (4 * g < rank) {
+            const int fr = uo * 128 + gi * 32 + 8 * (tok >> 2) + (tok & 3);
+            fa[gi] = *reinterpret_cast<const v4f*>(V + (int64_t)fr * rank + 4 * g);
+            fb[gi] = *reinterpret_cast<const v4f*>(V + (int64_t)(fr + 4) * rank + 4 * g);
+        }
+    }
+    // block ids of this wave's stages: lane k holds those of stage k (first
+    // and last row of the sub-tile; -1 for a bad id)
+    int id0 = -1, id1 = -1;
+    if (lane < n_st) {
+        const int r0 = kDmaRows * (wave + 4 * lane);
+        const int s0 = I.dst0 + r0, s1 = I.dst0 + min(r0 + kDmaRows, len) - 1;
+        id0 = A.bt[s0 >> bs];
+        id1 = A.bt[s1 >> bs];
+        if ((unsigned)id0 >= (unsigned)P.n_blocks) { raise_error(KVR_DEV_BAD_BLOCK); id0 = -1; }
+        if ((unsigned)id1 >= (unsigned)P.n_blocks) { raise_error(KVR_DEV_BAD_BLOCK); id1 = -1; }
+    }
+    // (cos, sin) of this lane's pairs j = 32 gl + 8 g + e (gl < 2, e < 8)
+    float2 cs[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) cs[k] = make_float2(1.f, 0.f);
+    if (rotate) {
+        double om[16];                               // all loads first, then the angles
+#pragma unroll
+        for (int k = 0; k < 16; ++k) om[k] = A.omega[32 * (k >> 3) + 8 * g + (k & 7)];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const double u = (double)I.shift * om[k];
+            const double f = u - rint(u);
+            float s, c;
+            sincosf((float)(f * 6.283185307179586476925), &s, &c);
+            cs[k] = make_float2(c, s);
+        }
+    }
+    // every load so far has landed (the compiler accounts for this wait, so
+    // it adds none later that would drain the direct loads)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (n_st == 0) return;
+
+    const uint32_t lds_w = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem + wave * kDmaWaveB;
+    const char* sink = reinterpret_cast<const char*>(&g_patch_sink[lane]);
+
+    // physical row of item row `row` of stage k (whose ids are i0 / i1), or
+    // nullptr when the row's block id is bad
+    auto row_addr = [&](int k, int row, int i0, int i1) __attribute__((always_inline)) -> const char* {
+        const int slot = I.dst0 + row;
+        const int first = (I.dst0 + kDmaRows * (wave + 4 * k)) >> bs;
+        const int id = (slot >> bs) == first ? i0 : i1;
+        return id < 0 ? nullptr : dst_base + (int64_t)id * dst_b + (int64_t)(slot & bmask) * dst_r + unit_off;
+    };
+    // direct loads of stage kk: 4 x (4 rows x 256 B) of data, then 16 U rows
+    auto issue = [&](int kk) __attribute__((always_inline)) {
+        const int k = min(kk, n_st - 1);
+        const int r0 = kDmaRows * (wave + 4 * k);
+        const uint32_t buf = lds_w + (uint32_t)(kk % kDmaBuf) * kDmaStageB;
+        const int i0 = __builtin_amdgcn_readlane(id0, k), i1 = __builtin_amdgcn_readlane(id1, k);
+        const char* first_addr = nullptr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            const int row = min(r0 + r, len - 1);
+            const uint32_t c = (uint32_t)(lane & 15) ^ (uint32_t)r;
+            const char* a;
+            if (INPLACE) {
+                const char* ra = row_addr(k, row, i0, i1);
+                a = (ra ? ra : dst_base + unit_off) + 16 * c;      // bad block: any in-range row
+            } else {
+                a = src_base + (int64_t)row * src_r + unit_off + 16 * c;
+            }
+            if (i == 0) first_addr = a;
+            dma16_va(a, buf + 1024 * i);
+        }
+        const char* ua = first_addr;
+        if (rank) {
+            const int64_t left = (int64_t)(len - r0) * rank * 4 - 16;   // last 16 bytes of the item's U
+            ua = reinterpret_cast<const char*>(U + (int64_t)r0 * rank) + min<int64_t>(16 * lane, left);
+        }
+        dma16_va(ua, buf + kDmaDataB);
+    };
+
+    for (int kk = 0; kk < 3; ++kk) issue(kk);
+    wait_vm<10>();                                   // stage 0 landed
+    for (int k = 0; k < n_st; ++k) {
+        const uint32_t buf = lds_w + (uint32_t)(k % kDmaBuf) * kDmaStageB;
+        const int r0 = kDmaRows * (wave + 4 * k);
+        const int i0 = __builtin_amdgcn_readlane(id0, k), i1 = __builtin_amdgcn_readlane(id1, k);
+        v4f u = v4f{0, 0, 0, 0};
+        if (4 * g < rank) u = *(const lds_v4f_t*)(size_t)(buf + kDmaDataB + 4 * (tok * rank + 4 * g));
+        v4u x[4];
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+            x[gi] = *(const lds_v4u_t*)(size_t)(buf + tok * 256 + 16 * ((uint32_t)(4 * gi + g) ^ (uint32_t)tok));
+        v4f pa[4], pb[4];
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            pa[gi] = v4f{0, 0, 0, 0};
+            pb[gi] = pa[gi];
+            if (rank) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    pa[gi] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[gi][kk], u[kk], pa[gi], 0, 0, 0);
+                    pb[gi] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[gi][kk], u[kk], pb[gi], 0, 0, 0);
+                }
+            }
+        }
+        if (rope) {
+#pragma unroll
+            for (int gl = 0; gl < 2; ++gl)
+                rot_patch(x[gl], x[gl + 2], cs + 8 * gl, rotate, rank > 0, pa[gl], pb[gl], pa[gl + 2], pb[gl + 2]);
+        } else if (rank) {
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) x[gi] = add_patch(x[gi], pa[gi], pb[gi]);
+        }
+        // Results go back to their own LDS slots and leave row-major: store i
+        // writes rows 4i..4i+3, 256 contiguous bytes each (whole 128-byte
+        // lines), lane l taking chunk position l % 16 of row 4i + l / 16.
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+            *(lds_v4u_t*)(size_t)(buf + tok * 256 + 16 * ((uint32_t)(4 * gi + g) ^ (uint32_t)tok)) = x[gi];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            const uint32_t p = (uint32_t)(lane & 15);
+            const v4u y = *(const lds_v4u_t*)(size_t)(buf + r * 256 + 16 * p);
+            const char* ra = r0 + r < len ? row_addr(k, r0 + r, i0, i1) : nullptr;
+            st16(const_cast<char*>(ra ? ra + 16 * (p ^ (uint32_t)r) : sink), y);
+        }
+        issue(k + 3);
+        if (k == 0) wait_vm<14>();                   // stage k + 1 landed
+        else        wait_vm<18>();
+    }
+    wait_vm<0>();                                    // no load may land in LDS after this
+}
+
 }  // namespace
 
 hipError_t launch_patch(const PatchArgs& a, bool inplace, hipStream_t s) {
-    if (inplace) hipLaunchKernelGGL(patch_kernel<true>, dim3(a.n_wg), dim3(kThreads), 0, s, a);
-    else         hipLaunchKernelGGL(patch_kernel<false>, dim3(a.n_wg), dim3(kThreads), 0, s, a);
+    if (a.dma) {
+        if (inplace) hipLaunchKernelGGL(patch_dma_kernel<true>, dim3(a.n_wg), dim3(kThreads), 0, s, a);
+        else         hipLaunchKernelGGL(patch_dma_kernel<false>, dim3(a.n_wg), dim3(kThreads), 0, s, a);
+    } else {
+        if (inplace) hipLaunchKernelGGL(patch_kernel<true>, dim3(a.n_wg), dim3(kThreads), 0, s, a);
+        else         hipLaunchKernelGGL(patch_kernel<false>, dim3(a.n_wg), dim3(kThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 
