@@ -43,6 +43,7 @@ MLA_ROW_BYTES = 1152
 # HBM counters stale (the shared headers and the host side count for all)
 KERNEL_SOURCES = {
     "reloc_kernel": ["relocate.hip"],
+    "patch_dma_kernel": ["patch.hip"],
     "patch_kernel": ["patch.hip"],
     "mla_decode_kernel": ["decode.hip", "kvr_lds.h"],
     "gqa_decode_kernel": ["gqa_decode.hip", "kvr_lds.h"],
@@ -402,7 +403,7 @@ class GqaPatch:
     16 chunks x 1024 tokens, 32 layers, K and V of 8 x 128 bf16, delta ~
     U{-30000..30000}, RoPE base 500000, factors fp32 N(0, 0.01^2)."""
     name = "gqa_patch"
-    kernel = "patch_kernel<gather>"
+    kernel = "patch_dma_kernel<gather>"
 
     def __init__(self):
         import kvsynth
