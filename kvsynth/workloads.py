@@ -315,6 +315,61 @@ def gqa_rotate_on_read_decode(batch=32, ctx=32768, q_heads=32, kv_heads=8, head_
         shape=GQA(n_layers=1, heads=kv_heads, head_dim=head_dim), seed_keys=(cfg,))
 
 
+# ------------------------------------------------------ patch formation ---
+
+@dataclass
+class PatchFormationWorkload:
+    name: str
+    n: int                 # deficit matrices (layers x chunks x tensors)
+    rows: int              # tokens of a chunk
+    cols: int              # features
+    rank: int              # m
+    sketch: int            # columns of the random test matrix
+    orders: int            # deficits averaged per matrix (orbit patch); 1 = plain formation
+    energy_dirs: int
+    decay: float
+    noise: float
+    omega: np.ndarray      # float32 [cols, sketch], N(0, 1)
+    seed_keys: tuple = field(default_factory=tuple)
+
+
+def patch_formation(n_layers=32, n_chunks=16, tensors=2, rows=1024, cols=1024, rank=16, sketch=32, orders=1,
+                    energy_dirs=32, decay=2.0 ** -0.125, noise=1e-3, cfg=8):
+    """Deficits of the GQA patch shape (per layer, chunk and tensor a
+    [1024 tokens x 1024 features] matrix) with their energy in `energy_dirs`
+    feature directions (singular values ~ decay^i) plus dense noise; `orders`
+    deficits per matrix for the orbit patch.  The random test matrix of the
+    range finder is drawn here and passed in."""
+    r = rng(cfg, 0)
+    omega = r.standard_normal((cols, sketch), dtype=np.float32)
+    return PatchFormationWorkload(
+        name=f"patch_formation_n{n_layers * n_chunks * tensors}_{rows}x{cols}_m{rank}_p{orders}",
+        n=n_layers * n_chunks * tensors, rows=rows, cols=cols, rank=rank, sketch=sketch, orders=orders,
+        energy_dirs=energy_dirs, decay=decay, noise=noise, omega=omega, seed_keys=(cfg,))
+
+
+def deficit_batch_(out, energy_dirs, decay, noise, *keys):
+    """Fill a float32 device tensor [n, rows, cols] with seeded synthetic
+    deficits: (A / sqrt(rows)) diag(decay^i) (B / sqrt(cols))^T with Gaussian
+    A, B, plus N(0, noise^2 / cols) per entry.  The matrices are built in
+    slabs on the tensor's own device (input synthesis, not the method)."""
+    import torch
+    n, rows, cols = out.shape
+    s = torch.tensor([decay ** i for i in range(energy_dirs)], dtype=torch.float32, device=out.device)
+    slab = max(1, (1 << 28) // (rows * cols))
+    for i0 in range(0, n, slab):
+        i1 = min(n, i0 + slab)
+        a = torch.empty((i1 - i0, rows, energy_dirs), dtype=torch.float32, device=out.device)
+        b = torch.empty((i1 - i0, cols, energy_dirs), dtype=torch.float32, device=out.device)
+        fill_normal_(a, *keys, 1, i0)
+        fill_normal_(b, *keys, 2, i0)
+        a *= s / rows ** 0.5
+        b /= cols ** 0.5
+        fill_normal_(out[i0:i1], *keys, 3, i0, std=noise / cols ** 0.5)
+        out[i0:i1] += torch.matmul(a, b.transpose(1, 2).contiguous())
+    return out
+
+
 # ---------------------------------------------------------------- keying ---
 
 @dataclass

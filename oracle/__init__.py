@@ -41,10 +41,13 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
 * ``keying``    -- pinned: xxHash64 against the xxhash library and its published
                    empty-input value, the Gear recurrence against its window
                    sum, the cut rule by brute force, content alignment.
+* ``svd``       -- pinned: exact recovery of planted rank-m deficits,
+                   Eckart-Young, a pure-Python power iteration for the leading
+                   triplet, a transposed-factor mutant, the orbit mean.
 * FORGET mode   -- status and truncated length only; parity unpinned beyond that
                    (truly forgetting needs a model re-prefill).
 * patch frame   -- the patch is added after rotation, in the target frame, as the
                    reuse operator is written; parity unpinned beyond that formula.
 """
 
-from . import bf16, rope, splice, gather, patch, decode, lazy, keying, tolerance  # noqa: F401
+from . import bf16, rope, splice, gather, patch, decode, lazy, keying, svd, tolerance  # noqa: F401
