@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "patch_kernel": ["patch.hip"],
     "mla_decode_kernel": ["decode.hip", "kvr_lds.h"],
     "gqa_decode_kernel": ["gqa_decode.hip", "kvr_lds.h"],
+    "sketch_gemm_kernel": ["patch_form.hip"],
 }
 SHARED_SOURCES = ["kvr_device.h", "kvr_internal.h", "api.cpp"]
 
@@ -645,6 +646,76 @@ class GqaDecode:
                           f"which may use up to {thr} threads)"}
 
 
+class PatchForm:
+    """Kamera patch formation on the GQA patch shape: 32 layers x 16 chunks x
+    2 tensors = 1024 deficits of 1024 tokens x 1024 features (float32,
+    energy in 32 feature directions), rank-16 factors by the randomized range
+    finder (32-column sketch, two power steps: five passes over each
+    deficit).  With orders > 1 (the orbit patch) each deficit is the mean of
+    that many order-specific deficits.  A unit is one deficit factored."""
+    kernel = "sketch_gemm_kernel + orth + eig"
+    dtype = "f32"
+    unit = "deficits/s"
+    data = "synthetic (seeded deficits: Gaussian factors of 32 decaying directions plus dense noise)"
+
+    def __init__(self, orders=1):
+        import kvsynth
+        self.w = kvsynth.patch_formation(orders=orders)
+        w = self.w
+        self.name = "patch_formation" if orders == 1 else "orbit_patch"
+        per = w.rows * w.cols * 4
+        self.slots = w.n
+        # the mean of the orders (read them, write the mean), five sketch
+        # passes over each deficit, the 32-column sketches, the factors
+        mean = w.n * per * (w.orders + 1) if w.orders > 1 else 0
+        sk = w.n * (w.rows + w.cols) * w.sketch * 4
+        self.bytes = mean + 5 * w.n * per + 5 * sk + w.n * ((w.rows + w.cols) * w.rank + w.rank) * 4
+        self.flops = 5 * 2 * w.n * w.rows * w.cols * w.sketch
+        self.launches = 1
+        self.config = {"workload": "kamera_patch_formation" if orders == 1 else "kamera_orbit_patch",
+                       "deficits": w.n, "rows": w.rows, "cols": w.cols, "rank": w.rank, "sketch": w.sketch,
+                       "power_steps": 2, "orders": w.orders, "energy_dirs": w.energy_dirs,
+                       "deficits_per_step": w.n, "gflop": self.flops / 1e9}
+
+    def setup(self):
+        import torch
+        import kvsynth
+        import rope_rotation_splice_amd as rrs
+        w = self.w
+        shape = (w.n, w.orders, w.rows, w.cols) if w.orders > 1 else (w.n, w.rows, w.cols)
+        self.d = torch.empty(shape, dtype=torch.float32, device="cuda")
+        kvsynth.deficit_batch_(self.d, w.energy_dirs, w.decay, w.noise, *w.seed_keys, w.orders)
+        self.omega = torch.from_numpy(w.omega).cuda()
+        self.out = (torch.empty((w.n, w.rows, w.rank), dtype=torch.float32, device="cuda"),
+                    torch.empty((w.n, w.cols, w.rank), dtype=torch.float32, device="cuda"),
+                    torch.empty((w.n, w.rank), dtype=torch.float32, device="cuda"))
+        self.rrs = rrs
+
+    def step(self):
+        self.rrs.kamera_patch_factors(self.d, self.w.rank, self.omega, out=self.out)
+
+    def cpu_baseline(self, budget_s):
+        import torch
+        import kvsynth
+        from oracle import svd
+        w = self.w
+        done, spent = 0, 0.0
+        while spent < budget_s and done < w.n:
+            shape = (1, w.orders, w.rows, w.cols) if w.orders > 1 else (1, w.rows, w.cols)
+            d = torch.empty(shape, dtype=torch.float32)
+            kvsynth.deficit_batch_(d, w.energy_dirs, w.decay, w.noise, *w.seed_keys, 9, done)
+            x = d[0].double().numpy()
+            t0 = time.perf_counter()
+            svd.truncated_factors(svd.orbit_deficit(x) if w.orders > 1 else x, w.rank)
+            spent += time.perf_counter() - t0
+            done += 1
+        import os as _os
+        thr = int(_os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(_os.sched_getaffinity(0))
+        return {"value": done / spent, "unit": "deficits/s", "cores": thr, "kind": "oracle",
+                "sample": f"{done} deficits of {w.rows} x {w.cols} (float64 SVD through numpy's LAPACK, which may "
+                          f"use up to {thr} threads), generation excluded"}
+
+
 class Copy:
     """A plain device-to-device copy of the registry gather's byte volume
     (torch's copy kernel): the practical read+write ceiling, and the known-size
@@ -675,7 +746,7 @@ class Copy:
 WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "splice_lazy": SpliceLazy,
              "gqa_patch": GqaPatch, "keys": Keys,
              "decode": Decode, "decode_zero_delta": lambda: Decode(zero_delta=True), "gqa_decode": GqaDecode,
-             "copy": Copy}
+             "patch_form": PatchForm, "orbit_patch": lambda: PatchForm(orders=4), "copy": Copy}
 
 
 def main():
@@ -693,7 +764,7 @@ def main():
         return 2
 
     wl = WORKLOADS[args.workload]()
-    unit = "keys/s" if isinstance(wl, (Decode, GqaDecode)) else "slots/s"
+    unit = getattr(wl, "unit", "keys/s" if isinstance(wl, (Decode, GqaDecode)) else "slots/s")
     # the CPU oracle runs before the GPU is touched
     cpu = None if args.no_cpu_baseline else wl.cpu_baseline(args.cpu_budget)
 

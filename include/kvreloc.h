@@ -307,6 +307,32 @@ kvr_status gqa_decode_rotate_on_read(const void* q, int32_t batch, int32_t q_hea
                                      hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kamera_patch_factors -- Kamera's patch formation (section 2: the m
+ * leading SVD factors of the conditioning deficit
+ * Delta = KV(B|A) - KV(B|empty); section 3: the orbit patch, from the deficit
+ * averaged over the sampled orders of a cached set).  For every deficit b:
+ *   D_b = mean over the `orders` matrices of b (orders = 1: the matrix itself)
+ *   U_b [rows x rank] = U_m Sigma_m,  V_b [cols x rank] = V_m,  sigma_b [rank]
+ * so that U_b V_b^T is the best rank-m approximation of D_b: the factors the
+ * reuse operator adds (kvr_lowrank layout U[t][k], V[f][k]).  Computed by a
+ * randomized range finder with a 32-column sketch and two power steps in
+ * float32 (accurate when sigma_33 << sigma_m).
+ *   d_deficits : device float32 [n][orders][rows][cols], 16-byte aligned
+ *   d_omega    : device float32 [cols][32], the range finder's random test
+ *                matrix (caller-drawn, e.g. N(0,1))
+ *   rows, cols : multiples of 64 in 64..16384;  rank : 1..16
+ *   d_U, d_V, d_sigma : device float32 outputs as above
+ *   d_workspace: kvr_patch_factors_workspace_bytes() bytes, 256-byte aligned
+ * Errors: KVR_E_ARG (null or misaligned pointer, n < 0, orders < 1),
+ * KVR_E_UNSUPPORTED (shapes, rank), KVR_E_RANGE, KVR_E_WORKSPACE, KVR_E_HIP.
+ * ---------------------------------------------------------------------- */
+size_t kvr_patch_factors_workspace_bytes(int32_t n, int32_t orders, int32_t rows, int32_t cols);
+
+kvr_status kamera_patch_factors(const float* d_deficits, int32_t n, int32_t orders, int32_t rows, int32_t cols,
+                                int32_t rank, const float* d_omega, float* d_U, float* d_V, float* d_sigma,
+                                void* d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * leyline_splice_lazy -- a block-aligned AMORTIZE splice done as an edit of
  * the block table and of the per-block pending shifts; no KV byte moves.
  * (Leyline, sections 2.2-2.3: the downstream slots are re-indexed and owe

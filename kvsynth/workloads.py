@@ -349,14 +349,18 @@ def patch_formation(n_layers=32, n_chunks=16, tensors=2, rows=1024, cols=1024, r
 
 
 def deficit_batch_(out, energy_dirs, decay, noise, *keys):
-    """Fill a float32 device tensor [n, rows, cols] with seeded synthetic
-    deficits: (A / sqrt(rows)) diag(decay^i) (B / sqrt(cols))^T with Gaussian
-    A, B, plus N(0, noise^2 / cols) per entry.  The matrices are built in
-    slabs on the tensor's own device (input synthesis, not the method)."""
+    """Fill a float32 device tensor [n, rows, cols] -- or [n, orders, rows,
+    cols], the deficits of one chunk under several orders -- with seeded
+    synthetic deficits: (A / sqrt(rows)) diag(decay^i) (B / sqrt(cols))^T with
+    Gaussian A, B (shared by a matrix's orders: the same chunk keeps its
+    low-rank directions), plus N(0, noise^2 / cols) per entry (drawn per
+    order).  The matrices are built in slabs on the tensor's own device
+    (input synthesis, not the method)."""
     import torch
-    n, rows, cols = out.shape
+    o4 = out if out.dim() == 4 else out.unsqueeze(1)
+    n, orders, rows, cols = o4.shape
     s = torch.tensor([decay ** i for i in range(energy_dirs)], dtype=torch.float32, device=out.device)
-    slab = max(1, (1 << 28) // (rows * cols))
+    slab = max(1, (1 << 28) // (orders * rows * cols))
     for i0 in range(0, n, slab):
         i1 = min(n, i0 + slab)
         a = torch.empty((i1 - i0, rows, energy_dirs), dtype=torch.float32, device=out.device)
@@ -365,8 +369,8 @@ def deficit_batch_(out, energy_dirs, decay, noise, *keys):
         fill_normal_(b, *keys, 2, i0)
         a *= s / rows ** 0.5
         b /= cols ** 0.5
-        fill_normal_(out[i0:i1], *keys, 3, i0, std=noise / cols ** 0.5)
-        out[i0:i1] += torch.matmul(a, b.transpose(1, 2).contiguous())
+        fill_normal_(o4[i0:i1], *keys, 3, i0, std=noise / cols ** 0.5)
+        o4[i0:i1] += torch.matmul(a, b.transpose(1, 2).contiguous()).unsqueeze(1)
     return out
 
 

@@ -68,6 +68,9 @@ SIGNATURES = {
     "kvr_gqa_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32]),
     "gqa_decode_rotate_on_read": (c_i32, [c_vp, c_i32, c_i32, P(kvr_cache), c_i32, c_vp, c_vp, c_i32,
                                           c_vp, c_i32, c_f32, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "kvr_patch_factors_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32]),
+    "kamera_patch_factors": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_size,
+                                     c_vp]),
     "leyline_splice_lazy": (c_i32, [c_i32, c_vp, c_vp, c_i32, c_i32, P(c_i64), P(kvr_directive), c_vp, c_vp,
                                     P(c_i64), c_vp]),
     "kvr_keys_workspace_bytes": (c_size, [c_i64]),

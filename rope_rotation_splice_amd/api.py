@@ -332,6 +332,32 @@ def gqa_decode_rotate_on_read(q, cache, layer, block_tables, pending_delta, seq_
     return out, lse
 
 
+def kamera_patch_factors(deficits, rank, omega, out=None, workspace=None):
+    """Rank-m factors (U [n, rows, m] = U_m Sigma_m, V [n, cols, m], sigma
+    [n, m]) of float32 deficits [n, rows, cols], or of the orbit mean of
+    [n, orders, rows, cols]; omega: float32 [cols, 32] random test matrix."""
+    lib = _abi.load()
+    if deficits.dtype != torch.float32 or not deficits.is_contiguous() or deficits.dim() not in (3, 4):
+        raise ValueError("deficits must be a contiguous float32 [n, (orders,) rows, cols] tensor")
+    d4 = deficits if deficits.dim() == 4 else deficits.unsqueeze(1)
+    n, orders, rows, cols = (int(x) for x in d4.shape)
+    if omega.dtype != torch.float32 or not omega.is_contiguous() or tuple(omega.shape) != (cols, 32):
+        raise ValueError("omega must be a contiguous float32 [cols, 32] tensor")
+    dev = deficits.device
+    if out is None:
+        out = (torch.empty((n, rows, rank), dtype=torch.float32, device=dev),
+               torch.empty((n, cols, rank), dtype=torch.float32, device=dev),
+               torch.empty((n, rank), dtype=torch.float32, device=dev))
+    U, V, s = out
+    need = int(lib.kvr_patch_factors_workspace_bytes(n, orders, rows, cols))
+    ws = workspace if workspace is not None else _workspace(need, dev, "form")
+    st = lib.kamera_patch_factors(d4.data_ptr(), n, orders, rows, cols, int(rank), omega.data_ptr(), U.data_ptr(),
+                                  V.data_ptr(), s.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                  _stream_handle())
+    _check("kamera_patch_factors", st)
+    return U, V, s
+
+
 def device_errors():
     """Synchronize and return (then clear) the library's device error bits."""
     lib = _abi.load()

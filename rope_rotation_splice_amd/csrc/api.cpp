@@ -686,6 +686,62 @@ kvr_status gqa_decode_rotate_on_read(const void* q, int32_t batch, int32_t q_hea
     return e == hipSuccess ? KVR_OK : hip_fail(e);
 }
 
+size_t kvr_patch_factors_workspace_bytes(int32_t n, int32_t orders, int32_t rows, int32_t cols) {
+    if (n < 0 || orders < 1 || rows < 1 || cols < 1) return 0;
+    const size_t y = round_up((size_t)n * rows * kFormSketch * 4);
+    const size_t z = round_up((size_t)n * cols * kFormSketch * 4);
+    const size_t m = orders > 1 ? round_up((size_t)n * rows * cols * 4) : 0;
+    return std::max<size_t>(kAlign, y + z + m);
+}
+
+kvr_status kamera_patch_factors(const float* d_deficits, int32_t n, int32_t orders, int32_t rows, int32_t cols,
+                                int32_t rank, const float* d_omega, float* d_U, float* d_V, float* d_sigma,
+                                void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    if (n < 0 || orders < 1) return KVR_E_ARG;
+    if (rank < 1 || rank > kFormMaxRank) return KVR_E_UNSUPPORTED;
+    if (rows < 64 || cols < 64 || rows % 64 || cols % 64 || rows > 16384 || cols > 16384) return KVR_E_UNSUPPORTED;
+    if (n == 0) return KVR_OK;
+    if ((int64_t)n * (std::max(rows, cols) / 64) >= ((int64_t)1 << 31)) return KVR_E_RANGE;
+    if (!d_deficits || !d_omega || !d_U || !d_V || !d_sigma) return KVR_E_ARG;
+    if (!aligned16(d_deficits) || !aligned16(d_omega) || (reinterpret_cast<uintptr_t>(d_U) & 3u) ||
+        (reinterpret_cast<uintptr_t>(d_V) & 3u) || (reinterpret_cast<uintptr_t>(d_sigma) & 3u))
+        return KVR_E_ARG;
+    const size_t need = kvr_patch_factors_workspace_bytes(n, orders, rows, cols);
+    if (!d_ws || (reinterpret_cast<uintptr_t>(d_ws) % kAlign) || ws_bytes < need) return KVR_E_WORKSPACE;
+    float* Y = (float*)d_ws;
+    float* Z = (float*)((char*)d_ws + round_up((size_t)n * rows * kFormSketch * 4));
+    const float* D = d_deficits;
+    const int64_t per = (int64_t)rows * cols;
+    hipError_t e;
+    if (orders > 1) {
+        float* Dm = (float*)((char*)Z + round_up((size_t)n * cols * kFormSketch * 4));
+        e = launch_form_mean(d_deficits, orders, per, n, Dm, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        D = Dm;
+    }
+    FormGemmArgs g;
+    std::memset(&g, 0, sizeof(g));
+    g.D = D;
+    g.d_stride = per;
+    g.n = n;
+    g.rows = rows;
+    g.cols = cols;
+    // Y = D Omega; twice: Z = D^T Y, Z = orth(Z), Y = D Z
+    g.X = d_omega; g.x_stride = 0; g.Y = Y; g.y_stride = (int64_t)rows * kFormSketch;
+    if ((e = launch_form_gemm(g, false, stream)) != hipSuccess) return hip_fail(e);
+    for (int step = 0; step < 2; ++step) {
+        g.X = Y; g.x_stride = (int64_t)rows * kFormSketch; g.Y = Z; g.y_stride = (int64_t)cols * kFormSketch;
+        if ((e = launch_form_gemm(g, true, stream)) != hipSuccess) return hip_fail(e);
+        FormOrthArgs o{Z, cols};
+        if ((e = launch_form_orth(o, n, stream)) != hipSuccess) return hip_fail(e);
+        g.X = Z; g.x_stride = (int64_t)cols * kFormSketch; g.Y = Y; g.y_stride = (int64_t)rows * kFormSketch;
+        if ((e = launch_form_gemm(g, false, stream)) != hipSuccess) return hip_fail(e);
+    }
+    FormEigArgs ea{Y, Z, d_U, d_V, d_sigma, rows, cols, rank};
+    e = launch_form_eig(ea, n, stream);
+    return e == hipSuccess ? KVR_OK : hip_fail(e);
+}
+
 kvr_status leyline_splice_lazy(int32_t block_size, int32_t* d_block_tables, int32_t* d_pending_delta,
                                int32_t bt_stride, int32_t n_seq, const int64_t* seq_lens,
                                const kvr_directive* dirs, const int32_t* d_stub_blocks,

@@ -180,6 +180,8 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(const GqaDecodeArgs A) {
             const float f = (float)(u - rint(u));
             s_cs[lane] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
         }
+        // the other lanes' entries are read next: order them after the writes
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         // pair j = 32s + 8 c4 + e (s < 2) couples qraw[s][e] and qraw[s + 2][e]
 #pragma unroll
         for (int s = 0; s < 2; ++s) {

@@ -78,6 +78,14 @@ __device__ __forceinline__ void angle_table(float2* cs, const double* omega, int
     }
 }
 
+// Workgroups reach the 8 XCDs round-robin (workgroup b runs on XCD b % 8,
+// each with its own L2).  This remap gives each XCD a contiguous range of
+// logical workgroup ids, so neighbouring logical workgroups share an L2.
+__device__ __forceinline__ int xcd_contiguous(int b, int n) {
+    const int x = b & 7, k = b >> 3, q = n >> 3, r = n & 7;
+    return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
 // Relaxed device-scope atomics (coherent across the XCDs' L2 caches).
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

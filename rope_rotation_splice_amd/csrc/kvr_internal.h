@@ -143,6 +143,23 @@ struct GqaDecodeArgs {
     double omega[kGqaDim / 2];
 };
 
+// Patch formation (patch_form.hip).
+constexpr int kFormSketch = 32;       // columns of the range finder's sketch
+constexpr int kFormMaxRank = 16;
+
+struct FormGemmArgs {
+    const float* D; int64_t d_stride;          // deficits, [n][rows][cols], stride in floats
+    const float* X; int64_t x_stride;          // [n][K][32] (stride 0: one X for all)
+    float* Y; int64_t y_stride;                // [n][M][32]
+    int32_t n, rows, cols;
+};
+struct FormOrthArgs { float* Z; int32_t n; };  // [count][n][32], orthonormalized in place
+struct FormEigArgs {
+    const float* Y; const float* V;            // [count][rows][32], [count][cols][32]
+    float* Uout; float* Vout; float* sigma;    // [count][rows][m], [count][cols][m], [count][m]
+    int32_t rows, cols, rank;
+};
+
 // Block-table splice (lazy.hip): one workgroup per sequence.
 constexpr int kLazyMaxBlocks = 8192;  // table entries a workgroup stages in LDS
 constexpr int kLazyMaxSeq = 96;       // sequences per launch
@@ -201,6 +218,11 @@ uint32_t read_and_clear_errors_patch();
 // Decode (decode.hip): split kernel + combine kernel.
 hipError_t launch_decode(const DecodeArgs& a, uint16_t* out, float* lse, hipStream_t s);
 uint32_t read_and_clear_errors_decode();
+// Patch formation (patch_form.hip).
+hipError_t launch_form_gemm(const FormGemmArgs& a, bool trans, hipStream_t s);
+hipError_t launch_form_orth(const FormOrthArgs& a, int count, hipStream_t s);
+hipError_t launch_form_eig(const FormEigArgs& a, int count, hipStream_t s);
+hipError_t launch_form_mean(const float* d, int orders, int64_t per, int64_t n, float* out, hipStream_t s);
 // GQA decode (gqa_decode.hip): split kernel + combine kernel.
 hipError_t launch_gqa_decode(const GqaDecodeArgs& a, uint16_t* out, float* lse, hipStream_t s);
 uint32_t read_and_clear_errors_gqa_decode();

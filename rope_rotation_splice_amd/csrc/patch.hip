@@ -102,14 +102,8 @@ __device__ __forceinline__ void rot_patch(v4u& lo, v4u& hi, const float2* cs, bo
     }
 }
 
-// Workgroups reach the 8 XCDs round-robin (workgroup b runs on XCD b % 8,
-// each with its own L2).  Every tile of an (item, layer) re-reads that
-// layer's feature-side factors, so each XCD is given a contiguous range of
-// logical workgroups: the tiles of one (item, layer) then share one L2.
-__device__ __forceinline__ int xcd_contiguous(int b, int n) {
-    const int x = b & 7, k = b >> 3, q = n >> 3, r = n & 7;
-    return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
-}
+// Every tile of an (item, layer) re-reads that layer's factors: with
+// xcd_contiguous the tiles of one (item, layer) share one XCD's L2.
 
 template <bool INPLACE>
 __global__ __launch_bounds__(kThreads) void patch_kernel(const PatchArgs A) {
@@ -523,6 +517,8 @@ __global__ __launch_bounds__(kThreads) void patch_dma_kernel(const PatchArgs A) 
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi)
             *(lds_v4u_t*)(size_t)(buf + tok * 256 + 16 * ((uint32_t)(4 * gi + g) ^ (uint32_t)tok)) = x[gi];
+        // other lanes' results are read next: order the reads after the writes
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * i + (lane >> 4);

@@ -1,0 +1,390 @@
+// Kamera patch formation (section 2: the m leading factors of the deficit
+// Delta = KV(B|A) - KV(B|empty) from an SVD; section 3: one orbit patch,
+// formed from the deficit averaged over the sampled orders, serves every
+// order of a cached set).
+//
+// Randomized range finder with two power steps on Delta^T Delta (a
+// 32-column sketch Omega, m <= 16):
+//   Y = Delta Omega
+//   twice:  Z = Delta^T Y,  V = orth(Z),  Y = Delta V
+//   Y^T Y = W Lambda W^T (Jacobi),  order by decreasing eigenvalue
+//   V_m = V W_m,  U_m Sigma_m = Y W_m,  sigma = sqrt(Lambda_m)
+// so that U V^T is the best rank-m approximation of Delta up to the
+// sketch's error ((sigma_33 / sigma_m)^5 per power step pair) and float32
+// rounding.  Omega is drawn by the caller.
+//
+// Kernels:
+// * sketch_gemm_kernel<TRANS>: Y = Delta X (or Delta^T X) for every
+//   deficit, X with 32 columns.  One workgroup per (deficit, 64 output
+//   rows); the K dimension is walked in 64-wide chunks staged in LDS (the
+//   next chunk's loads in flight while the current one is multiplied), on
+//   v_mfma_f32_16x16x4f32 with a float4 per lane covering four K-steps.
+// * orth_kernel: shifted CholeskyQR3 of Z (cols x 32) in place -- Gram on
+//   the matrix cores, Cholesky and the triangular inverse in one wave, the
+//   update Z L^-T by rows; the first pass adds the shift
+//   11 (n k + k (k + 1)) u ||Z||_F^2 to the Gram diagonal, which keeps the
+//   Cholesky factorization defined for any conditioning, and columns whose
+//   pivot falls to 1e-8 of the largest are dropped (a deficit of rank below
+//   32 gives a sketch of lower rank: the basis then has zero columns).
+// * eig_kernel: Gram of Y, cyclic Jacobi in one wave (tournament ordering:
+//   16 disjoint rotations per round, 31 rounds per sweep), eigenvalues
+//   ordered, then the factors V W_m, Y W_m and sigma.
+// * mean_kernel: the orbit deficit, the mean of each matrix's orders.
+#include "kvr_device.h"
+#include "kvr_internal.h"
+
+#include "../../include/kvreloc.h"
+
+namespace kvr {
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kSk = kFormSketch;     // sketch columns
+constexpr int kTm = 64;              // output rows per workgroup
+constexpr int kTk = 64;              // K chunk
+constexpr int kPad = 68;             // LDS row length in floats (16-byte rows, banks spread)
+constexpr int kSweeps = 8;
+
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <bool TRANS>
+__global__ __launch_bounds__(256) void sketch_gemm_kernel(const FormGemmArgs A) {
+    __shared__ __attribute__((aligned(16))) float sA[2][kTm * kPad];
+    __shared__ __attribute__((aligned(16))) float sB[2][kSk * kPad];
+    const int M = TRANS ? A.cols : A.rows, K = TRANS ? A.rows : A.cols;
+    const int tiles = M / kTm;
+    const int bid = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int b = bid / tiles, m0 = (bid - b * tiles) * kTm;
+    const float* D = A.D + (int64_t)b * A.d_stride;
+    const float* X = A.X + (int64_t)b * A.x_stride;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int i = lane & 15, q = lane >> 4;
+
+    // chunk k0: 1024 float4 of Delta (4 per thread) and 512 of X (2 per thread)
+    v4f ra[4], rb[2];
+    auto gload = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = tid + 256 * u;
+            if (!TRANS) ra[u] = *reinterpret_cast<const v4f*>(D + (int64_t)(m0 + (e >> 4)) * A.cols + k0 + 4 * (e & 15));
+            else        ra[u] = *reinterpret_cast<const v4f*>(D + (int64_t)(k0 + (e >> 4)) * A.cols + m0 + 4 * (e & 15));
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = tid + 256 * u;
+            rb[u] = *reinterpret_cast<const v4f*>(X + (int64_t)(k0 + (e >> 3)) * kSk + 4 * (e & 7));
+        }
+    };
+    // LDS layouts: sA[m][k] (the A operand, output rows by K), sB[n][k]
+    auto lstore = [&](int buf) __attribute__((always_inline)) {
+        float* a = sA[buf];
+        float* bb = sB[buf];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = tid + 256 * u;
+            if (!TRANS) {
+                *reinterpret_cast<v4f*>(a + (e >> 4) * kPad + 4 * (e & 15)) = ra[u];
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) a[(4 * (e & 15) + c) * kPad + (e >> 4)] = ra[u][c];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = tid + 256 * u;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bb[(4 * (e & 7) + c) * kPad + (e >> 3)] = rb[u][c];
+        }
+    };
+
+    v4f acc0 = {0, 0, 0, 0}, acc1 = acc0;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    const int nk = K / kTk;
+    for (int c = 0; c < nk; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < nk) gload((c + 1) * kTk);
+        // MFMA kk of block kb: lane (i, q) supplies K index 16 kb + 4 q + kk
+        const float* a = sA[buf] + (16 * w + i) * kPad + 4 * q;
+        const float* b0 = sB[buf] + i * kPad + 4 * q;
+        const float* b1 = sB[buf] + (16 + i) * kPad + 4 * q;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const v4f av = *reinterpret_cast<const v4f*>(a + 16 * kb);
+            const v4f bv0 = *reinterpret_cast<const v4f*>(b0 + 16 * kb);
+            const v4f bv1 = *reinterpret_cast<const v4f*>(b1 + 16 * kb);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                acc0 = mfma4(av[kk], bv0[kk], acc0);
+                acc1 = mfma4(av[kk], bv1[kk], acc1);
+            }
+        }
+        if (c + 1 < nk) lstore(buf ^ 1);
+        __syncthreads();
+    }
+    // output row 4 q + r of this wave's 16, column i (+ 16)
+    float* Y = A.Y + (int64_t)b * A.y_stride + (int64_t)(m0 + 16 * w + 4 * q) * kSk + i;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        Y[r * kSk] = acc0[r];
+        Y[r * kSk + 16] = acc1[r];
+    }
+}
+
+// Gram G = Z^T Z of a [n x 32] matrix into sG (32 x 33): wave w computes the
+// 16 x 16 tile (w / 2, w % 2), K = n (unrolled: the loads of 8 K-blocks are
+// in flight together).
+__device__ __forceinline__ void gram32(const float* Z, int n, float (*sG)[33], int tid) {
+    const int lane = tid & 63, w = tid >> 6, i = lane & 15, q = lane >> 4;
+    const int ma = 16 * (w >> 1) + i, nb = 16 * (w & 1) + i;
+    v4f acc = {0, 0, 0, 0};
+#pragma unroll 8
+    for (int k0 = 0; k0 < n; k0 += 16) {
+        float a[4], b[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const float* row = Z + (int64_t)(k0 + 4 * q + kk) * kSk;
+            a[kk] = row[ma];
+            b[kk] = row[nb];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma4(a[kk], b[kk], acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sG[16 * (w >> 1) + 4 * q + r][16 * (w & 1) + i] = acc[r];
+}
+
+__global__ __launch_bounds__(256) void orth_kernel(const FormOrthArgs A) {
+    __shared__ float sG[32][33];
+    __shared__ float sLi[32][33];
+    const int tid = threadIdx.x, lane = tid & 63;
+    float* Z = A.Z + (int64_t)blockIdx.x * A.n * kSk;
+    for (int pass = 0; pass < 3; ++pass) {
+        gram32(Z, A.n, sG, tid);
+        __syncthreads();
+        if (tid < 64) {
+            // One wave works on the 32 x 32 matrices; lanes hand values to
+            // each other through LDS, so every phase ends with a
+            // wavefront-scope fence (a later read must see other lanes'
+            // earlier writes).
+            if (pass == 0) {
+                // shift 11 (n k + k (k + 1)) u tr(G), u = 2^-24, k = 32
+                float tr = 0.f;
+                for (int dd = 0; dd < 32; ++dd) tr += sG[dd][dd];
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                if (lane < 32) sG[lane][lane] += 11.f * (float)(A.n * 32 + 32 * 33) * 5.9604645e-8f * tr;
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            }
+            // Cholesky G = L L^T (lower triangle, in place); lane i owns row
+            // i.  A pivot -- the squared norm of column j orthogonal to the
+            // earlier columns -- at or below 1e-8 of the largest diagonal
+            // entry marks column j as dependent: it is dropped (its row of
+            // L^-1 is zero, so Z's column j becomes 0).
+            float dmax = 0.f;
+            for (int k = 0; k < 32; ++k) dmax = fmaxf(dmax, sG[k][k]);
+            const float tau = 1e-8f * dmax;
+            uint32_t dead = 0;
+            for (int j = 0; j < 32; ++j) {
+                const float piv = sG[j][j];
+                if (piv <= tau) {
+                    dead |= 1u << j;
+                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    if (lane == j) sG[j][j] = 1.f;
+                    if (lane > j && lane < 32) sG[lane][j] = 0.f;
+                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    continue;
+                }
+                const float dj = sqrtf(piv);
+                float lij = 0.f;
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                if (lane == j) sG[j][j] = dj;
+                if (lane > j && lane < 32) {
+                    lij = sG[lane][j] / dj;
+                    sG[lane][j] = lij;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                if (lane > j && lane < 32)
+                    for (int k = j + 1; k <= lane; ++k) sG[lane][k] -= lij * sG[k][j];
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            }
+            // L^-1 by forward substitution, lane c owns column c; rows of
+            // dropped columns are zero
+            if (lane < 32) {
+                float x[32];
+#pragma unroll
+                for (int r = 0; r < 32; ++r) {
+                    float s = r == lane ? 1.f : 0.f;
+                    for (int k = 0; k < r; ++k) s -= sG[r][k] * x[k];
+                    x[r] = (r < lane || ((dead >> r) & 1u)) ? 0.f : s / sG[r][r];
+                    sLi[r][lane] = x[r];
+                }
+            }
+        }
+        __syncthreads();
+        // Z <- Z L^-T: z'_j = sum_{c <= j} z_c Li[j][c]
+        for (int row = tid; row < A.n; row += 256) {
+            float z[32];
+            const v4f* zr = reinterpret_cast<const v4f*>(Z + (int64_t)row * kSk);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const v4f v = zr[u];
+                z[4 * u] = v[0]; z[4 * u + 1] = v[1]; z[4 * u + 2] = v[2]; z[4 * u + 3] = v[3];
+            }
+            v4f* zo = reinterpret_cast<v4f*>(Z + (int64_t)row * kSk);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                v4f o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * u + e;
+                    float s = 0.f;
+#pragma unroll
+                    for (int c = 0; c <= j; ++c) s += z[c] * sLi[j][c];
+                    o[e] = s;
+                }
+                zo[u] = o;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void eig_kernel(const FormEigArgs A) {
+    __shared__ float sG[32][33];
+    __shared__ float sW[32][33];
+    __shared__ float s_c[16], s_s[16];
+    __shared__ int s_idx[32];
+    __shared__ float s_lam[32];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int b = blockIdx.x;
+    const float* Y = A.Y + (int64_t)b * A.rows * kSk;
+    const float* V = A.V + (int64_t)b * A.cols * kSk;
+    gram32(Y, A.rows, sG, tid);
+    if (tid < 32 * 32) {
+        for (int e = tid; e < 32 * 32; e += 256) sW[e >> 5][e & 31] = (e >> 5) == (e & 31) ? 1.f : 0.f;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // One wave runs the Jacobi rotations; lanes hand values to each other
+        // through LDS, so every phase ends with a wavefront-scope fence.
+        // Cyclic Jacobi, tournament ordering: in round r, position 0 holds
+        // index 0 and position i >= 1 index ((i - 1 + r) mod 31) + 1; pair k
+        // joins positions k and 31 - k.
+        auto player = [](int pos, int r) { return pos == 0 ? 0 : ((pos - 1 + r) % 31) + 1; };
+        for (int sweep = 0; sweep < kSweeps; ++sweep) {
+            for (int r = 0; r < 31; ++r) {
+                if (lane < 16) {
+                    const int p = player(lane, r), qq = player(31 - lane, r);
+                    const float apq = sG[p][qq];
+                    float c = 1.f, s = 0.f;
+                    if (fabsf(apq) > 1e-30f) {
+                        const float th = (sG[qq][qq] - sG[p][p]) / (2.f * apq);
+                        const float t = fabsf(th) > 1e18f ? 0.5f / th
+                                                          : copysignf(1.f, th) / (fabsf(th) + sqrtf(th * th + 1.f));
+                        c = 1.f / sqrtf(t * t + 1.f);
+                        s = t * c;
+                    }
+                    s_c[lane] = c;
+                    s_s[lane] = s;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                // rows: G <- J^T G
+                for (int u = lane; u < 16 * 32; u += 64) {
+                    const int k = u >> 5, col = u & 31;
+                    const int p = player(k, r), qq = player(31 - k, r);
+                    const float c = s_c[k], s = s_s[k];
+                    const float x = sG[p][col], y = sG[qq][col];
+                    sG[p][col] = c * x - s * y;
+                    sG[qq][col] = s * x + c * y;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                // columns: G <- G J, W <- W J
+                for (int u = lane; u < 16 * 32; u += 64) {
+                    const int k = u >> 5, row = u & 31;
+                    const int p = player(k, r), qq = player(31 - k, r);
+                    const float c = s_c[k], s = s_s[k];
+                    float x = sG[row][p], y = sG[row][qq];
+                    sG[row][p] = c * x - s * y;
+                    sG[row][qq] = s * x + c * y;
+                    x = sW[row][p];
+                    y = sW[row][qq];
+                    sW[row][p] = c * x - s * y;
+                    sW[row][qq] = s * x + c * y;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            }
+        }
+        // order by decreasing eigenvalue (ties by index)
+        if (lane < 32) {
+            const float l = sG[lane][lane];
+            int pos = 0;
+            for (int j = 0; j < 32; ++j) {
+                const float o = sG[j][j];
+                pos += (o > l) || (o == l && j < lane);
+            }
+            s_idx[pos] = lane;
+            s_lam[pos] = l;
+        }
+    }
+    __syncthreads();
+    const int m = A.rank;
+    if (tid < m) A.sigma[(int64_t)b * m + tid] = sqrtf(fmaxf(s_lam[tid], 0.f));
+    // V_m = V W_m (cols x m), U_m Sigma_m = Y W_m (rows x m)
+    for (int e = tid; e < (A.cols + A.rows) * m; e += 256) {
+        const bool isv = e < A.cols * m;
+        const int e2 = isv ? e : e - A.cols * m;
+        const int row = e2 / m, j = e2 - row * m;
+        const float* src = (isv ? V + (int64_t)row * kSk : Y + (int64_t)row * kSk);
+        const int col = s_idx[j];
+        float s = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < 32; ++c) s += src[c] * sW[c][col];
+        if (isv) A.Vout[(int64_t)b * A.cols * m + e2] = s;
+        else     A.Uout[(int64_t)b * A.rows * m + e2] = s;
+    }
+}
+
+__global__ __launch_bounds__(256) void mean_kernel(const float* D, int orders, int64_t per, int64_t total4, float* out) {
+    const float inv = 1.f / (float)orders;
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total4; u += (int64_t)gridDim.x * 256) {
+        const int64_t b = u / (per / 4), off = u - b * (per / 4);
+        const v4f* src = reinterpret_cast<const v4f*>(D + b * orders * per) + off;
+        v4f s = src[0];
+        for (int p = 1; p < orders; ++p) s += src[(int64_t)p * (per / 4)];
+        reinterpret_cast<v4f*>(out)[u] = s * inv;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_form_gemm(const FormGemmArgs& a, bool trans, hipStream_t s) {
+    const int M = trans ? a.cols : a.rows;
+    const dim3 grid((unsigned)((int64_t)a.n * (M / kTm)));
+    if (trans) hipLaunchKernelGGL(sketch_gemm_kernel<true>, grid, dim3(256), 0, s, a);
+    else       hipLaunchKernelGGL(sketch_gemm_kernel<false>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_form_orth(const FormOrthArgs& a, int count, hipStream_t s) {
+    hipLaunchKernelGGL(orth_kernel, dim3((unsigned)count), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_form_eig(const FormEigArgs& a, int count, hipStream_t s) {
+    hipLaunchKernelGGL(eig_kernel, dim3((unsigned)count), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_form_mean(const float* d, int orders, int64_t per, int64_t n, float* out, hipStream_t s) {
+    const int64_t total4 = n * per / 4;
+    const unsigned grid = (unsigned)std::min<int64_t>((total4 + 255) / 256, 8192);
+    hipLaunchKernelGGL(mean_kernel, dim3(grid), dim3(256), 0, s, d, orders, per, total4, out);
+    return hipGetLastError();
+}
+
+}  // namespace kvr
