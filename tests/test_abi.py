@@ -196,3 +196,55 @@ def test_keys_validation_errors():
     lib = _abi.load()
     assert lib.kvr_keys_workspace_bytes(1500) == 256
     assert lib.kvr_keys_workspace_bytes(64 * 32 * 3) == 3 * 256
+
+
+def gqa_cache(n_layers=2, kv_heads=8, head_dim=128, block_size=64, n_blocks=16):
+    c = _abi.kvr_cache()
+    c.n_layers, c.block_size, c.n_blocks = n_layers, block_size, n_blocks
+    w = kv_heads * head_dim
+    c.pf_width, c.pf_dtype = w, _abi.KVR_BF16
+    c.rope_heads, c.rope_dim, c.rope_dtype, c.rope_base = kv_heads, head_dim, _abi.KVR_BF16, 500000.0
+    c.pf = _abi.kvr_part(FAKE, n_blocks * block_size * w, block_size * w, w)
+    c.rope = _abi.kvr_part(FAKE + (1 << 30), n_blocks * block_size * w, block_size * w, w)
+    return c
+
+
+def gqa_decode(c, batch=2, q_heads=32, layer=0, bt_stride=8, max_len=512, ws_bytes=1 << 24, q=FAKE, scale=0.1):
+    lib = _abi.load()
+    return lib.gqa_decode_rotate_on_read(q, batch, q_heads, ctypes.byref(c), layer, FAKE, FAKE, bt_stride, FAKE,
+                                         max_len, scale, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def test_gqa_decode_validation_errors():
+    lib = _abi.load()
+    assert gqa_decode(gqa_cache(), q_heads=30) == -7                 # not a multiple of the KV heads
+    assert gqa_decode(gqa_cache(), q_heads=8 * 17) == -7             # 17 query heads per KV head
+    assert gqa_decode(gqa_cache(head_dim=64)) == -7                  # head dimension other than 128
+    assert gqa_decode(gqa_cache(block_size=32)) == -7
+    assert gqa_decode(gqa_cache(), layer=2) == -2
+    assert gqa_decode(gqa_cache(), max_len=8 * 64 + 1) == -2         # beyond the table
+    assert gqa_decode(gqa_cache(), q=FAKE + 8) == -1                 # misaligned q
+    assert gqa_decode(gqa_cache(), scale=float("nan")) == -1
+    assert gqa_decode(gqa_cache(), ws_bytes=16) == -6
+    need = lib.kvr_gqa_decode_workspace_bytes(2, 32, 8, 512)
+    assert need > 0 and lib.kvr_gqa_decode_workspace_bytes(2, 30, 8, 512) == 0
+    assert gqa_decode(gqa_cache(), ws_bytes=need - 1) == -6
+
+
+def form(n=2, orders=1, rows=128, cols=192, rank=16, ws_bytes=1 << 30, d=FAKE, omega=FAKE):
+    lib = _abi.load()
+    return lib.kamera_patch_factors(d, n, orders, rows, cols, rank, omega, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def test_patch_factors_validation_errors():
+    lib = _abi.load()
+    assert form(rank=0) == -7 and form(rank=17) == -7
+    assert form(rows=100) == -7 and form(cols=32) == -7 and form(rows=16384 + 64) == -7
+    assert form(n=-1) == -1 and form(orders=0) == -1
+    assert form(d=None) == -1 and form(omega=FAKE + 4) == -1
+    assert form(ws_bytes=64) == -6
+    assert form(n=0) == 0                                            # nothing to do
+    need = lib.kvr_patch_factors_workspace_bytes(2, 1, 128, 192)
+    assert need == (2 * 128 * 32 * 4) + (2 * 192 * 32 * 4)
+    assert lib.kvr_patch_factors_workspace_bytes(2, 4, 128, 192) == need + 2 * 128 * 192 * 4
+    assert form(ws_bytes=need - 1) == -6
