@@ -26,9 +26,10 @@
 //   Cholesky factorization defined for any conditioning, and columns whose
 //   pivot falls to 1e-8 of the largest are dropped (a deficit of rank below
 //   32 gives a sketch of lower rank: the basis then has zero columns).
-// * eig_kernel: Gram of Y, cyclic Jacobi in one wave (tournament ordering:
-//   16 disjoint rotations per round, 31 rounds per sweep), eigenvalues
-//   ordered, then the factors V W_m, Y W_m and sigma.
+// * eig_kernel: Gram of Y, cyclic Jacobi (tournament ordering: 16 disjoint
+//   rotations per round, 31 rounds per sweep, each round's rotations applied
+//   by the whole workgroup), eigenvalues ordered, then the factors V W_m,
+//   Y W_m and sigma.
 // * mean_kernel: the orbit deficit, the mean of each matrix's orders.
 #include "kvr_device.h"
 #include "kvr_internal.h"
@@ -161,7 +162,7 @@ __device__ __forceinline__ void gram32(const float* Z, int n, float (*sG)[33], i
 
 __global__ __launch_bounds__(256) void orth_kernel(const FormOrthArgs A) {
     __shared__ float sG[32][33];
-    __shared__ float sLi[32][33];
+    __shared__ __attribute__((aligned(16))) float sLi[32][36];
     const int tid = threadIdx.x, lane = tid & 63;
     float* Z = A.Z + (int64_t)blockIdx.x * A.n * kSk;
     for (int pass = 0; pass < 3; ++pass) {
@@ -226,28 +227,43 @@ __global__ __launch_bounds__(256) void orth_kernel(const FormOrthArgs A) {
             }
         }
         __syncthreads();
-        // Z <- Z L^-T: z'_j = sum_{c <= j} z_c Li[j][c]
-        for (int row = tid; row < A.n; row += 256) {
-            float z[32];
-            const v4f* zr = reinterpret_cast<const v4f*>(Z + (int64_t)row * kSk);
+        // Z <- Z L^-T on the matrix cores: Z'[row][j] = sum_c Z[row][c] Li[j][c].
+        // Wave w takes 16-row tiles w, w + 4, ...; lane (i, q) supplies
+        // K index c = 16 kb + 4 q + kk.
+        {
+            const int w = tid >> 6, i = lane & 15, q = lane >> 4;
+            float bl[2][2][4];                   // [N tile][kb][kk]: Li[16 nt + i][16 kb + 4 q + kk]
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const v4f v = zr[u];
-                z[4 * u] = v[0]; z[4 * u + 1] = v[1]; z[4 * u + 2] = v[2]; z[4 * u + 3] = v[3];
-            }
-            v4f* zo = reinterpret_cast<v4f*>(Z + (int64_t)row * kSk);
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                v4f o;
+                for (int kb = 0; kb < 2; ++kb) {
+                    const v4f v = *reinterpret_cast<const v4f*>(&sLi[16 * nt + i][16 * kb + 4 * q]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * u + e;
-                    float s = 0.f;
-#pragma unroll
-                    for (int c = 0; c <= j; ++c) s += z[c] * sLi[j][c];
-                    o[e] = s;
+                    for (int kk = 0; kk < 4; ++kk) bl[nt][kb][kk] = v[kk];
                 }
-                zo[u] = o;
+            for (int m0 = 16 * w; m0 < A.n; m0 += 64) {
+                const v4f* zr = reinterpret_cast<const v4f*>(Z + (int64_t)(m0 + i) * kSk);
+                const v4f a0 = zr[q], a1 = zr[4 + q];
+                v4f c0 = {0, 0, 0, 0}, c1 = c0;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    c0 = mfma4(a0[kk], bl[0][0][kk], c0);
+                    c1 = mfma4(a0[kk], bl[1][0][kk], c1);
+                }
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    c0 = mfma4(a1[kk], bl[0][1][kk], c0);
+                    c1 = mfma4(a1[kk], bl[1][1][kk], c1);
+                }
+                // every lane of the wave has read the tile before it is overwritten
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                float* zo = Z + (int64_t)(m0 + 4 * q) * kSk + i;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    zo[r * kSk] = c0[r];
+                    zo[r * kSk + 16] = c1[r];
+                }
             }
         }
         __syncthreads();
@@ -269,67 +285,63 @@ __global__ __launch_bounds__(256) void eig_kernel(const FormEigArgs A) {
         for (int e = tid; e < 32 * 32; e += 256) sW[e >> 5][e & 31] = (e >> 5) == (e & 31) ? 1.f : 0.f;
     }
     __syncthreads();
-    if (tid < 64) {
-        // One wave runs the Jacobi rotations; lanes hand values to each other
-        // through LDS, so every phase ends with a wavefront-scope fence.
-        // Cyclic Jacobi, tournament ordering: in round r, position 0 holds
-        // index 0 and position i >= 1 index ((i - 1 + r) mod 31) + 1; pair k
-        // joins positions k and 31 - k.
-        auto player = [](int pos, int r) { return pos == 0 ? 0 : ((pos - 1 + r) % 31) + 1; };
-        for (int sweep = 0; sweep < kSweeps; ++sweep) {
-            for (int r = 0; r < 31; ++r) {
-                if (lane < 16) {
-                    const int p = player(lane, r), qq = player(31 - lane, r);
-                    const float apq = sG[p][qq];
-                    float c = 1.f, s = 0.f;
-                    if (fabsf(apq) > 1e-30f) {
-                        const float th = (sG[qq][qq] - sG[p][p]) / (2.f * apq);
-                        const float t = fabsf(th) > 1e18f ? 0.5f / th
-                                                          : copysignf(1.f, th) / (fabsf(th) + sqrtf(th * th + 1.f));
-                        c = 1.f / sqrtf(t * t + 1.f);
-                        s = t * c;
-                    }
-                    s_c[lane] = c;
-                    s_s[lane] = s;
+    // Cyclic Jacobi, tournament ordering: in round r, position 0 holds index
+    // 0 and position i >= 1 index ((i - 1 + r) mod 31) + 1; pair k joins
+    // positions k and 31 - k.  The 16 rotations of a round are disjoint; the
+    // workgroup applies them to the rows, then to the columns (and to W).
+    auto player = [](int pos, int r) { return pos == 0 ? 0 : ((pos - 1 + r) % 31) + 1; };
+    for (int sweep = 0; sweep < kSweeps; ++sweep) {
+        for (int r = 0; r < 31; ++r) {
+            if (tid < 16) {
+                const int p = player(tid, r), qq = player(31 - tid, r);
+                const float apq = sG[p][qq];
+                float c = 1.f, s = 0.f;
+                if (fabsf(apq) > 1e-30f) {
+                    const float th = (sG[qq][qq] - sG[p][p]) / (2.f * apq);
+                    const float t = fabsf(th) > 1e18f ? 0.5f / th
+                                                      : copysignf(1.f, th) / (fabsf(th) + sqrtf(th * th + 1.f));
+                    c = 1.f / sqrtf(t * t + 1.f);
+                    s = t * c;
                 }
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                // rows: G <- J^T G
-                for (int u = lane; u < 16 * 32; u += 64) {
-                    const int k = u >> 5, col = u & 31;
-                    const int p = player(k, r), qq = player(31 - k, r);
-                    const float c = s_c[k], s = s_s[k];
-                    const float x = sG[p][col], y = sG[qq][col];
-                    sG[p][col] = c * x - s * y;
-                    sG[qq][col] = s * x + c * y;
-                }
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                // columns: G <- G J, W <- W J
-                for (int u = lane; u < 16 * 32; u += 64) {
-                    const int k = u >> 5, row = u & 31;
-                    const int p = player(k, r), qq = player(31 - k, r);
-                    const float c = s_c[k], s = s_s[k];
-                    float x = sG[row][p], y = sG[row][qq];
-                    sG[row][p] = c * x - s * y;
-                    sG[row][qq] = s * x + c * y;
-                    x = sW[row][p];
-                    y = sW[row][qq];
-                    sW[row][p] = c * x - s * y;
-                    sW[row][qq] = s * x + c * y;
-                }
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                s_c[tid] = c;
+                s_s[tid] = s;
             }
-        }
-        // order by decreasing eigenvalue (ties by index)
-        if (lane < 32) {
-            const float l = sG[lane][lane];
-            int pos = 0;
-            for (int j = 0; j < 32; ++j) {
-                const float o = sG[j][j];
-                pos += (o > l) || (o == l && j < lane);
+            __syncthreads();
+            // rows: G <- J^T G
+            for (int u = tid; u < 16 * 32; u += 256) {
+                const int k = u >> 5, col = u & 31;
+                const int p = player(k, r), qq = player(31 - k, r);
+                const float c = s_c[k], s = s_s[k];
+                const float x = sG[p][col], y = sG[qq][col];
+                sG[p][col] = c * x - s * y;
+                sG[qq][col] = s * x + c * y;
             }
-            s_idx[pos] = lane;
-            s_lam[pos] = l;
+            __syncthreads();
+            // columns: G <- G J, W <- W J
+            for (int u = tid; u < 2 * 16 * 32; u += 256) {
+                const bool onw = u >= 16 * 32;
+                const int u2 = onw ? u - 16 * 32 : u;
+                const int k = u2 >> 5, row = u2 & 31;
+                const int p = player(k, r), qq = player(31 - k, r);
+                const float c = s_c[k], s = s_s[k];
+                float (*M)[33] = onw ? sW : sG;
+                const float x = M[row][p], y = M[row][qq];
+                M[row][p] = c * x - s * y;
+                M[row][qq] = s * x + c * y;
+            }
+            __syncthreads();
         }
+    }
+    // order by decreasing eigenvalue (ties by index)
+    if (tid < 32) {
+        const float l = sG[tid][tid];
+        int pos = 0;
+        for (int j = 0; j < 32; ++j) {
+            const float o = sG[j][j];
+            pos += (o > l) || (o == l && j < tid);
+        }
+        s_idx[pos] = tid;
+        s_lam[pos] = l;
     }
     __syncthreads();
     const int m = A.rank;
