@@ -186,24 +186,32 @@ void mla_decode_kernel(const DecodeArgs A) {
     constexpr bool kEven = (kStage % NW == 0) && ((kStage / 8) % NW == 0);
     const int nc = kEven ? kStage / NW : (kStage - wave + NW - 1) / NW;
     const int n_items = kEven ? kStage / NW + (kStage / 8) / NW : nc + (kStage / 8 - wave + NW - 1) / NW;
-    auto issue_item = [&](int jj, int k) __attribute__((always_inline)) {
+    // The source rows of stage jj are looked up once, before its loads are
+    // issued: the direct loads clobber memory as far as the compiler knows,
+    // so a table read between them would be repeated, and each repeat waits
+    // for every LDS read in flight.
+    struct StageSrc { const char* ck; const char* kr; };
+    auto stage_src = [&](int jj) __attribute__((always_inline)) -> StageSrc {
         const int j = min(jj, n_st - 1);
         const int id = max(0, __builtin_amdgcn_readfirstlane(s_blk[j >> 1]));
         const int64_t row0 = 32 * (j & 1);
+        return {A.ckv + (int64_t)id * A.ckv_b + row0 * A.ckv_r, A.kr + (int64_t)id * A.kr_b + row0 * A.kr_r};
+    };
+    auto issue_item = [&](int jj, const StageSrc& src, int k) __attribute__((always_inline)) {
         if (k < nc) {
             const int r = wave + NW * k;
-            dma16(A.ckv + (int64_t)id * A.ckv_b + (row0 + r) * A.ckv_r, 16u * (lane ^ swz(r)),
-                  lds0 + (jj & 3) * kCkvStageB + r * kCkvRow);
+            dma16(src.ck + r * A.ckv_r, 16u * (lane ^ swz(r)), lds0 + (jj & 3) * kCkvStageB + r * kCkvRow);
         } else {
             const int g = wave + NW * (k - nc);
             const int r = 8 * g + (lane >> 3);
-            dma16(A.kr + (int64_t)id * A.kr_b + (row0 + 8 * g) * A.kr_r,
+            dma16(src.kr + 8 * g * A.kr_r,
                   (uint32_t)(lane >> 3) * (uint32_t)A.kr_r + 16u * ((lane & 7) ^ swz_kr(r)),
                   lds0 + kKrOff + (jj & 3) * kKrStageB + g * 1024);
         }
     };
     auto issue_all = [&](int j) __attribute__((always_inline)) {
-        for (int k = 0; k < n_items; ++k) issue_item(j, k);
+        const StageSrc src = stage_src(j);
+        for (int k = 0; k < n_items; ++k) issue_item(j, src, k);
     };
     // rotate stage j's k_r in place: item e = (row e/8, 8-byte unit e%8 of
     // the lo half and its partner in the hi half)
@@ -310,17 +318,23 @@ void mla_decode_kernel(const DecodeArgs A) {
         auto kop = [&](int s) __attribute__((always_inline)) {
             return s < 32 ? lds16_at((krow ^ (32u * (s & 7))) + 256u * (s >> 3)) : lds16_at(rrow ^ (32u * (s - 32)));
         };
+        const StageSrc src3 = stage_src(j + 3);
         v16f sacc = v16f{};
         constexpr int kWin = 4;             // K-row reads in flight ahead of the MFMAs
         v4u kw[kWin];
 #pragma unroll
         for (int s = 0; s < kWin; ++s) kw[s] = kop(s);
+        __builtin_amdgcn_sched_group_barrier(0x100, kWin, 0);
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
             const v4u cur = kw[s % kWin];
             if (s + kWin < 36) kw[s % kWin] = kop(s + kWin);
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(cur), q[s], sacc, 0, 0, 0);
-            if (s % kSlot == 0 && s / kSlot < kItemsMax && (kEven || s / kSlot < n_items)) issue_item(j + 3, s / kSlot);
+            if (s % kSlot == 0 && s / kSlot < kItemsMax && (kEven || s / kSlot < n_items)) issue_item(j + 3, src3, s / kSlot);
+            // keep the window: each K-row read is issued before the MFMA
+            // that precedes its use by kWin steps
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (s + kWin < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
 
         v8bf pb[2];
@@ -348,12 +362,15 @@ void mla_decode_kernel(const DecodeArgs A) {
             v4s wa[4], wb[4];
 #pragma unroll
             for (int f = 0; f < 4; ++f) { wa[f] = tr(ra, f); wb[f] = tr(rb, f); }
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
             for (int f = 0; f < 16; ++f) {
                 const v4s ta = wa[f & 3], tb = wb[f & 3];
                 if (f + 4 < 16) { wa[f & 3] = tr(ra, f + 4); wb[f & 3] = tr(rb, f + 4); }
                 const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
                 acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[f], 0, 0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (f + 4 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
         }
     };
