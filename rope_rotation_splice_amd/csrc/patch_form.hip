@@ -20,16 +20,19 @@
 //   next chunk's loads in flight while the current one is multiplied), on
 //   v_mfma_f32_16x16x4f32 with a float4 per lane covering four K-steps.
 // * orth_kernel: shifted CholeskyQR3 of Z (cols x 32) in place -- Gram on
-//   the matrix cores, Cholesky and the triangular inverse in one wave, the
-//   update Z L^-T by rows; the first pass adds the shift
+//   the matrix cores, Cholesky and the triangular inverse in the registers
+//   of one wave (a row per lane, other rows' entries broadcast by readlane),
+//   the update Z L^-T on the matrix cores; the first pass adds the shift
 //   11 (n k + k (k + 1)) u ||Z||_F^2 to the Gram diagonal, which keeps the
 //   Cholesky factorization defined for any conditioning, and columns whose
 //   pivot falls to 1e-8 of the largest are dropped (a deficit of rank below
 //   32 gives a sketch of lower rank: the basis then has zero columns).
 // * eig_kernel: Gram of Y, cyclic Jacobi (tournament ordering: 16 disjoint
-//   rotations per round, 31 rounds per sweep, each round's rotations applied
-//   by the whole workgroup), eigenvalues ordered, then the factors V W_m,
-//   Y W_m and sigma.
+//   rotations per round, 31 rounds per sweep; each thread applies a round to
+//   one 2 x 2 block of the Gram matrix and to two entry pairs of W;
+//   negligible rotations are skipped and the sweeps stop once a whole sweep
+//   skips them all), eigenvalues ordered, then the factors V W_m and Y W_m
+//   on the matrix cores, and sigma.
 // * mean_kernel: the orbit deficit, the mean of each matrix's orders.
 #include "kvr_device.h"
 #include "kvr_internal.h"
@@ -47,6 +50,11 @@ constexpr int kTm = 64;              // output rows per workgroup
 constexpr int kTk = 64;              // K chunk
 constexpr int kPad = 68;             // LDS row length in floats (16-byte rows, banks spread)
 constexpr int kSweeps = 8;
+
+// value of v in lane l (l uniform)
+__device__ __forceinline__ float rl(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 
 __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -137,24 +145,23 @@ __global__ __launch_bounds__(256) void sketch_gemm_kernel(const FormGemmArgs A) 
     }
 }
 
-// Gram G = Z^T Z of a [n x 32] matrix into sG (32 x 33): wave w computes the
-// 16 x 16 tile (w / 2, w % 2), K = n (unrolled: the loads of 8 K-blocks are
-// in flight together).
+// Gram G = Z^T Z of a [n x 32] matrix (n a multiple of 64) into sG
+// (32 x 33): wave w computes the 16 x 16 tile (w / 2, w % 2); the loads of
+// 64 rows are in flight together.
 __device__ __forceinline__ void gram32(const float* Z, int n, float (*sG)[33], int tid) {
     const int lane = tid & 63, w = tid >> 6, i = lane & 15, q = lane >> 4;
     const int ma = 16 * (w >> 1) + i, nb = 16 * (w & 1) + i;
     v4f acc = {0, 0, 0, 0};
-#pragma unroll 8
-    for (int k0 = 0; k0 < n; k0 += 16) {
-        float a[4], b[4];
+    for (int k0 = 0; k0 < n; k0 += 64) {
+        float a[16], b[16];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const float* row = Z + (int64_t)(k0 + 4 * q + kk) * kSk;
-            a[kk] = row[ma];
-            b[kk] = row[nb];
+        for (int u = 0; u < 16; ++u) {
+            const float* row = Z + (int64_t)(k0 + 16 * (u >> 2) + 4 * q + (u & 3)) * kSk;
+            a[u] = row[ma];
+            b[u] = row[nb];
         }
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma4(a[kk], b[kk], acc);
+        for (int u = 0; u < 16; ++u) acc = mfma4(a[u], b[u], acc);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) sG[16 * (w >> 1) + 4 * q + r][16 * (w & 1) + i] = acc[r];
@@ -169,61 +176,64 @@ __global__ __launch_bounds__(256) void orth_kernel(const FormOrthArgs A) {
         gram32(Z, A.n, sG, tid);
         __syncthreads();
         if (tid < 64) {
-            // One wave works on the 32 x 32 matrices; lanes hand values to
-            // each other through LDS, so every phase ends with a
-            // wavefront-scope fence (a later read must see other lanes'
-            // earlier writes).
+            // One wave factors the 32 x 32 Gram matrix in registers: lane i
+            // (< 32) holds row i in g[], and the values a step needs from
+            // other rows are broadcast with readlane (lanes 32..63 mirror
+            // lanes 0..31 and store nothing).
+            const int ri = lane & 31;
+            float g[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k) g[k] = sG[ri][k];
             if (pass == 0) {
                 // shift 11 (n k + k (k + 1)) u tr(G), u = 2^-24, k = 32
                 float tr = 0.f;
-                for (int dd = 0; dd < 32; ++dd) tr += sG[dd][dd];
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                if (lane < 32) sG[lane][lane] += 11.f * (float)(A.n * 32 + 32 * 33) * 5.9604645e-8f * tr;
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+                for (int k = 0; k < 32; ++k) tr += rl(g[k], k);
+                const float sh = 11.f * (float)(A.n * 32 + 32 * 33) * 5.9604645e-8f * tr;
+#pragma unroll
+                for (int k = 0; k < 32; ++k)
+                    if (k == ri) g[k] += sh;
             }
-            // Cholesky G = L L^T (lower triangle, in place); lane i owns row
-            // i.  A pivot -- the squared norm of column j orthogonal to the
-            // earlier columns -- at or below 1e-8 of the largest diagonal
-            // entry marks column j as dependent: it is dropped (its row of
-            // L^-1 is zero, so Z's column j becomes 0).
+            // Cholesky G = L L^T, right-looking, lower triangle.  A pivot --
+            // the squared norm of column j orthogonal to the earlier columns
+            // -- at or below 1e-8 of the largest diagonal entry marks column
+            // j as dependent: it is dropped (its row of L^-1 is zero, so Z's
+            // column j becomes 0).
             float dmax = 0.f;
-            for (int k = 0; k < 32; ++k) dmax = fmaxf(dmax, sG[k][k]);
+#pragma unroll
+            for (int k = 0; k < 32; ++k) dmax = fmaxf(dmax, rl(g[k], k));
             const float tau = 1e-8f * dmax;
             uint32_t dead = 0;
+#pragma unroll
             for (int j = 0; j < 32; ++j) {
-                const float piv = sG[j][j];
+                const float piv = rl(g[j], j);
                 if (piv <= tau) {
                     dead |= 1u << j;
-                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                    if (lane == j) sG[j][j] = 1.f;
-                    if (lane > j && lane < 32) sG[lane][j] = 0.f;
-                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    g[j] = ri == j ? 1.f : (ri > j ? 0.f : g[j]);
                     continue;
                 }
                 const float dj = sqrtf(piv);
-                float lij = 0.f;
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                if (lane == j) sG[j][j] = dj;
-                if (lane > j && lane < 32) {
-                    lij = sG[lane][j] / dj;
-                    sG[lane][j] = lij;
-                }
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                if (lane > j && lane < 32)
-                    for (int k = j + 1; k <= lane; ++k) sG[lane][k] -= lij * sG[k][j];
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            }
-            // L^-1 by forward substitution, lane c owns column c; rows of
-            // dropped columns are zero
-            if (lane < 32) {
-                float x[32];
+                const float lij = g[j] / dj;
+                g[j] = ri == j ? dj : (ri > j ? lij : g[j]);
 #pragma unroll
-                for (int r = 0; r < 32; ++r) {
-                    float s = r == lane ? 1.f : 0.f;
-                    for (int k = 0; k < r; ++k) s -= sG[r][k] * x[k];
-                    x[r] = (r < lane || ((dead >> r) & 1u)) ? 0.f : s / sG[r][r];
-                    sLi[r][lane] = x[r];
+                for (int k = j + 1; k < 32; ++k) {
+                    const float lkj = rl(g[j], k);          // L[k][j]
+                    if (ri >= k) g[k] -= lij * lkj;
                 }
+            }
+            // L^-1 by forward substitution, lane c builds column c; rows of
+            // dropped columns are zero
+            float x[32];
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                float s = r == ri ? 1.f : 0.f;
+#pragma unroll
+                for (int k = 0; k < r; ++k) s -= rl(g[k], r) * x[k];      // L[r][k]
+                x[r] = (r < ri || ((dead >> r) & 1u)) ? 0.f : s / rl(g[r], r);
+            }
+            if (lane < 32) {
+#pragma unroll
+                for (int r = 0; r < 32; ++r) sLi[r][lane] = x[r];
             }
         }
         __syncthreads();
@@ -274,6 +284,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const FormEigArgs A) {
     __shared__ float sG[32][33];
     __shared__ float sW[32][33];
     __shared__ float s_c[16], s_s[16];
+    __shared__ int s_p[16], s_q[16];
     __shared__ int s_idx[32];
     __shared__ float s_lam[32];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -281,23 +292,28 @@ __global__ __launch_bounds__(256) void eig_kernel(const FormEigArgs A) {
     const float* Y = A.Y + (int64_t)b * A.rows * kSk;
     const float* V = A.V + (int64_t)b * A.cols * kSk;
     gram32(Y, A.rows, sG, tid);
-    if (tid < 32 * 32) {
-        for (int e = tid; e < 32 * 32; e += 256) sW[e >> 5][e & 31] = (e >> 5) == (e & 31) ? 1.f : 0.f;
-    }
+    for (int e = tid; e < 32 * 32; e += 256) sW[e >> 5][e & 31] = (e >> 5) == (e & 31) ? 1.f : 0.f;
     __syncthreads();
     // Cyclic Jacobi, tournament ordering: in round r, position 0 holds index
     // 0 and position i >= 1 index ((i - 1 + r) mod 31) + 1; pair k joins
-    // positions k and 31 - k.  The 16 rotations of a round are disjoint; the
-    // workgroup applies them to the rows, then to the columns (and to W).
-    auto player = [](int pos, int r) { return pos == 0 ? 0 : ((pos - 1 + r) % 31) + 1; };
+    // positions k and 31 - k.  The 16 rotations of a round are disjoint.
+    // Threads 0..15 form them; then thread t applies G <- J^T G J to the
+    // 2 x 2 block (pair t / 16 of rows, pair t % 16 of columns) and W <- W J
+    // to two (row, pair) items.  A rotation whose off-diagonal entry is at
+    // most 2^-24 sqrt(|app aqq|) is skipped, and the sweeps stop after one in
+    // which every rotation was skipped (the matrix is diagonal to working
+    // precision).
     for (int sweep = 0; sweep < kSweeps; ++sweep) {
+        int rotated = 0;
         for (int r = 0; r < 31; ++r) {
             if (tid < 16) {
-                const int p = player(tid, r), qq = player(31 - tid, r);
-                const float apq = sG[p][qq];
+                const int p = tid == 0 ? 0 : ((tid - 1 + r) % 31) + 1;
+                const int qq = ((30 - tid + r) % 31) + 1;
+                const float app = sG[p][p], aqq = sG[qq][qq], apq = sG[p][qq];
                 float c = 1.f, s = 0.f;
-                if (fabsf(apq) > 1e-30f) {
-                    const float th = (sG[qq][qq] - sG[p][p]) / (2.f * apq);
+                if (fabsf(apq) > 0x1p-24f * sqrtf(fabsf(app)) * sqrtf(fabsf(aqq))) {
+                    rotated = 1;
+                    const float th = (aqq - app) / (2.f * apq);
                     const float t = fabsf(th) > 1e18f ? 0.5f / th
                                                       : copysignf(1.f, th) / (fabsf(th) + sqrtf(th * th + 1.f));
                     c = 1.f / sqrtf(t * t + 1.f);
@@ -305,32 +321,35 @@ __global__ __launch_bounds__(256) void eig_kernel(const FormEigArgs A) {
                 }
                 s_c[tid] = c;
                 s_s[tid] = s;
+                s_p[tid] = p;
+                s_q[tid] = qq;
             }
             __syncthreads();
-            // rows: G <- J^T G
-            for (int u = tid; u < 16 * 32; u += 256) {
-                const int k = u >> 5, col = u & 31;
-                const int p = player(k, r), qq = player(31 - k, r);
-                const float c = s_c[k], s = s_s[k];
-                const float x = sG[p][col], y = sG[qq][col];
-                sG[p][col] = c * x - s * y;
-                sG[qq][col] = s * x + c * y;
-            }
-            __syncthreads();
-            // columns: G <- G J, W <- W J
-            for (int u = tid; u < 2 * 16 * 32; u += 256) {
-                const bool onw = u >= 16 * 32;
-                const int u2 = onw ? u - 16 * 32 : u;
-                const int k = u2 >> 5, row = u2 & 31;
-                const int p = player(k, r), qq = player(31 - k, r);
-                const float c = s_c[k], s = s_s[k];
-                float (*M)[33] = onw ? sW : sG;
-                const float x = M[row][p], y = M[row][qq];
-                M[row][p] = c * x - s * y;
-                M[row][qq] = s * x + c * y;
+            {
+                const int kr = tid >> 4, kc = tid & 15;
+                const int pr = s_p[kr], qr = s_q[kr], pc = s_p[kc], qc = s_q[kc];
+                const float cr = s_c[kr], sr = s_s[kr], cc = s_c[kc], sc = s_s[kc];
+                const float g00 = sG[pr][pc], g01 = sG[pr][qc], g10 = sG[qr][pc], g11 = sG[qr][qc];
+                const float h00 = cr * g00 - sr * g10, h01 = cr * g01 - sr * g11;
+                const float h10 = sr * g00 + cr * g10, h11 = sr * g01 + cr * g11;
+                sG[pr][pc] = cc * h00 - sc * h01;
+                sG[pr][qc] = sc * h00 + cc * h01;
+                sG[qr][pc] = cc * h10 - sc * h11;
+                sG[qr][qc] = sc * h10 + cc * h11;
+                const int row = tid >> 3;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int k = 2 * (tid & 7) + u;
+                    const int pk = s_p[k], qk = s_q[k];
+                    const float c = s_c[k], s = s_s[k];
+                    const float x = sW[row][pk], y = sW[row][qk];
+                    sW[row][pk] = c * x - s * y;
+                    sW[row][qk] = s * x + c * y;
+                }
             }
             __syncthreads();
         }
+        if (!__syncthreads_or(rotated)) break;
     }
     // order by decreasing eigenvalue (ties by index)
     if (tid < 32) {
@@ -346,18 +365,34 @@ __global__ __launch_bounds__(256) void eig_kernel(const FormEigArgs A) {
     __syncthreads();
     const int m = A.rank;
     if (tid < m) A.sigma[(int64_t)b * m + tid] = sqrtf(fmaxf(s_lam[tid], 0.f));
-    // V_m = V W_m (cols x m), U_m Sigma_m = Y W_m (rows x m)
-    for (int e = tid; e < (A.cols + A.rows) * m; e += 256) {
-        const bool isv = e < A.cols * m;
-        const int e2 = isv ? e : e - A.cols * m;
-        const int row = e2 / m, j = e2 - row * m;
-        const float* src = (isv ? V + (int64_t)row * kSk : Y + (int64_t)row * kSk);
-        const int col = s_idx[j];
-        float s = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < 32; ++c) s += src[c] * sW[c][col];
-        if (isv) A.Vout[(int64_t)b * A.cols * m + e2] = s;
-        else     A.Uout[(int64_t)b * A.rows * m + e2] = s;
+    // V_m = V W_m (cols x m) and U_m Sigma_m = Y W_m (rows x m) on the matrix
+    // cores, 16-row tiles spread over the waves: B[k][j] = W[k][idx_j] (zero
+    // for j >= m); lane (i, q) supplies K index 16 kb + 4 q + kk
+    {
+        const int w = tid >> 6, i = lane & 15, q = lane >> 4;
+        const int col = i < m ? s_idx[i] : 0;
+        float bw[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) bw[kb][kk] = i < m ? sW[16 * kb + 4 * q + kk][col] : 0.f;
+        const int tiles_v = A.cols / 16, tiles = tiles_v + A.rows / 16;
+        for (int t = w; t < tiles; t += 4) {
+            const bool isv = t < tiles_v;
+            const int m0 = 16 * (isv ? t : t - tiles_v);
+            const v4f* src = reinterpret_cast<const v4f*>((isv ? V : Y) + (int64_t)(m0 + i) * kSk);
+            const v4f a0 = src[q], a1 = src[4 + q];
+            v4f c = {0, 0, 0, 0};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) c = mfma4(a0[kk], bw[0][kk], c);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) c = mfma4(a1[kk], bw[1][kk], c);
+            float* out = isv ? A.Vout + (int64_t)b * A.cols * m : A.Uout + (int64_t)b * A.rows * m;
+            if (i < m) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[(int64_t)(m0 + 4 * q + r) * m + i] = c[r];
+            }
+        }
     }
 }
 
