@@ -16,9 +16,20 @@
 // Kernels:
 // * sketch_gemm_kernel<TRANS>: Y = Delta X (or Delta^T X) for every
 //   deficit, X with 32 columns.  One workgroup per (deficit, 64 output
-//   rows); the K dimension is walked in 64-wide chunks staged in LDS (the
-//   next chunk's loads in flight while the current one is multiplied), on
-//   v_mfma_f32_16x16x4f32 with a float4 per lane covering four K-steps.
+//   rows); K is walked in stages of 64 rows whose Delta block (16 KB) and X
+//   block (8 KB) go global -> LDS directly, kNs - 1 stages ahead, with one
+//   barrier per stage.  v_mfma_f32_16x16x4f32, wave w on output rows
+//   16 w .. 16 w + 15.  LDS layouts (16-byte chunks permuted so that every
+//   operand read touches each bank once):
+//     Delta, Y = Delta X: row m (256 bytes), chunk c at c ^ (m mod 16); lane
+//       (i, q) reads a float4 covering K = 16 kb + 4 q .. + 3.
+//     Delta, Z = Delta^T Y: K row t (256 bytes), chunk c at c ^ 4 (t mod 4);
+//       lane (i, q) reads one float at K = 4 ks + q.
+//     X: K row k (128 bytes) in slot row k ^ ((k >> 2) & 1) with chunk c at
+//       c ^ 4 ((k >> 3) & 1) (Y = Delta X), or in row k with chunk c at
+//       c ^ 4 ((k >> 1) & 1) (Z = Delta^T Y).
+//   The direct loads come from inline assembly with exact vmcnt waits, and
+//   the loop holds no other memory access the compiler would wait on.
 // * orth_kernel: shifted CholeskyQR3 of Z (cols x 32) in place -- Gram on
 //   the matrix cores, Cholesky and the triangular inverse in the registers
 //   of one wave (a row per lane, other rows' entries broadcast by readlane),
@@ -36,6 +47,7 @@
 // * mean_kernel: the orbit deficit, the mean of each matrix's orders.
 #include "kvr_device.h"
 #include "kvr_internal.h"
+#include "kvr_lds.h"
 
 #include "../../include/kvreloc.h"
 
@@ -43,12 +55,12 @@ namespace kvr {
 
 namespace {
 
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 constexpr int kSk = kFormSketch;     // sketch columns
 constexpr int kTm = 64;              // output rows per workgroup
-constexpr int kTk = 64;              // K chunk
-constexpr int kPad = 68;             // LDS row length in floats (16-byte rows, banks spread)
+constexpr int kTk = 64;              // K rows per stage
+constexpr int kNs = 3;               // stage buffers (loads run kNs - 1 stages ahead)
+constexpr int kDeltaB = kTm * kTk * 4;                // Delta block of a stage
+constexpr int kStageB = kDeltaB + kTk * kSk * 4;      // + X block
 constexpr int kSweeps = 8;
 
 // value of v in lane l (l uniform)
@@ -62,80 +74,105 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
 
 template <bool TRANS>
 __global__ __launch_bounds__(256) void sketch_gemm_kernel(const FormGemmArgs A) {
-    __shared__ __attribute__((aligned(16))) float sA[2][kTm * kPad];
-    __shared__ __attribute__((aligned(16))) float sB[2][kSk * kPad];
+    __shared__ __attribute__((aligned(1024))) char smem[kNs * kStageB];
+    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
     const int M = TRANS ? A.cols : A.rows, K = TRANS ? A.rows : A.cols;
     const int tiles = M / kTm;
     const int bid = xcd_contiguous(blockIdx.x, gridDim.x);
     const int b = bid / tiles, m0 = (bid - b * tiles) * kTm;
-    const float* D = A.D + (int64_t)b * A.d_stride;
-    const float* X = A.X + (int64_t)b * A.x_stride;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const char* D = reinterpret_cast<const char*>(A.D + (int64_t)b * A.d_stride);
+    const char* X = reinterpret_cast<const char*>(A.X + (int64_t)b * A.x_stride);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 15, q = lane >> 4;
+    const int nk = K / kTk;
 
-    // chunk k0: 1024 float4 of Delta (4 per thread) and 512 of X (2 per thread)
-    v4f ra[4], rb[2];
-    auto gload = [&](int k0) __attribute__((always_inline)) {
+    // Direct loads of stage s (K rows k0 = 64 s .. k0 + 63) into buffer s % kNs:
+    // 16 KB of Delta (16 loads of 1 KB) and 8 KB of X (8 loads); wave w
+    // issues Delta loads w, w + 4, w + 8, w + 12 and X loads w, w + 4.
+    // Stages past the end reload the last one into a buffer nobody reads
+    // again, so every stage issues the same loads.
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        const int k0 = kTk * min(s, nk - 1);
+        const uint32_t buf = lds0 + (uint32_t)(s % kNs) * kStageB;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = tid + 256 * u;
-            if (!TRANS) ra[u] = *reinterpret_cast<const v4f*>(D + (int64_t)(m0 + (e >> 4)) * A.cols + k0 + 4 * (e & 15));
-            else        ra[u] = *reinterpret_cast<const v4f*>(D + (int64_t)(k0 + (e >> 4)) * A.cols + m0 + 4 * (e & 15));
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int e = tid + 256 * u;
-            rb[u] = *reinterpret_cast<const v4f*>(X + (int64_t)(k0 + (e >> 3)) * kSk + 4 * (e & 7));
-        }
-    };
-    // LDS layouts: sA[m][k] (the A operand, output rows by K), sB[n][k]
-    auto lstore = [&](int buf) __attribute__((always_inline)) {
-        float* a = sA[buf];
-        float* bb = sB[buf];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = tid + 256 * u;
+        for (int v = 0; v < 4; ++v) {
+            const int u = w + 4 * v;
+            const int r = 4 * u + (lane >> 4), p = lane & 15;
             if (!TRANS) {
-                *reinterpret_cast<v4f*>(a + (e >> 4) * kPad + 4 * (e & 15)) = ra[u];
+                // row m0 + r, 16-byte chunk c of its 64 K-floats
+                const uint32_t c = (uint32_t)(p ^ (r & 15));
+                dma16(D + ((int64_t)m0 * A.cols + k0) * 4, (uint32_t)(r * A.cols) * 4u + 16u * c, buf + 1024u * u);
             } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) a[(4 * (e & 15) + c) * kPad + (e >> 4)] = ra[u][c];
+                // K row k0 + r, 16-byte chunk c of its 64 M-floats
+                const uint32_t c = (uint32_t)(p ^ (4 * (r & 3)));
+                dma16(D + ((int64_t)k0 * A.cols + m0) * 4, (uint32_t)(r * A.cols) * 4u + 16u * c, buf + 1024u * u);
             }
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int e = tid + 256 * u;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) bb[(4 * (e & 7) + c) * kPad + (e >> 3)] = rb[u][c];
+        for (int v = 0; v < 2; ++v) {
+            const int u = w + 4 * v;
+            const int ks = 8 * u + (lane >> 3), cs = lane & 7;       // LDS slot (row, chunk)
+            const int k = TRANS ? ks : ks ^ ((ks >> 2) & 1);
+            const int c = TRANS ? cs ^ (4 * ((ks >> 1) & 1)) : cs ^ (4 * ((k >> 3) & 1));
+            dma16(X + (int64_t)k0 * (kSk * 4), (uint32_t)(k * kSk + 4 * c) * 4u, buf + kDeltaB + 1024u * u);
         }
+    };
+    // LDS byte offsets of the operands (see the layouts above)
+    auto x_at = [&](uint32_t buf, int k, int n) __attribute__((always_inline)) -> uint32_t {
+        const int c = n >> 2;
+        const uint32_t slot = TRANS ? (uint32_t)(8 * k + (c ^ (4 * ((k >> 1) & 1))))
+                                    : (uint32_t)(8 * (k ^ ((k >> 2) & 1)) + (c ^ (4 * ((k >> 3) & 1))));
+        return buf + kDeltaB + 16u * slot + 4u * (n & 3);
     };
 
     v4f acc0 = {0, 0, 0, 0}, acc1 = acc0;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    const int nk = K / kTk;
-    for (int c = 0; c < nk; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < nk) gload((c + 1) * kTk);
-        // MFMA kk of block kb: lane (i, q) supplies K index 16 kb + 4 q + kk
-        const float* a = sA[buf] + (16 * w + i) * kPad + 4 * q;
-        const float* b0 = sB[buf] + i * kPad + 4 * q;
-        const float* b1 = sB[buf] + (16 + i) * kPad + 4 * q;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const v4f av = *reinterpret_cast<const v4f*>(a + 16 * kb);
-            const v4f bv0 = *reinterpret_cast<const v4f*>(b0 + 16 * kb);
-            const v4f bv1 = *reinterpret_cast<const v4f*>(b1 + 16 * kb);
+    for (int s = 0; s < kNs - 1; ++s) issue(s);
+    for (int j = 0; j < nk; ++j) {
+        wait_vmcnt<6 * (kNs - 2)>();        // stage j landed (this wave's part)
+        __syncthreads();                     // every wave's part; stage j - 1 consumed
+        issue(j + kNs - 1);
+        const uint32_t buf = lds0 + (uint32_t)(j % kNs) * kStageB;
+        // the stage's operands are read into registers first, then the 32
+        // MFMAs run back to back
+        typedef const __attribute__((address_space(3))) float* lds_f;
+        typedef const __attribute__((address_space(3))) v4f* lds_f4;
+        float av[16], b0[16], b1[16];
+        if (!TRANS) {
+            // lane (i, q) supplies K index 16 kb + 4 q + kk: a float4 of row 16 w + i
+            const uint32_t arow = buf + (uint32_t)(16 * w + i) * 256u;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                acc0 = mfma4(av[kk], bv0[kk], acc0);
-                acc1 = mfma4(av[kk], bv1[kk], acc1);
+            for (int kb = 0; kb < 4; ++kb) {
+                const v4f v = *(lds_f4)(size_t)(arow + 16u * (uint32_t)((4 * kb + q) ^ i));
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int k = 16 * kb + 4 * q + kk;
+                    av[4 * kb + kk] = v[kk];
+                    b0[4 * kb + kk] = *(lds_f)(size_t)x_at(buf, k, i);
+                    b1[4 * kb + kk] = *(lds_f)(size_t)x_at(buf, k, 16 + i);
+                }
+            }
+        } else {
+            // lane (i, q) supplies K index 4 ks + q: Delta[k0 + t][m0 + 16 w + i]
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks) {
+                const int t = 4 * ks + q;
+                const uint32_t ca = (uint32_t)((4 * w + (i >> 2)) ^ (4 * (t & 3)));
+                av[ks] = *(lds_f)(size_t)(buf + (uint32_t)t * 256u + 16u * ca + 4u * (i & 3));
+                b0[ks] = *(lds_f)(size_t)x_at(buf, t, i);
+                b1[ks] = *(lds_f)(size_t)x_at(buf, t, 16 + i);
             }
         }
-        if (c + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            acc0 = mfma4(av[u], b0[u], acc0);
+            acc1 = mfma4(av[u], b1[u], acc1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, TRANS ? 48 : 36, 0);    // every LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);                 // then the MFMAs
     }
+    wait_vmcnt<0>();                         // no direct load may land after the workgroup ends
     // output row 4 q + r of this wave's 16, column i (+ 16)
     float* Y = A.Y + (int64_t)b * A.y_stride + (int64_t)(m0 + 16 * w + 4 * q) * kSk + i;
 #pragma unroll
