@@ -33,7 +33,9 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
 * ``gather``    -- pinned: brute-force paged maps, O(n^2) overlap check.
 * ``patch``     -- pinned: textbook GEMM on asymmetric shapes; memory fractions.
 * ``lazy``      -- pinned: slot map equal to the eager splice's, block
-                   conservation, one-rotation composition.
+                   conservation, one-rotation composition; the block-table
+                   gather against each entry row's landing slot and owed shift,
+                   and against decoding the eagerly relocated rows.
 * ``decode``    -- pinned: textbook softmax attention on explicitly rotated keys,
                    needle retrieval, brute-force per-key loop on tiny inputs;
                    the GQA form against torch's scaled_dot_product_attention on
