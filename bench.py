@@ -348,6 +348,79 @@ class SpliceLazy:
                 "sample": f"{units} sequence table edits (the step's 64, repeated), numpy, one process"}
 
 
+class GatherLazy:
+    """The registry-gather draw placed by reference: 32 entries kept in pool
+    blocks (their lengths rounded down to whole 64-row blocks: rows past the
+    last whole block would take the eager gather) packed at block-aligned
+    targets in the draw's order.  Each step is one kv_relocate_gather_lazy
+    call: table and pending-shift edits, no KV byte moves.  Slots counted are
+    the entry rows placed per step."""
+    name = "lazy_gather"
+    kernel = "lazy_gather_kernel"
+    dtype = "int32"
+    data = "synthetic (the registry-gather draw of lengths, base positions and order; seeded block ids)"
+
+    def __init__(self):
+        import kvsynth
+        self.w = kvsynth.registry_gather()
+        w = self.w
+        B = w.block_size
+        nb = np.maximum(1, w.lens // B)
+        order = np.argsort(w.p_target, kind="stable")
+        tgt = np.zeros(len(nb), np.int64)
+        k = 0
+        for c in order:
+            tgt[c] = k * B
+            k += int(nb[c])
+        self.nb, self.tgt, self.bt_stride = nb, tgt, int(k)
+        self.slots = int((nb * B).sum())
+        # per block: old id read, new id and shift written, entry id read, replaced id written
+        self.bytes = int(20 * nb.sum())
+        self.launches = 1
+        self.config = {"workload": "irminsul_lazy_gather", "entries": len(nb), "block_size": B,
+                       "entry_len": "U{256..2048} rounded down to whole blocks", "base_pos": "U{0..60000}",
+                       "slots_per_step": self.slots, "kv_bytes_moved": 0}
+
+    def setup(self):
+        import torch
+        import rope_rotation_splice_amd as rrs
+        w, B = self.w, self.w.block_size
+        r = np.random.default_rng(77)
+        self.bt = torch.from_numpy(r.permutation(4 * self.bt_stride)[: self.bt_stride].astype(np.int32)
+                                   .reshape(1, -1)).cuda()
+        self.pend = torch.zeros_like(self.bt)
+        ids = torch.arange(4 * self.bt_stride, 5 * self.bt_stride, dtype=torch.int32, device="cuda")
+        self.ents, off = [], 0
+        for c in range(len(self.nb)):
+            n = int(self.nb[c])
+            self.ents.append(rrs.LazyEntry(0, ids[off:off + n], n * B, int(w.base_pos[c]), int(self.tgt[c])))
+            off += n
+        self.rrs = rrs
+
+    def step(self):
+        self.rrs.kv_relocate_gather_lazy(self.bt, self.pend, self.w.block_size, self.ents)
+
+    def cpu_baseline(self, budget_s):
+        from oracle import lazy as olazy
+        w, B = self.w, self.w.block_size
+        bt = np.arange(self.bt_stride)
+        pend = np.zeros(self.bt_stride, np.int64)
+        pl, off = [], 0
+        for c in range(len(self.nb)):
+            n = int(self.nb[c])
+            pl.append((np.arange(off, off + n), None, n * B, int(w.base_pos[c]), int(self.tgt[c])))
+            off += n
+        slots, spent, steps = 0, 0.0, 0
+        while spent < budget_s:
+            t0 = time.perf_counter()
+            olazy.lazy_gather_tables(bt, pend, B, pl)
+            spent += time.perf_counter() - t0
+            slots += self.slots
+            steps += 1
+        return {"value": slots / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
+                "sample": f"{steps} table edits of the step's {len(pl)} placements, numpy, one process"}
+
+
 class Keys:
     """Registry keying of 64 token streams x 32768 tokens (vocab 131072): Gear
     CDC (threshold 2^56, chunks 64..2048 tokens), xxHash64 per chunk and per
@@ -749,6 +822,7 @@ class Copy:
 
 
 WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "splice_lazy": SpliceLazy,
+             "gather_lazy": GatherLazy,
              "gqa_patch": GqaPatch, "keys": Keys,
              "decode": Decode, "decode_zero_delta": lambda: Decode(zero_delta=True), "gqa_decode": GqaDecode,
              "patch_form": PatchForm, "orbit_patch": lambda: PatchForm(orders=4), "copy": Copy}

@@ -377,6 +377,52 @@ kvr_status leyline_splice_lazy(int32_t block_size, int32_t* d_block_tables, int3
                                int32_t* d_freed_blocks, int64_t* new_lens, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kv_relocate_gather_lazy -- registry entries placed by reference.  A
+ * registry hit reuses a chunk's KV at a new position and owes
+ * R(p_target - p_source) (Irminsul, section 2.2); when the entry is kept in
+ * pool blocks from row 0 of its first block and p_target is a multiple of
+ * the block size, the placement is an edit of the destination's block table
+ * and per-block pending shifts, and mla_decode_rotate_on_read applies the
+ * shift on read (Irminsul, sections 2.2 and 4).  No KV byte moves.
+ *
+ * For entry e, B = block_size, nb = ceil(len / B), k < nb, slot =
+ * p_target / B + k in row `seq` of the tables:
+ *   d_replaced[off_e + k] = the old d_block_tables[seq][slot]   (off_e = the
+ *                           nb of the earlier entries, summed; skipped when
+ *                           d_replaced is NULL)
+ *   d_block_tables[seq][slot]  = d_blocks[k]
+ *   d_pending_delta[seq][slot] = (d_pend ? d_pend[k] : 0) + p_target - base_pos
+ * The entry's blocks are then shared by the registry and the sequence; the
+ * replaced ids pass to the caller.  Rows of a ragged last block past len
+ * are the entry block's own rows, so an entry whose len is not a multiple of
+ * B must be the last thing in its sequence up to that block's end.
+ *   block_size      : slots per block, > 0
+ *   d_block_tables,
+ *   d_pending_delta : device int32 [n_seq][bt_stride], edited in place
+ *   bt_stride       : 1 .. 8192 blocks; capacity = bt_stride * block_size
+ *   entries         : host [n]; d_blocks and d_pend are device int32 [nb]
+ *   d_replaced      : device int32 out [sum of nb], or NULL
+ * A pending shift that would leave the int32 range raises KVR_DEV_RANGE (see
+ * kvr_device_errors) and that slot keeps the entry block's own shift.
+ * Errors: KVR_E_ARG (null tables, entries or d_blocks where needed,
+ * block_size <= 0, bt_stride outside 1..8192, n < 0, seq outside
+ * 0..n_seq-1, p_target not a multiple of B), KVR_E_RANGE (len < 0,
+ * p_target < 0, p_target + len > capacity, |p_target - base_pos| >= 2^31),
+ * KVR_E_OVERLAP (two entries of one sequence covering one logical block),
+ * KVR_E_HIP.  Nothing is enqueued unless every entry validates.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t seq;                /* row of the block and shift tables */
+    const int32_t* d_blocks;    /* device int32 [nb]: pool blocks holding the entry, in order */
+    const int32_t* d_pend;      /* device int32 [nb]: shifts those blocks already owe, or NULL for 0 */
+    int64_t len, base_pos, p_target;
+} kvr_lazy_entry;
+
+kvr_status kv_relocate_gather_lazy(int32_t block_size, int32_t* d_block_tables, int32_t* d_pending_delta,
+                                   int32_t bt_stride, int32_t n_seq, const kvr_lazy_entry* entries, int32_t n,
+                                   int32_t* d_replaced, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * registry_chunk_keys -- registry keying of token streams (Irminsul, section
  * 2.2): content-defined chunks cut by a Gear rolling hash over 64-token
  * windows, each fingerprinted with xxHash64, plus the S1 fallback's fixed

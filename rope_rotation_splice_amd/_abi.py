@@ -46,6 +46,11 @@ class kvr_cdc_params(ctypes.Structure):
                 ("reserved", c_i32), ("seed", ctypes.c_uint64)]
 
 
+class kvr_lazy_entry(ctypes.Structure):
+    _fields_ = [("seq", c_i32), ("d_blocks", c_vp), ("d_pend", c_vp), ("len", c_i64), ("base_pos", c_i64),
+                ("p_target", c_i64)]
+
+
 P = ctypes.POINTER
 
 # name -> (restype, argtypes); the names and order follow include/kvreloc.h
@@ -73,6 +78,7 @@ SIGNATURES = {
                                      c_vp]),
     "leyline_splice_lazy": (c_i32, [c_i32, c_vp, c_vp, c_i32, c_i32, P(c_i64), P(kvr_directive), c_vp, c_vp,
                                     P(c_i64), c_vp]),
+    "kv_relocate_gather_lazy": (c_i32, [c_i32, c_vp, c_vp, c_i32, c_i32, P(kvr_lazy_entry), c_i32, c_vp, c_vp]),
     "kvr_keys_workspace_bytes": (c_size, [c_i64]),
     "registry_chunk_keys": (c_i32, [c_vp, P(c_i64), c_i32, c_vp, c_i32, P(kvr_cdc_params), c_vp, c_vp, c_i32, c_vp,
                                     c_vp, c_vp, c_vp, c_size, c_vp]),

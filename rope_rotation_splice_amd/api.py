@@ -204,6 +204,52 @@ def leyline_splice_lazy(block_tables, pending_delta, block_size, seq_lens, direc
     return np.array(out[:n], dtype=np.int64), freed[:n_free], st
 
 
+class LazyEntry:
+    """A registry entry kept in pool blocks (row 0 at the start of blocks[0]),
+    placed by reference at ``p_target`` of sequence ``seq``.  blocks: int32
+    device tensor [ceil(len / block_size)]; pend: the shifts those blocks
+    already owe (int32 device tensor of the same length) or None."""
+
+    def __init__(self, seq, blocks, length, base_pos, p_target, pend=None):
+        self.seq, self.blocks, self.len = int(seq), blocks, int(length)
+        self.base_pos, self.p_target, self.pend = int(base_pos), int(p_target), pend
+
+
+def kv_relocate_gather_lazy(block_tables, pending_delta, block_size, entries):
+    """Registry entries placed at block-aligned targets as edits of the block
+    table and of the per-block pending shifts (no KV bytes move); decode with
+    mla_decode_rotate_on_read applies the shift on read.
+
+    block_tables, pending_delta: int32 device tensors [n_seq, bt_stride],
+    edited in place.  Returns (replaced int32 device tensor: the ids each
+    entry's logical blocks held before, entry after entry; status).
+    """
+    lib = _abi.load()
+    for t in (block_tables, pending_delta):
+        if t.dtype != torch.int32 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("block_tables and pending_delta must be int32 [n_seq, blocks] with unit last stride")
+    if pending_delta.shape != block_tables.shape or pending_delta.stride(0) != block_tables.stride(0):
+        raise ValueError("pending_delta must match block_tables in shape and row stride")
+    n = len(entries)
+    arr = (_abi.kvr_lazy_entry * max(1, n))()
+    total = 0
+    for i, e in enumerate(entries):
+        nb = -(-e.len // int(block_size)) if e.len > 0 else 0
+        for t in (e.blocks, e.pend):
+            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < nb):
+                raise ValueError("entry blocks and pend must be contiguous int32 tensors of ceil(len / B) ids")
+        arr[i].seq, arr[i].len, arr[i].base_pos, arr[i].p_target = e.seq, e.len, e.base_pos, e.p_target
+        arr[i].d_blocks = e.blocks.data_ptr() if e.blocks is not None and e.blocks.numel() else None
+        arr[i].d_pend = e.pend.data_ptr() if e.pend is not None and e.pend.numel() else None
+        total += max(0, nb)
+    replaced = torch.empty(max(1, total), dtype=torch.int32, device=block_tables.device)
+    st = lib.kv_relocate_gather_lazy(int(block_size), block_tables.data_ptr(), pending_delta.data_ptr(),
+                                     int(block_tables.stride(0)), int(block_tables.shape[0]), arr, n,
+                                     replaced.data_ptr() if total else None, _stream_handle())
+    _check("kv_relocate_gather_lazy", st)
+    return replaced[:total], st
+
+
 def registry_chunk_keys(tokens, offsets, gear, threshold, min_len, max_len, s1_window, seed=0,
                         with_hash=False, with_s1=True):
     """Content-defined chunking of token streams with a Gear rolling hash and

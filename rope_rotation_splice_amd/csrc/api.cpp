@@ -818,6 +818,66 @@ kvr_status leyline_splice_lazy(int32_t block_size, int32_t* d_block_tables, int3
     return forget ? KVR_FORGET_NEEDS_PREFILL : KVR_OK;
 }
 
+kvr_status kv_relocate_gather_lazy(int32_t block_size, int32_t* d_block_tables, int32_t* d_pending_delta,
+                                   int32_t bt_stride, int32_t n_seq, const kvr_lazy_entry* entries, int32_t n,
+                                   int32_t* d_replaced, hipStream_t stream) {
+    if (block_size <= 0 || bt_stride <= 0 || bt_stride > kLazyMaxBlocks || n < 0 || n_seq < 0) return KVR_E_ARG;
+    if (n == 0) return KVR_OK;
+    if (!d_block_tables || !d_pending_delta || !entries) return KVR_E_ARG;
+    const int64_t B = block_size, cap = (int64_t)bt_stride * B;
+    // validate everything first: no table is touched unless all entries pass
+    std::vector<std::vector<std::pair<int64_t, int64_t>>> used(n_seq);   // block ranges per sequence
+    int64_t total = 0;
+    for (int32_t e = 0; e < n; ++e) {
+        const kvr_lazy_entry& E = entries[e];
+        if (E.seq < 0 || E.seq >= n_seq) return KVR_E_ARG;
+        if (E.len < 0 || E.p_target < 0 || E.p_target > cap - E.len) return KVR_E_RANGE;
+        if (E.p_target % B) return KVR_E_ARG;
+        // |p_target - base_pos| < 2^31 (p_target <= 2^44, so neither bound overflows)
+        if (E.base_pos <= E.p_target - ((int64_t)1 << 31) || E.base_pos >= E.p_target + ((int64_t)1 << 31))
+            return KVR_E_RANGE;
+        const int64_t nb = (E.len + B - 1) / B;
+        if (nb > 0 && !E.d_blocks) return KVR_E_ARG;
+        if (nb > 0) used[E.seq].push_back({E.p_target / B, E.p_target / B + nb});
+        total += nb;
+    }
+    for (auto& v : used) {
+        std::sort(v.begin(), v.end());
+        for (size_t i = 1; i < v.size(); ++i)
+            if (v[i].first < v[i - 1].second) return KVR_E_OVERLAP;   // non-empty, sorted by start
+    }
+    if (total >= ((int64_t)1 << 31)) return KVR_E_RANGE;
+
+    LazyGatherArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.bt = d_block_tables;
+    a.pend = d_pending_delta;
+    a.replaced = d_replaced;
+    a.bt_stride = bt_stride;
+    int32_t off = 0;
+    for (int32_t e = 0; e < n; ++e) {
+        const kvr_lazy_entry& E = entries[e];
+        const int32_t nb = (int32_t)((E.len + B - 1) / B);
+        if (nb > 0) {
+            LazyEntry& L = a.ents[a.n++];
+            L.blocks = E.d_blocks;
+            L.pend = E.d_pend;
+            L.row = E.seq;
+            L.slot0 = (int32_t)(E.p_target / B);
+            L.nb = nb;
+            L.delta = (int32_t)(E.p_target - E.base_pos);
+            L.rep_off = off;
+        }
+        off += nb;
+        if (a.n == kLazyMaxEntries || (e == n - 1 && a.n > 0)) {
+            hipError_t err = launch_lazy_gather(a, stream);
+            if (err != hipSuccess) return hip_fail(err);
+            a.n = 0;
+        }
+    }
+    return KVR_OK;
+}
+
 size_t kvr_keys_workspace_bytes(int64_t total_tokens) {
     if (total_tokens <= 0) return kAlign;
     return round_up((size_t)((total_tokens + 63) / 64) * 8);

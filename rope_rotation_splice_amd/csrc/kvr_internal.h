@@ -181,6 +181,25 @@ struct LazyArgs {
     LazySeq seqs[kLazyMaxSeq];
 };
 static_assert(sizeof(LazyArgs) <= 4000, "lazy splice arguments too large");
+
+// Block-table gather (lazy.hip): one workgroup per entry.
+constexpr int kLazyMaxEntries = 80;   // entries per launch
+struct LazyEntry {
+    const int32_t* blocks;            // the entry's pool blocks
+    const int32_t* pend;              // their own pending shifts, or null
+    int32_t row;                      // sequence (row of the tables)
+    int32_t slot0, nb;                // first logical block, block count
+    int32_t delta;                    // p_target - base_pos
+    int32_t rep_off;                  // offset into the replaced-id list
+};
+struct LazyGatherArgs {
+    int32_t* bt;
+    int32_t* pend;
+    int32_t* replaced;                // or null
+    int32_t bt_stride, n;
+    LazyEntry ents[kLazyMaxEntries];
+};
+static_assert(sizeof(LazyGatherArgs) <= 4000, "lazy gather arguments too large");
 static_assert(sizeof(GqaDecodeArgs) <= 4000, "GQA decode arguments too large");
 
 // Registry keying (keying.hip).
@@ -228,6 +247,7 @@ hipError_t launch_gqa_decode(const GqaDecodeArgs& a, uint16_t* out, float* lse, 
 uint32_t read_and_clear_errors_gqa_decode();
 // Block-table splice (lazy.hip).
 hipError_t launch_lazy(const LazyArgs& a, hipStream_t s);
+hipError_t launch_lazy_gather(const LazyGatherArgs& a, hipStream_t s);
 uint32_t read_and_clear_errors_lazy();
 // Registry keying (keying.hip): Gear hashes and candidates, cuts, fingerprints.
 hipError_t launch_keys(const KeyArgs& a, hipStream_t s);

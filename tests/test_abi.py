@@ -26,7 +26,7 @@ def test_header_functions_exported():
     lib = _abi.load()
     names = declared_functions()
     assert {"leyline_splice", "kv_relocate_gather", "kv_patch_lowrank", "mla_decode_rotate_on_read",
-            "leyline_splice_lazy", "registry_chunk_keys"} <= set(names)
+            "leyline_splice_lazy", "kv_relocate_gather_lazy", "registry_chunk_keys"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_abi.SIGNATURES), "binding and header disagree"
@@ -160,6 +160,44 @@ def lazy(dirs, lens, B=64, bt_stride=512, stubs=FAKE, freed=FAKE):
 def test_lazy_validation_errors(d, n, kw, code):
     st, _ = lazy([d], [n], **kw)
     assert st == code
+
+
+def lazy_gather(ents, B=64, bt_stride=64, n_seq=4, tables=FAKE):
+    """ents: (seq, len, base_pos, p_target[, blocks])"""
+    lib = _abi.load()
+    n = len(ents)
+    arr = (_abi.kvr_lazy_entry * max(1, n))()
+    for i, e in enumerate(ents):
+        arr[i].seq, arr[i].len, arr[i].base_pos, arr[i].p_target = e[0], e[1], e[2], e[3]
+        arr[i].d_blocks = e[4] if len(e) > 4 else FAKE
+        arr[i].d_pend = None
+    return lib.kv_relocate_gather_lazy(B, tables, tables, bt_stride, n_seq, arr, n, FAKE, None)
+
+
+@pytest.mark.parametrize("ents, kw, code", [
+    ([(0, 100, 0, 65)], {}, -1),                              # target off the block grid
+    ([(4, 100, 0, 64)], {}, -1),                              # sequence outside the tables
+    ([(-1, 100, 0, 64)], {}, -1),
+    ([(0, 100, 0, 64, None)], {}, -1),                        # blocks needed
+    ([(0, 100, 0, 64)], {"B": 0}, -1),
+    ([(0, 100, 0, 64)], {"bt_stride": 8193}, -1),
+    ([(0, 100, 0, 64)], {"tables": None}, -1),
+    ([(0, -1, 0, 64)], {}, -2),                               # negative length
+    ([(0, 100, 0, -64)], {}, -2),                             # negative target
+    ([(0, 100, 0, 64 * 63)], {}, -2),                         # past the table (64 blocks of 64)
+    ([(0, 100, 1 << 31, 0)], {}, -2),                         # shift does not fit 32 bits
+    ([(0, 100, -(1 << 31), 0)], {}, -2),
+    ([(0, 100, 0, 0), (0, 10, 5, 64)], {}, -4),               # both cover logical block 1
+    ([(1, 129, 0, 128), (1, 64, 0, 0), (1, 64, 0, 192)], {}, -4),
+])
+def test_lazy_gather_validation_errors(ents, kw, code):
+    assert lazy_gather(ents, **kw) == code
+
+
+def test_lazy_gather_accepts_without_launch():
+    # nothing to do: no entries, or only empty ones, and distinct sequences sharing block numbers
+    assert lazy_gather([]) == 0
+    assert lazy_gather([(0, 0, 5, 64, None), (1, 0, 7, 64, None)]) == 0
 
 
 def test_lazy_forget_and_empty_need_no_launch():

@@ -1,7 +1,7 @@
-"""Parity of leyline_splice_lazy (HIP, through the C ABI): the edited block
-tables and pending shifts are compared integer for integer with the oracle,
-and a rotate-on-read decode over the lazily spliced cache with the fp64
-oracle on the composed keys."""
+"""Parity of leyline_splice_lazy and kv_relocate_gather_lazy (HIP, through
+the C ABI): the edited block tables and pending shifts are compared integer
+for integer with the oracle, and a rotate-on-read decode over the lazily
+spliced or gathered cache with the fp64 oracle on the composed keys."""
 
 import math
 
@@ -149,3 +149,124 @@ def test_lazy_splice_then_decode_composes():
         assert (bt_d.cpu().numpy() == bt2).all() and (pd_d.cpu().numpy() == pd2).all()
         lens = [int(x) for x in new_lens]
         _decode_check(pool_h, pool_d, bt_d, pd_d, lens, qn, qr, scale)
+
+
+# ---- kv_relocate_gather_lazy ------------------------------------------------
+
+def _lazy_gather_case(B, bt_stride, n_seq, keys):
+    """Tables for n_seq sequences and entries kept in spare pool blocks, placed
+    at distinct block-aligned targets (ragged lengths only where the entry
+    ends its sequence's content), half of them with their own shifts."""
+    r = kvsynth.rng(22, *keys)
+    n_blocks = n_seq * bt_stride + 16 * bt_stride
+    perm = r.permutation(n_blocks).astype(np.int32)
+    bt = perm[: n_seq * bt_stride].reshape(n_seq, bt_stride).copy()
+    pend = r.integers(-100000, 100000, size=(n_seq, bt_stride), endpoint=True).astype(np.int32)
+    spare = list(perm[n_seq * bt_stride:])
+    ents = []
+    for s in range(n_seq):
+        k = 0
+        while True:
+            k += int(r.integers(0, 4))
+            nb = int(r.integers(1, 6))
+            if k + nb > bt_stride:
+                break
+            last = k + nb + 4 > bt_stride
+            length = nb * B - (int(r.integers(1, B)) if last and B > 1 else 0)
+            blocks = np.array([spare.pop() for _ in range(nb)], np.int32)
+            own = r.integers(-50000, 50000, size=nb).astype(np.int32) if r.integers(0, 2) else None
+            ents.append((s, blocks, own, length, int(r.integers(0, 200000)), k * B))
+            k += nb
+            if last:
+                break
+    return bt, pend, ents, n_blocks
+
+
+def _run_lazy_gather(bt_d, pd_d, B, ents):
+    import torch
+    import rope_rotation_splice_amd as rrs
+    objs = [rrs.LazyEntry(s, torch.from_numpy(bl).cuda(), ln, base, p,
+                          None if own is None else torch.from_numpy(own).cuda())
+            for s, bl, own, ln, base, p in ents]
+    replaced, st = rrs.kv_relocate_gather_lazy(bt_d, pd_d, B, objs)
+    torch.cuda.synchronize()
+    assert rrs.device_errors() == 0
+    return replaced.cpu().numpy(), st
+
+
+def _lazy_gather_oracle(bt, pend, B, ents):
+    bt2, pd2, rep = bt.astype(np.int64).copy(), pend.astype(np.int64).copy(), []
+    for s in range(bt.shape[0]):
+        mine = [(bl, own, ln, base, p) for (q, bl, own, ln, base, p) in ents if q == s]
+        bt2[s], pd2[s], _ = olazy.lazy_gather_tables(bt[s], pend[s], B, mine)
+    for s, bl, own, ln, base, p in ents:                 # replaced ids in entry order
+        rep += list(bt[s][p // B: p // B + len(bl)])
+    return bt2, pd2, np.array(rep, np.int64)
+
+
+@pytest.mark.parametrize("B", [1, 16, 64])
+def test_lazy_gather_tables_bit_exact(B):
+    import torch
+    bt, pend, ents, _ = _lazy_gather_case(B, 48, 5, keys=(B,))
+    assert len(ents) > 10
+    bt_d, pd_d = torch.from_numpy(bt.copy()).cuda(), torch.from_numpy(pend.copy()).cuda()
+    rep, st = _run_lazy_gather(bt_d, pd_d, B, ents)
+    bt2, pd2, rep2 = _lazy_gather_oracle(bt, pend, B, ents)
+    assert st == 0
+    assert (bt_d.cpu().numpy() == bt2).all() and (pd_d.cpu().numpy() == pd2).all()
+    assert list(rep) == list(rep2)
+
+
+def test_lazy_gather_many_entries_span_launches():
+    """More entries than one launch carries (80), across 3 sequences."""
+    import torch
+    B, bt_stride = 4, 400
+    r = kvsynth.rng(22, 9)
+    bt = r.permutation(3 * bt_stride).astype(np.int32).reshape(3, bt_stride)
+    pend = np.zeros_like(bt)
+    ents, nxt = [], 10000
+    for s in range(3):
+        for k in range(0, bt_stride - 2, 3):
+            ents.append((s, np.array([nxt, nxt + 1], np.int32), None, 2 * B, k * B + 7 * s, k * B))
+            nxt += 2
+    bt_d, pd_d = torch.from_numpy(bt.copy()).cuda(), torch.from_numpy(pend.copy()).cuda()
+    rep, st = _run_lazy_gather(bt_d, pd_d, B, ents)
+    bt2, pd2, rep2 = _lazy_gather_oracle(bt, pend, B, ents)
+    assert len(ents) > 200 and st == 0
+    assert (bt_d.cpu().numpy() == bt2).all() and (pd_d.cpu().numpy() == pd2).all()
+    assert list(rep) == list(rep2)
+
+
+def test_lazy_gather_shift_overflow_flagged():
+    import torch
+    import rope_rotation_splice_amd as rrs
+    B = 64
+    bt_d = torch.arange(8, dtype=torch.int32).reshape(1, 8).cuda()
+    pd_d = torch.zeros((1, 8), dtype=torch.int32).cuda()
+    own = torch.full((2,), 2 ** 31 - 10, dtype=torch.int32).cuda()
+    blocks = torch.tensor([70, 71], dtype=torch.int32).cuda()
+    rrs.kv_relocate_gather_lazy(bt_d, pd_d, B, [rrs.LazyEntry(0, blocks, 2 * B, 0, 3 * B, own)])   # +192 overflows
+    torch.cuda.synchronize()
+    assert rrs.device_errors() & 8
+    assert (pd_d.cpu().numpy()[0, 3:5] == 2 ** 31 - 10).all()
+    assert (bt_d.cpu().numpy()[0, 3:5] == [70, 71]).all()
+
+
+def test_lazy_gather_then_decode():
+    """Registry entries placed by reference, then a rotate-on-read decode over
+    the shared blocks checked against the fp64 oracle: the keys are attended
+    at R(own shift + p_target - base_pos), applied once, on read."""
+    import torch
+    B, bt_stride, heads = 64, 48, 128
+    bt, pend, ents, n_blocks = _lazy_gather_case(B, bt_stride, 3, keys=(5,))
+    r = kvsynth.rng(22, 6)
+    pool_h = kvsynth.bf16_normal(r, (n_blocks * 64, 576))
+    qn_h = kvsynth.bf16_normal(r, (3, heads, 512))
+    qr_h = kvsynth.bf16_normal(r, (3, heads, 64))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    pool_d = dev(pool_h).reshape(1, n_blocks, 64, 576)
+    bt_d, pd_d = torch.from_numpy(bt.copy()).cuda(), torch.from_numpy(pend.copy()).cuda()
+    _run_lazy_gather(bt_d, pd_d, B, ents)
+    # each sequence ends where its last entry ends (a ragged entry comes last)
+    lens = [max([p + ln for (q, bl, own, ln, base, p) in ents if q == s] + [B]) for s in range(3)]
+    _decode_check(pool_h, pool_d, bt_d, pd_d, lens, (qn_h, dev(qn_h)), (qr_h, dev(qr_h)), 1.0 / math.sqrt(576.0))
