@@ -63,7 +63,7 @@ def _oracle(host, b, scale, pend=None):
     return o, lse, odec.score_bound(qr, kr, d, scale, TH)
 
 
-@pytest.mark.parametrize("heads", [32, 64, 128])
+@pytest.mark.parametrize("heads", [32, 64, 96, 128])
 def test_decode_small(heads):
     lens = [64, 100, 1000, 2048 + 17]
     host, devs = _setup(4, heads, lens, bt_stride=40, keys=(1, heads))
