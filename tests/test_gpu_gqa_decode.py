@@ -72,7 +72,8 @@ def _check(o, lse, host, scale, seqs, **kw):
                          f"max |dLSE| {np.abs(lse[b] - l_ref).max():.3g}"
 
 
-@pytest.mark.parametrize("q_heads,kv_heads", [(32, 8), (8, 8), (16, 8), (32, 2), (64, 4)])
+@pytest.mark.parametrize("q_heads,kv_heads", [(32, 8), (8, 8), (16, 8), (32, 2), (64, 4), (64, 8), (24, 8),
+                                                (40, 8), (21, 3)])
 def test_gqa_decode_small(q_heads, kv_heads):
     lens = [64, 100, 1000, 2048 + 17, 1, 33]
     host, devs = _setup(len(lens), q_heads, kv_heads, lens, bt_stride=40, keys=(1, q_heads, kv_heads))
