@@ -433,14 +433,37 @@ __global__ __launch_bounds__(256) void eig_kernel(const FormEigArgs A) {
     }
 }
 
-__global__ __launch_bounds__(256) void mean_kernel(const float* D, int orders, int64_t per, int64_t total4, float* out) {
+// Workgroup w takes 1024 float4 of matrix w / chunks; each thread streams
+// four of them with every order's loads unrolled ahead of the sums (read
+// once: nontemporal).
+__global__ __launch_bounds__(256) void mean_kernel(const float* D, int orders, int64_t per4, int chunks, float* out) {
+    const int wg = blockIdx.x;
+    const int b = wg / chunks, c = wg - b * chunks;
     const float inv = 1.f / (float)orders;
-    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total4; u += (int64_t)gridDim.x * 256) {
-        const int64_t b = u / (per / 4), off = u - b * (per / 4);
-        const v4f* src = reinterpret_cast<const v4f*>(D + b * orders * per) + off;
-        v4f s = src[0];
-        for (int p = 1; p < orders; ++p) s += src[(int64_t)p * (per / 4)];
-        reinterpret_cast<v4f*>(out)[u] = s * inv;
+    const v4f* src = reinterpret_cast<const v4f*>(D) + (int64_t)b * orders * per4;
+    v4f* dst = reinterpret_cast<v4f*>(out) + (int64_t)b * per4;
+    const int64_t u0 = (int64_t)c * 1024 + threadIdx.x;
+    v4f s[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t u = u0 + 256 * k;
+        s[k] = u < per4 ? __builtin_nontemporal_load(src + u) : v4f{0, 0, 0, 0};
+    }
+#pragma unroll 3
+    for (int p = 1; p < orders; ++p) {
+        v4f x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t u = u0 + 256 * k;
+            x[k] = u < per4 ? __builtin_nontemporal_load(src + (int64_t)p * per4 + u) : v4f{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s[k] += x[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t u = u0 + 256 * k;
+        if (u < per4) __builtin_nontemporal_store(s[k] * inv, dst + u);
     }
 }
 
@@ -465,10 +488,17 @@ hipError_t launch_form_eig(const FormEigArgs& a, int count, hipStream_t s) {
 }
 
 hipError_t launch_form_mean(const float* d, int orders, int64_t per, int64_t n, float* out, hipStream_t s) {
-    const int64_t total4 = n * per / 4;
-    const unsigned grid = (unsigned)std::min<int64_t>((total4 + 255) / 256, 8192);
-    hipLaunchKernelGGL(mean_kernel, dim3(grid), dim3(256), 0, s, d, orders, per, total4, out);
-    return hipGetLastError();
+    const int64_t per4 = per / 4;
+    const int chunks = (int)((per4 + 1023) / 1024);
+    const int64_t batch = std::max<int64_t>(1, ((int64_t)1 << 30) / chunks);     // matrices per launch
+    for (int64_t b0 = 0; b0 < n; b0 += batch) {
+        const int64_t nb = std::min(batch, n - b0);
+        hipLaunchKernelGGL(mean_kernel, dim3((unsigned)(nb * chunks)), dim3(256), 0, s, d + b0 * orders * per, orders,
+                           per4, chunks, out + b0 * per);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kvr
