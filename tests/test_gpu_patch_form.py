@@ -78,6 +78,15 @@ def test_orbit_patch_of_the_mean_deficit():
         _check(svd.orbit_deficit(d[b].cpu().double().numpy()), U[b], V[b], s[b], 16)
 
 
+@pytest.mark.parametrize("orders", [2, 3, 7])
+def test_orbit_mean_order_counts(orders):
+    """Other order counts: the factors are those of the mean deficit."""
+    d = _deficits(2, 128, 192, (5, orders), orders=orders, noise=5e-3)
+    U, V, s = _run(d, 8, _omega(192, 4))
+    for b in range(2):
+        _check(svd.orbit_deficit(d[b].cpu().double().numpy()), U[b], V[b], s[b], 8)
+
+
 def test_planted_low_rank_and_rank_deficient():
     """A planted rank-8 deficit without noise: with m = 8 the patch is the
     deficit itself; with m = 16 the first 8 singular values are recovered,
