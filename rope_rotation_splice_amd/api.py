@@ -128,19 +128,59 @@ def _workspace(nbytes, device, kind):
     return ws
 
 
+# numpy mirror of kvr_directive (three int64, mode, reserved), filled in one
+# vectorized pass; the ctypes pointer keeps the array alive
+_DIR_DT = np.dtype([("s_start", "<i8"), ("s_end", "<i8"), ("r_len", "<i8"), ("mode", "<i4"), ("reserved", "<i4")])
+assert _DIR_DT.itemsize == ctypes.sizeof(kvr_directive)
+# numpy mirror of kvr_lazy_entry (seq, padding, two device pointers, three int64)
+_LAZY_DT = np.dtype([("seq", "<i4"), ("pad", "<i4"), ("d_blocks", "<u8"), ("d_pend", "<u8"), ("len", "<i8"),
+                     ("base_pos", "<i8"), ("p_target", "<i8")])
+assert _LAZY_DT.itemsize == ctypes.sizeof(_abi.kvr_lazy_entry)
+
+
+class _HostArray:
+    """A host array handed to the library as a typed pointer: a ctypes array
+    (cheapest for a few items) or a numpy array (cheapest for many; holding
+    this object keeps it alive for the call, since ctypes.cast keeps no
+    reference and ndarray.ctypes.data_as is slow)."""
+    __slots__ = ("a", "p")
+
+    def __init__(self, a, ctype=None):
+        self.a = a
+        self.p = a if ctype is None else ctypes.cast(a.ctypes.data, ctypes.POINTER(ctype))
+
+    def values(self, n):
+        return np.array(self.a[:n], dtype=np.int64)
+
+
+_FEW = 8      # below this many items plain ctypes arrays are cheaper than numpy
+
+
 def _directives(directives):
-    d = np.asarray(directives, dtype=np.int64).reshape(-1, 4) if len(directives) else np.zeros((0, 4), np.int64)
-    arr = (kvr_directive * max(1, len(d)))()
-    for i, (s, e, r, m) in enumerate(d):
-        arr[i] = kvr_directive(int(s), int(e), int(r), int(m), 0)
-    return arr, len(d)
+    """(host array of kvr_directive, count); pass ``.p`` to the library."""
+    n = len(directives)
+    if n <= _FEW:
+        return _HostArray((kvr_directive * max(1, n))(*[kvr_directive(int(s), int(e), int(r), int(m), 0)
+                                                        for s, e, r, m in directives])), n
+    d = np.asarray(directives, dtype=np.int64).reshape(-1, 4)
+    arr = np.zeros(len(d), dtype=_DIR_DT)
+    arr["s_start"], arr["s_end"], arr["r_len"], arr["mode"] = d[:, 0], d[:, 1], d[:, 2], d[:, 3]
+    return _HostArray(arr, kvr_directive), len(d)
+
+
+def _i64(values, n):
+    """A host int64 array of at least one element (the first n from values)."""
+    if n <= _FEW:
+        return _HostArray((ctypes.c_int64 * max(1, n))(*[int(values[i]) for i in range(n)]))
+    a = np.asarray(values, dtype=np.int64).reshape(-1)[:n].copy()
+    return _HostArray(a, ctypes.c_int64)
 
 
 def splice_workspace_bytes(cache, seq_lens, directives):
     lib = _abi.load()
     dirs, n = _directives(directives)
-    lens = (ctypes.c_int64 * max(1, n))(*[int(x) for x in seq_lens])
-    return int(lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens, dirs))
+    lens = _i64(seq_lens, n)
+    return int(lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens.p, dirs.p))
 
 
 def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, workspace=None):
@@ -154,21 +194,20 @@ def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, worksp
     dirs, n = _directives(directives)
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.stride(1) != 1:
         raise ValueError("block_tables must be an int32 [n_seq, blocks] tensor with unit last stride")
-    lens = (ctypes.c_int64 * max(1, n))(*[int(x) for x in seq_lens])
-    out = (ctypes.c_int64 * max(1, n))()
+    lens, out = _i64(seq_lens, n), _i64(np.zeros(n, np.int64), n)
     stub_arr = None
     if stubs is not None:
         stub_arr = (kvr_rows * max(1, n))()
         for i, s in enumerate(stubs):
             if s is not None:
                 stub_arr[i] = s.c()
-    need = lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens, dirs)
+    need = lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens.p, dirs.p)
     ws = workspace if workspace is not None else _workspace(need, cache.pf.device, "splice")
     st = lib.leyline_splice(ctypes.byref(cache.c), block_tables.data_ptr(), int(block_tables.stride(0)), n,
-                            lens, dirs, stub_arr, out, ws.data_ptr(), ws.numel() * ws.element_size(),
+                            lens.p, dirs.p, stub_arr, out.p, ws.data_ptr(), ws.numel() * ws.element_size(),
                             _stream_handle())
     _check("leyline_splice", st)
-    return np.array(out[:n], dtype=np.int64), st
+    return out.values(n), st
 
 
 def leyline_splice_lazy(block_tables, pending_delta, block_size, seq_lens, directives, stub_blocks=None):
@@ -188,31 +227,50 @@ def leyline_splice_lazy(block_tables, pending_delta, block_size, seq_lens, direc
             raise ValueError("block_tables and pending_delta must be int32 [n_seq, blocks] with unit last stride")
     if pending_delta.shape != block_tables.shape or pending_delta.stride(0) != block_tables.stride(0):
         raise ValueError("pending_delta must match block_tables in shape and row stride")
-    d = np.asarray(directives, dtype=np.int64).reshape(-1, 4)
-    amort = d[:, 3] == 0
-    n_free = int(((d[:, 1] - d[:, 0]) // block_size)[amort].sum()) if n else 0
+    if n > _FEW:
+        da = dirs.a
+        n_free = int(((da["s_end"] - da["s_start"]) // block_size)[da["mode"] == 0].sum())
+    else:
+        n_free = sum(int((d[1] - d[0]) // block_size) for d in directives if int(d[3]) == KVR_AMORTIZE)
     if stub_blocks is not None and (stub_blocks.dtype != torch.int32 or not stub_blocks.is_contiguous()):
         raise ValueError("stub_blocks must be a contiguous int32 tensor")
     freed = torch.empty(max(1, n_free), dtype=torch.int32, device=block_tables.device)
-    lens = (ctypes.c_int64 * max(1, n))(*[int(x) for x in seq_lens])
-    out = (ctypes.c_int64 * max(1, n))()
+    lens, out = _i64(seq_lens, n), _i64(np.zeros(n, np.int64), n)
     st = lib.leyline_splice_lazy(int(block_size), block_tables.data_ptr(), pending_delta.data_ptr(),
-                                 int(block_tables.stride(0)), n, lens, dirs,
+                                 int(block_tables.stride(0)), n, lens.p, dirs.p,
                                  stub_blocks.data_ptr() if stub_blocks is not None and stub_blocks.numel() else None,
-                                 freed.data_ptr() if n_free else None, out, _stream_handle())
+                                 freed.data_ptr() if n_free else None, out.p, _stream_handle())
     _check("leyline_splice_lazy", st)
-    return np.array(out[:n], dtype=np.int64), freed[:n_free], st
+    return out.values(n), freed[:n_free], st
 
 
 class LazyEntry:
     """A registry entry kept in pool blocks (row 0 at the start of blocks[0]),
     placed by reference at ``p_target`` of sequence ``seq``.  blocks: int32
     device tensor [ceil(len / block_size)]; pend: the shifts those blocks
-    already owe (int32 device tensor of the same length) or None."""
+    already owe (int32 device tensor of the same length) or None.  The
+    tensors are checked and their addresses taken once, here: an entry is
+    immutable, and its tensors must not be resized while it is in use."""
+    __slots__ = ("_seq", "_blocks", "_pend", "_len", "_base", "_target", "_row", "_n_blocks", "_n_pend")
 
     def __init__(self, seq, blocks, length, base_pos, p_target, pend=None):
-        self.seq, self.blocks, self.len = int(seq), blocks, int(length)
-        self.base_pos, self.p_target, self.pend = int(base_pos), int(p_target), pend
+        for t in (blocks, pend):
+            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+                raise ValueError("entry blocks and pend must be contiguous int32 tensors")
+        self._seq, self._blocks, self._pend, self._len = int(seq), blocks, pend, int(length)
+        self._base, self._target = int(base_pos), int(p_target)
+        self._n_blocks = blocks.numel() if blocks is not None else 0
+        self._n_pend = pend.numel() if pend is not None else None
+        self._row = (self._seq, 0, blocks.data_ptr() if self._n_blocks else 0,
+                     pend.data_ptr() if pend is not None and self._n_pend else 0,
+                     self._len, self._base, self._target)
+
+    seq = property(lambda self: self._seq)
+    blocks = property(lambda self: self._blocks)
+    pend = property(lambda self: self._pend)
+    len = property(lambda self: self._len)
+    base_pos = property(lambda self: self._base)
+    p_target = property(lambda self: self._target)
 
 
 def kv_relocate_gather_lazy(block_tables, pending_delta, block_size, entries):
@@ -231,20 +289,18 @@ def kv_relocate_gather_lazy(block_tables, pending_delta, block_size, entries):
     if pending_delta.shape != block_tables.shape or pending_delta.stride(0) != block_tables.stride(0):
         raise ValueError("pending_delta must match block_tables in shape and row stride")
     n = len(entries)
-    arr = (_abi.kvr_lazy_entry * max(1, n))()
     total = 0
-    for i, e in enumerate(entries):
-        nb = -(-e.len // int(block_size)) if e.len > 0 else 0
-        for t in (e.blocks, e.pend):
-            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < nb):
-                raise ValueError("entry blocks and pend must be contiguous int32 tensors of ceil(len / B) ids")
-        arr[i].seq, arr[i].len, arr[i].base_pos, arr[i].p_target = e.seq, e.len, e.base_pos, e.p_target
-        arr[i].d_blocks = e.blocks.data_ptr() if e.blocks is not None and e.blocks.numel() else None
-        arr[i].d_pend = e.pend.data_ptr() if e.pend is not None and e.pend.numel() else None
-        total += max(0, nb)
+    B = int(block_size)
+    for e in entries:
+        nb = -(-e._len // B) if e._len > 0 else 0
+        if e._n_blocks < nb or (e._n_pend is not None and e._n_pend < nb):
+            raise ValueError("entry blocks and pend need ceil(len / block_size) ids")
+        total += nb
+    arr = np.array([e._row for e in entries] or [(0, 0, 0, 0, 0, 0, 0)], dtype=_LAZY_DT)
+    ents = _HostArray(arr, _abi.kvr_lazy_entry)
     replaced = torch.empty(max(1, total), dtype=torch.int32, device=block_tables.device)
     st = lib.kv_relocate_gather_lazy(int(block_size), block_tables.data_ptr(), pending_delta.data_ptr(),
-                                     int(block_tables.stride(0)), int(block_tables.shape[0]), arr, n,
+                                     int(block_tables.stride(0)), int(block_tables.shape[0]), ents.p, n,
                                      replaced.data_ptr() if total else None, _stream_handle())
     _check("kv_relocate_gather_lazy", st)
     return replaced[:total], st
