@@ -191,6 +191,27 @@ class Splice:
         # the same directive on the restored length: same bytes and hazards each step
         self.rrs.leyline_splice(self.cache, self.bt, [4096], self.dirs, self.stubs)
 
+    def extra(self):
+        """Latency of one call, end to end (host marshalling, launch and the
+        kernel, to completion), warm and after writing 1 GiB to flush the
+        L2 and the MALL: medians of 30 calls each."""
+        import torch
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        out = {}
+        for kind in ("warm", "after_1GiB_flush"):
+            ts = []
+            for _ in range(30):
+                if kind != "warm":
+                    flush.zero_()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                self.step()
+                torch.cuda.synchronize()
+                ts.append((time.perf_counter() - t0) * 1e6)
+            out[kind] = float(np.median(ts))
+        del flush
+        return {"latency_us": out}
+
     def cpu_baseline(self, budget_s):
         import kvsynth
         from oracle import splice as osplice, rope as orope
@@ -905,6 +926,8 @@ def main():
         "cpu_baseline": cpu,
     }
     out.update(extra)
+    if hasattr(wl, "extra"):
+        out.update(wl.extra())
     print(json.dumps(out))
     return 0
 
