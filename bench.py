@@ -816,19 +816,24 @@ class PatchForm:
 
 
 class Copy:
-    """A plain device-to-device copy of the registry gather's byte volume
-    (torch's copy kernel): the practical read+write ceiling, and the known-size
-    kernel that calibrates the HBM byte counters."""
+    """A plain device-to-device copy (torch's copy kernel) of the registry
+    gather's byte volume, or with ``batched`` of the batched splice's (64.5 GB
+    read, 64.5 GB written): the practical read+write ceiling, and the
+    known-size kernel that calibrates the HBM byte counters."""
     name = "copy"
     kernel = "torch copy_"
 
-    def __init__(self):
-        g = Gather()
-        self.nbytes = g.bytes // 2 // 2 * 2
-        self.slots = g.slots
+    def __init__(self, batched=False):
+        if batched:
+            w = SpliceBatched()
+            self.nbytes, self.slots = w.bytes // 2 // 2 * 2, w.slots
+        else:
+            g = Gather()
+            self.nbytes, self.slots = g.bytes // 2 // 2 * 2, g.slots
         self.bytes = 2 * self.nbytes
         self.launches = 1
-        self.config = {"workload": "device_copy", "bytes_read": self.nbytes, "bytes_written": self.nbytes}
+        self.config = {"workload": "device_copy_batched_splice_volume" if batched else "device_copy",
+                       "bytes_read": self.nbytes, "bytes_written": self.nbytes}
 
     def setup(self):
         import torch
@@ -846,7 +851,8 @@ WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched
              "gather_lazy": GatherLazy,
              "gqa_patch": GqaPatch, "keys": Keys,
              "decode": Decode, "decode_zero_delta": lambda: Decode(zero_delta=True), "gqa_decode": GqaDecode,
-             "patch_form": PatchForm, "orbit_patch": lambda: PatchForm(orders=4), "copy": Copy}
+             "patch_form": PatchForm, "orbit_patch": lambda: PatchForm(orders=4), "copy": Copy,
+             "copy_batched": lambda: Copy(batched=True)}
 
 
 def main():
