@@ -270,3 +270,48 @@ def test_lazy_gather_then_decode():
     # each sequence ends where its last entry ends (a ragged entry comes last)
     lens = [max([p + ln for (q, bl, own, ln, base, p) in ents if q == s] + [B]) for s in range(3)]
     _decode_check(pool_h, pool_d, bt_d, pd_d, lens, (qn_h, dev(qn_h)), (qr_h, dev(qr_h)), 1.0 / math.sqrt(576.0))
+
+
+def test_lazy_splice_workload_full_size():
+    """The lazy-splice benchmark's configuration (64 sequences x 32768 slots,
+    512-entry tables, the batched-splice directives widened to blocks), table
+    for table against the oracle."""
+    import torch
+    import bench
+    wl = bench.SpliceLazy()
+    w, B = wl.w, wl.w.block_size
+    bt = w.block_tables.astype(np.int32)
+    pend = kvsynth.rng(23, 1).integers(-100000, 100000, size=bt.shape, endpoint=True).astype(np.int32)
+    n_stub = sum(d[2] // B for d in wl.dirs)
+    stubs = np.arange(w.n_blocks, w.n_blocks + n_stub, dtype=np.int32)
+    bt_d, pd_d = torch.from_numpy(bt.copy()).cuda(), torch.from_numpy(pend.copy()).cuda()
+    lens = [int(x) for x in w.seq_lens]
+    new_lens, freed, st = _apply(bt_d, pd_d, B, lens, wl.dirs, stubs)
+    bt2, pd2, fr2, nl2 = _oracle_all(bt, pend, B, lens, wl.dirs, stubs)
+    assert st == 0 and list(new_lens) == list(nl2)
+    assert (bt_d.cpu().numpy() == bt2).all() and (pd_d.cpu().numpy() == pd2).all()
+    assert list(freed) == list(fr2)
+
+
+def test_lazy_gather_workload_full_size():
+    """The lazy-gather benchmark's configuration (32 registry entries packed at
+    block-aligned targets of one 590-block sequence) against the oracle."""
+    import torch
+    import bench
+    wl = bench.GatherLazy()
+    B = wl.w.block_size
+    r = kvsynth.rng(23, 2)
+    bt = r.permutation(4 * wl.bt_stride)[: wl.bt_stride].astype(np.int32).reshape(1, -1)
+    pend = r.integers(-100000, 100000, size=bt.shape, endpoint=True).astype(np.int32)
+    ents, nxt = [], 10 * wl.bt_stride
+    for c in range(len(wl.nb)):
+        n = int(wl.nb[c])
+        own = r.integers(-5000, 5000, size=n).astype(np.int32) if c % 3 == 0 else None
+        ents.append((0, np.arange(nxt, nxt + n, dtype=np.int32), own, n * B, int(wl.w.base_pos[c]), int(wl.tgt[c])))
+        nxt += n
+    bt_d, pd_d = torch.from_numpy(bt.copy()).cuda(), torch.from_numpy(pend.copy()).cuda()
+    rep, st = _run_lazy_gather(bt_d, pd_d, B, ents)
+    bt2, pd2, rep2 = _lazy_gather_oracle(bt, pend, B, ents)
+    assert st == 0
+    assert (bt_d.cpu().numpy() == bt2).all() and (pd_d.cpu().numpy() == pd2).all()
+    assert list(rep) == list(rep2)
