@@ -89,6 +89,22 @@ def test_decode_layer_offset_and_many_splits():
             f"seq {b}: max rel-L2 {rel.max():.3g}, max |dLSE| {np.abs(lse[b] - l_ref).max():.3g}"
 
 
+def test_decode_empty_sequence():
+    """A sequence with no cached token attends to nothing: O = 0, LSE = -inf;
+    its neighbours in the batch are unaffected."""
+    import rope_rotation_splice_amd as rrs
+    lens = [0, 70, 0, 64]
+    host, devs = _setup(4, 64, lens, bt_stride=4, keys=(4,))
+    scale = 1.0 / math.sqrt(576.0)
+    o, lse = _run(devs, scale, max_len=4 * 64)
+    for b in (0, 2):
+        assert (o[b] == 0).all() and np.isneginf(lse[b]).all()
+    for b in (1, 3):
+        o_ref, l_ref, eps = _oracle(host, b, scale)
+        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps).all()
+    assert rrs.device_errors() == 0
+
+
 def test_decode_large_logits_restart():
     """Scores that jump far above the first tile's maximum (a sharp needle late
     in a split) exercise the restart path: still exact to tolerance."""
