@@ -65,6 +65,9 @@ SIGNATURES = {
                                P(c_i64), c_vp, c_size, c_vp]),
     "kv_relocate_gather": (c_i32, [P(kvr_cache), c_vp, c_i32, P(kvr_rows), P(c_i64), c_i32,
                                    P(kvr_lowrank), P(kvr_lowrank), c_vp]),
+    "kvr_gather_workspace_bytes": (c_size, [P(kvr_cache), P(kvr_rows), c_i32]),
+    "kv_relocate_gather_ws": (c_i32, [P(kvr_cache), c_vp, c_i32, P(kvr_rows), P(c_i64), c_i32,
+                                      P(kvr_lowrank), P(kvr_lowrank), c_vp, c_size, c_vp]),
     "kv_patch_lowrank": (c_i32, [P(kvr_cache), c_vp, c_i32, c_i32, P(c_i64), P(c_i64), P(kvr_lowrank),
                                  c_i32, c_vp]),
     "kvr_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32]),
@@ -93,7 +96,7 @@ def load():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m rope_rotation_splice_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python rope_rotation_splice_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

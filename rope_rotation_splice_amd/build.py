@@ -1,6 +1,6 @@
 """Build the HIP library ``libkvreloc.so`` in-tree for gfx950.
 
-``python -m rope_rotation_splice_amd.build`` (or ``build()``) compiles every
+``python rope_rotation_splice_amd/build.py`` (or ``build()``) compiles every
 source under ``csrc/`` with hipcc and links the shared library next to this
 file.  It always recompiles.
 """

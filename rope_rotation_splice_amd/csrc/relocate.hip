@@ -57,19 +57,38 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
     const Pool& P = A.pool;
 
     // ---- which unit (item, layer) and which tile --------------------------
-    int it = 0;
-    {
-        int hi = A.n_items - 1;          // last item whose first workgroup <= bid
-        while (it < hi) {
-            const int mid = (it + hi + 1) >> 1;
-            if (bid >= A.items[mid].wg_off) it = mid; else hi = mid - 1;
+    // last item whose first workgroup (splice) or tile (gather) is <= x: the
+    // offsets are ascending and padded with INT32_MAX, so a count suffices
+    auto item_at = [&](int x) __attribute__((always_inline)) {
+        int n = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxItems; ++i) n += x >= A.offs[i] ? 1 : 0;
+        return n;
+    };
+    int it = MODE == kSplice ? item_at(bid) : 0;
+    int t, layer;
+    if (MODE == kGather) {
+        // layer after layer; in destination order the k-th workgroup of a
+        // layer takes the (tile, item) pair order[k] = tile << 5 | item
+        layer = bid / A.n_tiles;
+        const int k = bid - layer * A.n_tiles;
+        if (A.order) {
+            const uint32_t v = A.order[k];
+            it = (int)(v & 31u);
+            t = (int)(v >> 5);
+            if (it >= A.n_items || t >= A.items[it].tiles) {   // a damaged order table
+                if (tid == 0) raise_error(KVR_DEV_BAD_TICKET);
+                return;
+            }
+        } else {
+            it = item_at(k);
+            t = k - A.offs[it];
         }
     }
     const Item& I = A.items[it];
-    const int local = bid - I.wg_off;
-    const int layer = local / I.tiles;
-    int t;
     if (MODE == kSplice) {
+        const int local = bid - I.wg_off;
+        layer = local / I.tiles;
         if (tid == 0) {
             int tk = -1;
             if ((__hip_atomic_load(&g_errors_relocate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
@@ -84,8 +103,6 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
         __syncthreads();
         t = s_ticket;
         if (t < 0) return;
-    } else {
-        t = local - layer * I.tiles;
     }
 
     const int T = A.tile_rows;
@@ -274,6 +291,87 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
         p[i] = 0u;
 }
 
+// Counting sort of a gather's tiles by the physical block (>> bucket_shift)
+// that each tile's first row lands in; ids outside the pool go last.  One
+// workgroup: LDS histogram, exclusive scan, then scatter through LDS atomics
+// (tiles sharing a bucket land in any order among themselves).  Each thread
+// looks up 8 tiles' block ids at a time so their loads overlap, and the
+// bucket of each of the first kOrderKeyCache tiles is kept in LDS for the
+// scatter pass.
+constexpr int kOrderKeyCache = 32768;
+
+__global__ __launch_bounds__(kOrderThreads) void gather_order_kernel(const GatherOrderArgs A) {
+    __shared__ uint32_t cnt[kOrderBuckets];
+    __shared__ uint16_t key[kOrderKeyCache];
+    __shared__ uint32_t wsum[kOrderThreads / 64];
+    __shared__ int32_t s_off[kMaxItems + 1], s_slot0[kMaxItems];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nbk = ((A.n_blocks - 1) >> A.bucket_shift) + 2;
+    for (int i = tid; i < nbk; i += kOrderThreads) cnt[i] = 0u;
+    if (tid <= A.n_items) s_off[tid] = A.tile_off[tid];
+    if (tid < A.n_items) s_slot0[tid] = A.slot0[tid];
+    __syncthreads();
+    // item of tile g (binary search over the tile offsets)
+    auto item_of = [&](int g) -> int {
+        int it = 0, hi = A.n_items - 1;
+        while (it < hi) {
+            const int mid = (it + hi + 1) >> 1;
+            if (g >= s_off[mid]) it = mid; else hi = mid - 1;
+        }
+        return it;
+    };
+    auto block_index = [&](int g) -> int {
+        const int it = item_of(g);
+        const int slot = s_slot0[it] + (g - s_off[it]) * A.tile_rows;
+        return A.bs_shift >= 0 ? (slot >> A.bs_shift) : slot / A.block_size;
+    };
+    auto to_bucket = [&](int id) -> uint32_t {
+        return (unsigned)id < (unsigned)A.n_blocks ? (uint32_t)(id >> A.bucket_shift) : (uint32_t)(nbk - 1);
+    };
+    constexpr int kBatch = 8;
+    for (int g0 = tid; g0 < A.n_tiles; g0 += kBatch * kOrderThreads) {
+        int id[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int g = g0 + u * kOrderThreads;
+            id[u] = g < A.n_tiles ? A.bt[block_index(g)] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int g = g0 + u * kOrderThreads;
+            if (g < A.n_tiles) {
+                const uint32_t b = to_bucket(id[u]);
+                if (g < kOrderKeyCache) key[g] = (uint16_t)b;
+                atomicAdd(&cnt[b], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    // exclusive scan: each thread owns `per` consecutive counters
+    const int per = (nbk + kOrderThreads - 1) / kOrderThreads;
+    const int c0 = min(nbk, tid * per), c1 = min(nbk, c0 + per);
+    uint32_t own = 0;
+    for (int i = c0; i < c1; ++i) own += cnt[i];
+    uint32_t incl = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t base = incl - own;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    for (int i = c0; i < c1; ++i) { const uint32_t c = cnt[i]; cnt[i] = base; base += c; }
+    __syncthreads();
+    for (int g = tid; g < A.n_tiles; g += kOrderThreads) {
+        const uint32_t b = g < kOrderKeyCache ? (uint32_t)key[g] : to_bucket(A.bt[block_index(g)]);
+        const uint32_t pos = atomicAdd(&cnt[b], 1u);
+        const int it = item_of(g);
+        A.order[pos] = ((uint32_t)(g - s_off[it]) << 5) | (uint32_t)it;
+    }
+}
+
 template <int MODE, int PFI, int RS>
 hipError_t launch_one(const RelocArgs& a, bool f32, hipStream_t s) {
     if (f32) hipLaunchKernelGGL((reloc_kernel<MODE, PFI, RS, true>), dim3(a.n_wg), dim3(kThreads), 0, s, a);
@@ -314,6 +412,11 @@ hipError_t launch_splice(const RelocArgs& a, int pfi, int rs, bool f32, hipStrea
 }
 hipError_t launch_gather(const RelocArgs& a, int pfi, int rs, bool f32, hipStream_t s) {
     return launch<kGather>(a, pfi, rs, f32, s);
+}
+
+hipError_t launch_gather_order(const GatherOrderArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(gather_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
