@@ -225,33 +225,6 @@ kvr_status kv_relocate_gather(const kvr_cache* dst, const int32_t* d_block_table
                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * kv_relocate_gather_ws -- kv_relocate_gather (same operation, arguments,
- * results and errors; Irminsul 2.2) with a workspace that lets the row mover
- * visit its tiles in destination order: a one-workgroup kernel first sorts
- * the tiles by the physical block each one writes, so every layer's writes
- * sweep the pool in address order.  The order changes nothing in the
- * results (each destination row is written by exactly one tile).  It is used
- * when a launch moves at least 512 MiB (the extra launch costs a few
- * microseconds); the environment variable KVR_GATHER_ORDER=1 / 0 forces it
- * on / off.  With patch factors the workspace is unused.
- *
- *   d_workspace : device, at least kvr_gather_workspace_bytes(dst, entries,
- *                 n) bytes, 256-byte aligned, contents need no
- *                 initialization.  Calls sharing a workspace must be
- *                 ordered on one stream.
- * Errors: those of kv_relocate_gather, and KVR_E_WORKSPACE (missing,
- * misaligned or too small).
- * ---------------------------------------------------------------------- */
-size_t kvr_gather_workspace_bytes(const kvr_cache* dst, const kvr_rows* entries, int32_t n);
-
-kvr_status kv_relocate_gather_ws(const kvr_cache* dst, const int32_t* d_block_table,
-                                 int32_t bt_len, const kvr_rows* entries,
-                                 const int64_t* p_target, int32_t n,
-                                 const kvr_lowrank* patch_rope, const kvr_lowrank* patch_pf,
-                                 void* d_workspace, size_t workspace_bytes,
-                                 hipStream_t stream);
-
-/* ------------------------------------------------------------------------
  * kv_patch_lowrank -- add Kamera's rank-m patch in place to rows already in
  * the cache (Kamera 2): for item i, logical slots [p_start[i], p_start[i] +
  * len[i]) of every layer, X += U_i V_i^T on the chosen part (0 = position-

@@ -65,9 +65,6 @@ SIGNATURES = {
                                P(c_i64), c_vp, c_size, c_vp]),
     "kv_relocate_gather": (c_i32, [P(kvr_cache), c_vp, c_i32, P(kvr_rows), P(c_i64), c_i32,
                                    P(kvr_lowrank), P(kvr_lowrank), c_vp]),
-    "kvr_gather_workspace_bytes": (c_size, [P(kvr_cache), P(kvr_rows), c_i32]),
-    "kv_relocate_gather_ws": (c_i32, [P(kvr_cache), c_vp, c_i32, P(kvr_rows), P(c_i64), c_i32,
-                                      P(kvr_lowrank), P(kvr_lowrank), c_vp, c_size, c_vp]),
     "kv_patch_lowrank": (c_i32, [P(kvr_cache), c_vp, c_i32, c_i32, P(c_i64), P(c_i64), P(kvr_lowrank),
                                  c_i32, c_vp]),
     "kvr_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32]),

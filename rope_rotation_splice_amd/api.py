@@ -346,14 +346,10 @@ def registry_chunk_keys(tokens, offsets, gear, threshold, min_len, max_len, s1_w
     return out
 
 
-def kv_relocate_gather(cache, block_table, entries, p_targets, patch_rope=None, patch_pf=None, ordered=True,
-                       workspace=None):
+def kv_relocate_gather(cache, block_table, entries, p_targets, patch_rope=None, patch_pf=None):
     """Gather registry entries (list of Rows) into one paged destination
     sequence at logical slots p_targets[i] + t; optional rank-m patches
-    (lists of LowRank or None).  ordered=True goes through
-    kv_relocate_gather_ws (tiles visited in destination order, with a
-    workspace kept per device and stream unless one is given); False calls
-    the plain kv_relocate_gather."""
+    (lists of LowRank or None)."""
     lib = _abi.load()
     n = len(entries)
     if block_table.dtype != torch.int32 or block_table.dim() != 1 or block_table.stride(0) != 1:
@@ -370,16 +366,9 @@ def kv_relocate_gather(cache, block_table, entries, p_targets, patch_rope=None, 
                 arr[i] = f.c()
         return arr
 
-    if not ordered:
-        st = lib.kv_relocate_gather(ctypes.byref(cache.c), block_table.data_ptr(), int(block_table.numel()), ents,
-                                    pt, n, lr(patch_rope), lr(patch_pf), _stream_handle())
-        return _check("kv_relocate_gather", st)
-    need = int(lib.kvr_gather_workspace_bytes(ctypes.byref(cache.c), ents, n))
-    ws = workspace if workspace is not None else _workspace(need, block_table.device, "gather")
-    st = lib.kv_relocate_gather_ws(ctypes.byref(cache.c), block_table.data_ptr(), int(block_table.numel()), ents,
-                                   pt, n, lr(patch_rope), lr(patch_pf), ws.data_ptr(),
-                                   ws.numel() * ws.element_size(), _stream_handle())
-    return _check("kv_relocate_gather_ws", st)
+    st = lib.kv_relocate_gather(ctypes.byref(cache.c), block_table.data_ptr(), int(block_table.numel()), ents,
+                                pt, n, lr(patch_rope), lr(patch_pf), _stream_handle())
+    return _check("kv_relocate_gather", st)
 
 
 def kv_patch_lowrank(cache, block_table, part, p_starts, lens, factors):

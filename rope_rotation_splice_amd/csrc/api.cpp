@@ -399,28 +399,10 @@ kvr_status leyline_splice(const kvr_cache* cache, const int32_t* d_block_tables,
 
 // ------------------------------------------------------------------ gather --
 
-namespace {
-
-// Tiles per layer of the gather's row mover for these entries (all batches).
-int64_t gather_tiles(const kvr_cache* dst, const kvr_rows* entries, int32_t n) {
-    Pool pool;
-    double omega[kMaxPairs];
-    if (make_pool(dst, pool, omega) != KVR_OK) return -1;
-    const int T = choose_tile(pool, dst->rope_dtype == KVR_F32, false).T;
-    int64_t tiles = 0;
-    for (int32_t i = 0; i < n; ++i)
-        if (entries[i].len > 0) tiles += (entries[i].len + T - 1) / T;
-    return tiles;
-}
-
-// Destination order pays for its extra launch (a few microseconds) once a
-// launch moves this many bytes; KVR_GATHER_ORDER=1 / 0 forces it on / off.
-constexpr int64_t kOrderMinBytes = (int64_t)512 << 20;
-
-kvr_status gather_impl(const kvr_cache* dst, const int32_t* d_block_table, int32_t bt_len,
-                       const kvr_rows* entries, const int64_t* p_target, int32_t n,
-                       const kvr_lowrank* patch_rope, const kvr_lowrank* patch_pf,
-                       void* d_ws, size_t ws_bytes, hipStream_t stream) {
+kvr_status kv_relocate_gather(const kvr_cache* dst, const int32_t* d_block_table, int32_t bt_len,
+                              const kvr_rows* entries, const int64_t* p_target, int32_t n,
+                              const kvr_lowrank* patch_rope, const kvr_lowrank* patch_pf,
+                              hipStream_t stream) {
     Pool pool;
     double omega[kMaxPairs];
     kvr_status st = make_pool(dst, pool, omega);
@@ -480,19 +462,9 @@ kvr_status gather_impl(const kvr_cache* dst, const int32_t* d_block_table, int32
 
     const TileShape tile = choose_tile(pool, dst->rope_dtype == KVR_F32, false);
     const int T = tile.T;
-    if (d_ws) {
-        const int64_t tiles = gather_tiles(dst, entries, n);
-        if ((reinterpret_cast<uintptr_t>(d_ws) % kAlign) || tiles < 0 || ws_bytes < (size_t)tiles * 4)
-            return KVR_E_WORKSPACE;
-    }
-    int force = -1;
-    if (const char* e = std::getenv("KVR_GATHER_ORDER")) force = std::atoi(e) != 0;
-    const int64_t row_bytes = 16 * (int64_t)(pool.pf_chunks + 2 * pool.rope_items);
-    int bucket_shift = 0;
-    while (((pool.n_blocks - 1) >> bucket_shift) + 2 > kOrderBuckets) ++bucket_shift;
-
+    // Workgroups go layer after layer, each layer's tiles item after item.
     std::vector<Item> cur;
-    int64_t tiles = 0, rows = 0;     // of the batch, per layer
+    int64_t tiles = 0;               // of the batch, per layer
     auto flush = [&]() -> kvr_status {
         if (cur.empty()) return KVR_OK;
         RelocArgs a;
@@ -509,33 +481,9 @@ kvr_status gather_impl(const kvr_cache* dst, const int32_t* d_block_table, int32
             a.items[i] = cur[i];
             a.offs[i] = cur[i].wg_off;
         }
-        const bool big = 2 * rows * dst->n_layers * row_bytes >= kOrderMinBytes;
-        bool fits = true;                // tile numbers fit the order entries
-        for (const Item& c : cur) fits = fits && c.tiles < kOrderMaxItemTiles;
-        if (d_ws && fits && (force >= 0 ? force == 1 : big)) {
-            GatherOrderArgs o;
-            std::memset(&o, 0, sizeof(o));
-            o.bt = d_block_table;
-            o.order = static_cast<uint32_t*>(d_ws);
-            o.n_items = a.n_items;
-            o.n_tiles = a.n_tiles;
-            o.tile_rows = T;
-            o.block_size = pool.block_size;
-            o.bs_shift = pool.bs_shift;
-            o.n_blocks = pool.n_blocks;
-            o.bucket_shift = bucket_shift;
-            for (size_t i = 0; i < cur.size(); ++i) {
-                o.tile_off[i] = cur[i].wg_off;
-                o.slot0[i] = cur[i].a;
-            }
-            o.tile_off[cur.size()] = a.n_tiles;
-            hipError_t e = launch_gather_order(o, stream);
-            if (e != hipSuccess) return hip_fail(e);
-            a.order = o.order;
-        }
         hipError_t e = launch_gather(a, tile.pfi, tile.rs, dst->rope_dtype == KVR_F32, stream);
         cur.clear();
-        tiles = rows = 0;
+        tiles = 0;
         return e == hipSuccess ? KVR_OK : hip_fail(e);
     };
     for (int32_t i = 0; i < n; ++i) {
@@ -555,35 +503,9 @@ kvr_status gather_impl(const kvr_cache* dst, const int32_t* d_block_table, int32
         }
         it.wg_off = (int32_t)tiles;
         tiles += it.tiles;
-        rows += it.moved;
         cur.push_back(it);
     }
     return flush();
-}
-
-}  // namespace
-
-kvr_status kv_relocate_gather(const kvr_cache* dst, const int32_t* d_block_table, int32_t bt_len,
-                              const kvr_rows* entries, const int64_t* p_target, int32_t n,
-                              const kvr_lowrank* patch_rope, const kvr_lowrank* patch_pf,
-                              hipStream_t stream) {
-    return gather_impl(dst, d_block_table, bt_len, entries, p_target, n, patch_rope, patch_pf, nullptr, 0,
-                       stream);
-}
-
-size_t kvr_gather_workspace_bytes(const kvr_cache* dst, const kvr_rows* entries, int32_t n) {
-    if (!dst || n < 0 || (n > 0 && !entries)) return 0;
-    const int64_t tiles = gather_tiles(dst, entries, n);
-    return tiles < 0 ? 0 : round_up((size_t)std::max<int64_t>(tiles, 1) * 4);
-}
-
-kvr_status kv_relocate_gather_ws(const kvr_cache* dst, const int32_t* d_block_table, int32_t bt_len,
-                                 const kvr_rows* entries, const int64_t* p_target, int32_t n,
-                                 const kvr_lowrank* patch_rope, const kvr_lowrank* patch_pf,
-                                 void* d_workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!d_workspace) return KVR_E_WORKSPACE;
-    return gather_impl(dst, d_block_table, bt_len, entries, p_target, n, patch_rope, patch_pf, d_workspace,
-                       workspace_bytes, stream);
 }
 
 kvr_status kv_patch_lowrank(const kvr_cache* cache, const int32_t* d_block_table, int32_t bt_len, int32_t part,

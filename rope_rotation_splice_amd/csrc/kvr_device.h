@@ -66,16 +66,21 @@ __device__ __forceinline__ void rot_f32x4(v4u& lo, v4u& hi, const float2* cs) {
 // f = u - rint(u) in [-1/2, 1/2] is exact.  Only the reduced angle 2 pi f,
 // |2 pi f| <= pi, goes to float32 sincos, so the error stays ~2e-7 absolute at
 // any |shift| (a float32 product shift * theta would lose ~|shift| * 2^-24 rad).
-// The caller must __syncthreads() before reading `cs`.
-__device__ __forceinline__ void angle_table(float2* cs, const double* omega, int n_pairs,
-                                            int shift, int tid) {
+// The caller must __syncthreads() before reading `cs`.  angle_table_from
+// takes omega[tid] already loaded (so that a kernel can request it before
+// its row loads and not wait behind them).
+__device__ __forceinline__ void angle_table_from(float2* cs, double omega_tid, int n_pairs, int shift, int tid) {
     if (tid < n_pairs) {
-        const double u = (double)shift * omega[tid];
+        const double u = (double)shift * omega_tid;
         const double f = u - rint(u);
         float s, c;
         sincosf((float)(f * 6.283185307179586476925), &s, &c);
         cs[tid] = make_float2(c, s);
     }
+}
+__device__ __forceinline__ void angle_table(float2* cs, const double* omega, int n_pairs,
+                                            int shift, int tid) {
+    angle_table_from(cs, tid < n_pairs ? omega[tid] : 0.0, n_pairs, shift, tid);
 }
 
 // Workgroups reach the 8 XCDs round-robin (workgroup b runs on XCD b % 8,

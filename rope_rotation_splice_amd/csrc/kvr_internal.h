@@ -52,34 +52,11 @@ struct Item {
                           // gather: first tile of this item (per layer)
 };
 
-// Destination order of a gather launch.  Workgroups are numbered layer after
-// layer; within a layer the k-th one takes tile t of item i with
-// order[k] = t << 5 | i (kMaxItems = 32), or, without an order, the k-th
-// tile counted item after item (Item::wg_off is an item's first tile).  The
-// order kernel buckets the tiles by the physical block their first row lands
-// in, so the writes sweep each layer's pool in address order and the reads
-// (contiguous registry rows) take the scatter instead.
-constexpr int32_t kOrderMaxItemTiles = 1 << 26;   // longer items: launch unordered
-static_assert(kMaxItems <= 32, "order entries keep the item in 5 bits");
-constexpr int kOrderThreads = 1024;
-constexpr int kOrderBuckets = 16384;      // LDS counters, the last one for bad ids
-
-struct GatherOrderArgs {
-    const int32_t* bt;
-    uint32_t* order;           // [n_tiles]
-    int32_t n_items, n_tiles, tile_rows;
-    int32_t block_size, bs_shift, n_blocks;
-    int32_t bucket_shift;      // physical block id >> bucket_shift = bucket
-    int32_t tile_off[kMaxItems + 1];
-    int32_t slot0[kMaxItems];  // destination slot of each item's row 0
-};
-
 struct RelocArgs {
     Pool pool;
     const int32_t* bt;
     uint32_t* counters;   // splice: one ticket counter per (item, layer)
     uint32_t* flags;      // splice: one "sources read" flag per tile
-    const uint32_t* order;  // gather: tile visited k-th in each layer (null: tile k)
     int32_t n_items;
     int32_t tile_rows;
     uint32_t epoch;       // value a flag takes when set in this launch
@@ -257,7 +234,6 @@ static_assert(sizeof(RelocArgs) <= 4000, "relocation kernel arguments too large"
 // of two up to 16, rope_slots <= pf_slots); rope_f32 selects fp32 keys.
 hipError_t launch_splice(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
 hipError_t launch_gather(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
-hipError_t launch_gather_order(const GatherOrderArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 uint32_t read_and_clear_errors_relocate();
 // Patch kernel (patch.hip): fused gather + patch, or in-place patch.

@@ -65,25 +65,15 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
         for (int i = 1; i < kMaxItems; ++i) n += x >= A.offs[i] ? 1 : 0;
         return n;
     };
-    int it = MODE == kSplice ? item_at(bid) : 0;
-    int t, layer;
+    int it, t, layer;
     if (MODE == kGather) {
-        // layer after layer; in destination order the k-th workgroup of a
-        // layer takes the (tile, item) pair order[k] = tile << 5 | item
+        // layer after layer, tiles numbered item after item within a layer
         layer = bid / A.n_tiles;
         const int k = bid - layer * A.n_tiles;
-        if (A.order) {
-            const uint32_t v = A.order[k];
-            it = (int)(v & 31u);
-            t = (int)(v >> 5);
-            if (it >= A.n_items || t >= A.items[it].tiles) {   // a damaged order table
-                if (tid == 0) raise_error(KVR_DEV_BAD_TICKET);
-                return;
-            }
-        } else {
-            it = item_at(k);
-            t = k - A.offs[it];
-        }
+        it = item_at(k);
+        t = k - A.offs[it];
+    } else {
+        it = item_at(bid);
     }
     const Item& I = A.items[it];
     if (MODE == kSplice) {
@@ -123,21 +113,24 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
     // destination slot of row i of this tile's range
     const int dbase = (MODE == kGather) ? I.a : (is_move ? I.a + I.shift : I.b);
 
-    // ---- block-table lookups: one per row, staged in LDS -------------------
+    // ---- block-table lookups ----------------------------------------------
     // Vector-memory loads complete in order, so each row's block-table entry
     // is requested before any row data: using it later never waits behind a
-    // row load.  Source rows of a splice move live in the pool and need their
-    // entries before the data loads (one round trip + barrier); registry and
-    // stub rows are contiguous and load at once.
+    // row load.  The splice stages one entry per row in LDS; its source rows
+    // of a move live in the pool and need their entries before the data loads
+    // (one round trip + barrier).  Registry and stub rows are contiguous and
+    // load at once.
     auto bt_index = [&](int slot) { return P.bs_shift >= 0 ? (slot >> P.bs_shift) : slot / P.block_size; };
     auto in_block = [&](int slot) {
         return P.bs_shift >= 0 ? (slot & (P.block_size - 1)) : slot - (slot / P.block_size) * P.block_size;
     };
+    // theta_j / 2 pi of this thread's pair, requested ahead of every row load
+    const double om = rotate && tid < P.n_pairs ? A.omega[tid] : 0.0;
     const int sbase = I.a + r0;            // source slot of row 0 (splice move tiles)
     const int dslot0 = dbase + r0;
     const unsigned nb = (unsigned)P.n_blocks;
     int my_db = 0, my_sb = 0;
-    if (tid < nrows) {
+    if (MODE == kSplice && tid < nrows) {
         my_db = bt[bt_index(dslot0 + tid)];
         if (src_in_pool) my_sb = bt[bt_index(sbase + tid)];
     }
@@ -151,65 +144,101 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
         __syncthreads();
     }
 
+    // ---- this thread's items: 16-byte chunks of the position-free part and
+    // (lo, hi) chunk pairs of the rotary part, and the rows they belong to
     const int pfc = P.pf_chunks;
     const int pf_total = nrows * pfc;
     const int step_row = kThreads / pfc, step_c = kThreads % pfc;
     const int ri = P.rope_items;
     const int rp_total = nrows * ri;
-    const char* spf = src_in_pool ? P.pf + (int64_t)layer * P.pf_l : I.src.pf + (int64_t)layer * I.src.pf_l;
-    const char* srp = src_in_pool ? P.rp + (int64_t)layer * P.rp_l : I.src.rp + (int64_t)layer * I.src.rp_l;
-    v4u pv[PFI];
     int pf_row[PFI], pf_c[PFI];
     {
         int row = tid / pfc, c = tid - (tid / pfc) * pfc;
 #pragma unroll
         for (int k = 0; k < PFI; ++k) {
-            pf_row[k] = -1;
-            if (tid + k * kThreads < pf_total && (!src_in_pool || s_src_blk[row] >= 0)) {
-                pf_row[k] = row;
-                pf_c[k] = c;
-                const char* p = src_in_pool
-                    ? spf + (int64_t)s_src_blk[row] * P.pf_b + (int64_t)s_src_row[row] * P.pf_r
-                    : spf + (int64_t)(r0 + row) * I.src.pf_r;
-                pv[k] = ld16(p + c * 16);
-            }
+            const bool ok = tid + k * kThreads < pf_total && (!src_in_pool || s_src_blk[row] >= 0);
+            pf_row[k] = ok ? row : -1;
+            pf_c[k] = c;
             row += step_row; c += step_c;
             if (c >= pfc) { c -= pfc; ++row; }
         }
     }
-    v4u lo[RS], hi[RS];
     int rp_row[RS], rp_off[RS];
 #pragma unroll
     for (int k = 0; k < RS; ++k) {
         const int q = tid + k * kThreads;
         rp_row[k] = -1;
+        rp_off[k] = 0;
         if (q < rp_total) {
             const int row = q / ri, item = q - row * ri;
             if (!src_in_pool || s_src_blk[row] >= 0) {
                 const int head = item / P.half_chunks, hc = item - head * P.half_chunks;
                 rp_row[k] = row;
                 rp_off[k] = head * P.head_bytes + hc * 16;
-                const char* p = src_in_pool
-                    ? srp + (int64_t)s_src_blk[row] * P.rp_b + (int64_t)s_src_row[row] * P.rp_r
-                    : srp + (int64_t)(r0 + row) * I.src.rp_r;
-                lo[k] = ld16(p + rp_off[k]);
-                hi[k] = ld16(p + rp_off[k] + P.half_bytes);
             }
+        }
+    }
+    // Gather: every thread looks up the destination block of its own items'
+    // rows (lanes of a wave mostly share one entry), before its row loads, so
+    // the waves store independently, with no barrier between loads and stores.
+    int pf_db[PFI], rp_db[RS];
+    if (MODE == kGather) {
+#pragma unroll
+        for (int k = 0; k < PFI; ++k) pf_db[k] = pf_row[k] >= 0 ? bt[bt_index(dslot0 + pf_row[k])] : -1;
+#pragma unroll
+        for (int k = 0; k < RS; ++k) rp_db[k] = rp_row[k] >= 0 ? bt[bt_index(dslot0 + rp_row[k])] : -1;
+    }
+
+    // ---- row loads ---------------------------------------------------------
+    const char* spf = src_in_pool ? P.pf + (int64_t)layer * P.pf_l : I.src.pf + (int64_t)layer * I.src.pf_l;
+    const char* srp = src_in_pool ? P.rp + (int64_t)layer * P.rp_l : I.src.rp + (int64_t)layer * I.src.rp_l;
+    v4u pv[PFI];
+#pragma unroll
+    for (int k = 0; k < PFI; ++k) {
+        const int row = pf_row[k];
+        if (row >= 0) {
+            const char* p = src_in_pool
+                ? spf + (int64_t)s_src_blk[row] * P.pf_b + (int64_t)s_src_row[row] * P.pf_r
+                : spf + (int64_t)(r0 + row) * I.src.pf_r;
+            pv[k] = ld16(p + pf_c[k] * 16);
+        }
+    }
+    v4u lo[RS], hi[RS];
+#pragma unroll
+    for (int k = 0; k < RS; ++k) {
+        const int row = rp_row[k];
+        if (row >= 0) {
+            const char* p = src_in_pool
+                ? srp + (int64_t)s_src_blk[row] * P.rp_b + (int64_t)s_src_row[row] * P.rp_r
+                : srp + (int64_t)(r0 + row) * I.src.rp_r;
+            lo[k] = ld16(p + rp_off[k]);
+            hi[k] = ld16(p + rp_off[k] + P.half_bytes);
         }
     }
 
     // ---- while the rows are in flight: destination rows, angle table -------
-    if (tid < nrows) {
+    if (MODE == kSplice && tid < nrows) {
         const bool ok = (unsigned)my_db < nb;
         if (!ok) raise_error(KVR_DEV_BAD_BLOCK);
         s_dst_blk[tid] = ok ? my_db : -1;
         s_dst_row[tid] = in_block(dslot0 + tid);
     }
-    if (rotate) angle_table(s_cs, A.omega, P.n_pairs, I.shift, tid);
+    if (rotate) angle_table_from(s_cs, om, P.n_pairs, I.shift, tid);
 
-    if (MODE == kSplice) wait_loads();
-    __syncthreads();                     // destination rows and angle table ready;
-                                         // splice: every source row is in registers
+    if (MODE == kSplice) {
+        wait_loads();
+        __syncthreads();                 // destination rows and angle table ready;
+                                         // every source row is in registers
+    } else if (rotate) {
+        // the angle table is ready; when its writers and every rotation item
+        // sit in wave 0, a wave-level fence is enough
+        if (P.n_pairs <= 64 && rp_total <= 64) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        } else {
+            __syncthreads();
+        }
+    }
     if (MODE == kSplice && is_move && tid == 0)
         st_dev(A.flags + (I.wg_off + layer * I.tiles) + t, A.epoch);
 
@@ -268,20 +297,33 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
 
     // ---- stores -----------------------------------------------------------
     const int64_t dpf = (int64_t)layer * P.pf_l, drp = (int64_t)layer * P.rp_l;
+    auto dst_block = [&](int row, int db) __attribute__((always_inline)) -> int {
+        if (MODE == kSplice) return s_dst_blk[row];
+        if ((unsigned)db >= nb) { raise_error(KVR_DEV_BAD_BLOCK); return -1; }
+        return db;
+    };
+    auto dst_row = [&](int row) __attribute__((always_inline)) -> int {
+        return MODE == kSplice ? s_dst_row[row] : in_block(dslot0 + row);
+    };
 #pragma unroll
     for (int k = 0; k < PFI; ++k) {
         const int row = pf_row[k];
-        if (row >= 0 && s_dst_blk[row] >= 0)
-            st16(P.pf + dpf + (int64_t)s_dst_blk[row] * P.pf_b + (int64_t)s_dst_row[row] * P.pf_r + pf_c[k] * 16,
-                 pv[k]);
+        if (row >= 0) {
+            const int db = dst_block(row, MODE == kGather ? pf_db[k] : 0);
+            if (db >= 0)
+                st16(P.pf + dpf + (int64_t)db * P.pf_b + (int64_t)dst_row(row) * P.pf_r + pf_c[k] * 16, pv[k]);
+        }
     }
 #pragma unroll
     for (int k = 0; k < RS; ++k) {
         const int row = rp_row[k];
-        if (row >= 0 && s_dst_blk[row] >= 0) {
-            char* p = P.rp + drp + (int64_t)s_dst_blk[row] * P.rp_b + (int64_t)s_dst_row[row] * P.rp_r + rp_off[k];
-            st16(p, lo[k]);
-            st16(p + P.half_bytes, hi[k]);
+        if (row >= 0) {
+            const int db = dst_block(row, MODE == kGather ? rp_db[k] : 0);
+            if (db >= 0) {
+                char* p = P.rp + drp + (int64_t)db * P.rp_b + (int64_t)dst_row(row) * P.rp_r + rp_off[k];
+                st16(p, lo[k]);
+                st16(p + P.half_bytes, hi[k]);
+            }
         }
     }
 }
@@ -289,87 +331,6 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
 __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = 0u;
-}
-
-// Counting sort of a gather's tiles by the physical block (>> bucket_shift)
-// that each tile's first row lands in; ids outside the pool go last.  One
-// workgroup: LDS histogram, exclusive scan, then scatter through LDS atomics
-// (tiles sharing a bucket land in any order among themselves).  Each thread
-// looks up 8 tiles' block ids at a time so their loads overlap, and the
-// bucket of each of the first kOrderKeyCache tiles is kept in LDS for the
-// scatter pass.
-constexpr int kOrderKeyCache = 32768;
-
-__global__ __launch_bounds__(kOrderThreads) void gather_order_kernel(const GatherOrderArgs A) {
-    __shared__ uint32_t cnt[kOrderBuckets];
-    __shared__ uint16_t key[kOrderKeyCache];
-    __shared__ uint32_t wsum[kOrderThreads / 64];
-    __shared__ int32_t s_off[kMaxItems + 1], s_slot0[kMaxItems];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nbk = ((A.n_blocks - 1) >> A.bucket_shift) + 2;
-    for (int i = tid; i < nbk; i += kOrderThreads) cnt[i] = 0u;
-    if (tid <= A.n_items) s_off[tid] = A.tile_off[tid];
-    if (tid < A.n_items) s_slot0[tid] = A.slot0[tid];
-    __syncthreads();
-    // item of tile g (binary search over the tile offsets)
-    auto item_of = [&](int g) -> int {
-        int it = 0, hi = A.n_items - 1;
-        while (it < hi) {
-            const int mid = (it + hi + 1) >> 1;
-            if (g >= s_off[mid]) it = mid; else hi = mid - 1;
-        }
-        return it;
-    };
-    auto block_index = [&](int g) -> int {
-        const int it = item_of(g);
-        const int slot = s_slot0[it] + (g - s_off[it]) * A.tile_rows;
-        return A.bs_shift >= 0 ? (slot >> A.bs_shift) : slot / A.block_size;
-    };
-    auto to_bucket = [&](int id) -> uint32_t {
-        return (unsigned)id < (unsigned)A.n_blocks ? (uint32_t)(id >> A.bucket_shift) : (uint32_t)(nbk - 1);
-    };
-    constexpr int kBatch = 8;
-    for (int g0 = tid; g0 < A.n_tiles; g0 += kBatch * kOrderThreads) {
-        int id[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int g = g0 + u * kOrderThreads;
-            id[u] = g < A.n_tiles ? A.bt[block_index(g)] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int g = g0 + u * kOrderThreads;
-            if (g < A.n_tiles) {
-                const uint32_t b = to_bucket(id[u]);
-                if (g < kOrderKeyCache) key[g] = (uint16_t)b;
-                atomicAdd(&cnt[b], 1u);
-            }
-        }
-    }
-    __syncthreads();
-    // exclusive scan: each thread owns `per` consecutive counters
-    const int per = (nbk + kOrderThreads - 1) / kOrderThreads;
-    const int c0 = min(nbk, tid * per), c1 = min(nbk, c0 + per);
-    uint32_t own = 0;
-    for (int i = c0; i < c1; ++i) own += cnt[i];
-    uint32_t incl = own;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t v = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += v;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t base = incl - own;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
-    for (int i = c0; i < c1; ++i) { const uint32_t c = cnt[i]; cnt[i] = base; base += c; }
-    __syncthreads();
-    for (int g = tid; g < A.n_tiles; g += kOrderThreads) {
-        const uint32_t b = g < kOrderKeyCache ? (uint32_t)key[g] : to_bucket(A.bt[block_index(g)]);
-        const uint32_t pos = atomicAdd(&cnt[b], 1u);
-        const int it = item_of(g);
-        A.order[pos] = ((uint32_t)(g - s_off[it]) << 5) | (uint32_t)it;
-    }
 }
 
 template <int MODE, int PFI, int RS>
@@ -412,11 +373,6 @@ hipError_t launch_splice(const RelocArgs& a, int pfi, int rs, bool f32, hipStrea
 }
 hipError_t launch_gather(const RelocArgs& a, int pfi, int rs, bool f32, hipStream_t s) {
     return launch<kGather>(a, pfi, rs, f32, s);
-}
-
-hipError_t launch_gather_order(const GatherOrderArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(gather_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a);
-    return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {

@@ -134,34 +134,6 @@ def test_gather_validation_errors():
     assert gather(c, [rows(10, base=-(1 << 40))], [0]) == -2       # shift does not fit 32 bits
 
 
-def gather_ws(c, ents, pts, ws=FAKE, ws_bytes=1 << 20, bt_len=8):
-    lib = _abi.load()
-    n = len(ents)
-    E = (_abi.kvr_rows * max(1, n))(*ents)
-    P = (ctypes.c_int64 * max(1, n))(*pts)
-    return lib.kv_relocate_gather_ws(ctypes.byref(c), FAKE, bt_len, E, P, n, None, None, ws, ws_bytes, None)
-
-
-def test_gather_workspace_query_and_errors():
-    lib = _abi.load()
-    c = mla_cache()
-    E = (_abi.kvr_rows * 3)(rows(100), rows(0), rows(17))
-    # 1152-byte rows move in tiles of 8: ceil(100 / 8) + ceil(17 / 8) = 16 tiles, 4 bytes each, 256-rounded
-    assert lib.kvr_gather_workspace_bytes(ctypes.byref(c), E, 3) == 256
-    E2 = (_abi.kvr_rows * 1)(rows(500))
-    assert lib.kvr_gather_workspace_bytes(ctypes.byref(c), E2, 1) == 256      # 63 tiles
-    E3 = (_abi.kvr_rows * 1)(rows(512))
-    assert lib.kvr_gather_workspace_bytes(ctypes.byref(c), E3, 1) == 256      # 64 tiles = 256 bytes
-    assert lib.kvr_gather_workspace_bytes(None, E, 3) == 0
-    # the plain gather's argument errors come first, then the workspace's
-    assert gather_ws(c, [rows(10), rows(10)], [0, 5]) == -4
-    assert gather_ws(c, [rows(100)], [500]) == -2
-    assert gather_ws(c, [rows(10)], [0], ws=None) == -6
-    assert gather_ws(c, [rows(10)], [0], ws=FAKE + 4) == -6
-    assert gather_ws(c, [rows(100), rows(17)], [0, 200], ws_bytes=15 * 4) == -6
-    assert gather_ws(c, [], []) == 0                                        # nothing to do
-
-
 def lazy(dirs, lens, B=64, bt_stride=512, stubs=FAKE, freed=FAKE):
     lib = _abi.load()
     n = len(dirs)

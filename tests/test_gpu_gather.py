@@ -8,20 +8,8 @@ from tests import relocation_cases as rc
 
 pytestmark = pytest.mark.gpu
 
-# How the row mover visits its tiles: destination order forced on (a small
-# launch would not take it by default), the workspace entry point with the
-# order forced off, and the plain entry point (no workspace).
-ORDERS = ["sorted", "unsorted", "plain"]
 
-
-@pytest.fixture(params=ORDERS)
-def order(request, monkeypatch):
-    if request.param != "plain":
-        monkeypatch.setenv("KVR_GATHER_ORDER", "1" if request.param == "sorted" else "0")
-    return request.param
-
-
-def _run(lay, n_layers, block_size, n_dst_blocks, spare, chunks, keys, order="sorted"):
+def _run(lay, n_layers, block_size, n_dst_blocks, spare, chunks, keys):
     """chunks: list of (len, base_pos, p_target)."""
     import torch
     import rope_rotation_splice_amd as rrs
@@ -37,7 +25,7 @@ def _run(lay, n_layers, block_size, n_dst_blocks, spare, chunks, keys, order="so
         ents_h.append((epf, erp, base))
         tp, tr = rc.rows_to_device(lay, epf, erp)
         ents_d.append(rrs.Rows(tp, tr, base))
-    rrs.kv_relocate_gather(cache, d_bt, ents_d, [c[2] for c in chunks], ordered=order != "plain")
+    rrs.kv_relocate_gather(cache, d_bt, ents_d, [c[2] for c in chunks])
     torch.cuda.synchronize()
     after = rc.from_device(lay, cache)
     assert rrs.device_errors() == 0
@@ -45,35 +33,26 @@ def _run(lay, n_layers, block_size, n_dst_blocks, spare, chunks, keys, order="so
 
 
 @pytest.mark.parametrize("block_size", [1, 4, 64])
-def test_gather_small_mla(block_size, order):
+def test_gather_small_mla(block_size):
     n_dst = 2048 // block_size
     chunks = [(300, 60000, 5), (1, 0, 400), (0, 5, 500), (129, 700, 700), (1000, 31, 1040)]
-    _run(rc.MLA, 3, block_size, n_dst, 5, chunks, (block_size, 11), order)
+    _run(rc.MLA, 3, block_size, n_dst, 5, chunks, (block_size, 11))
 
 
-def test_gather_many_entries_multiple_launches(order):
-    # 40 entries: two launches, which share the order workspace in turn
+def test_gather_many_entries_multiple_launches():
     r = kvsynth.rng(12)
     chunks, pos = [], 3
     for i in range(40):
         ln = int(r.integers(1, 70))
         chunks.append((ln, int(r.integers(0, 100000)), pos))
         pos += ln + int(r.integers(0, 5))
-    _run(rc.MLA, 2, 16, (pos + 15) // 16, 4, chunks, (13,), order)
+    _run(rc.MLA, 2, 16, (pos + 15) // 16, 4, chunks, (13,))
 
 
-def test_gather_gqa_and_fp32(order):
+def test_gather_gqa_and_fp32():
     chunks = [(200, 30000, 64), (77, 0, 300), (333, 9000, 400)]
-    _run(rc.GQA, 2, 64, 12, 2, chunks, (14,), order)
-    _run(rc.MLA_F32, 2, 32, 24, 2, chunks, (15,), order)
-
-
-def test_gather_order_coarse_buckets(monkeypatch):
-    # a pool of 40,000 one-row blocks: more block ids than the order kernel
-    # has counters, so tiles are bucketed by block id >> 2
-    monkeypatch.setenv("KVR_GATHER_ORDER", "1")
-    chunks = [(5000, 77, 3), (9000, 123456, 6000), (1, 9, 15500), (4321, 0, 15600)]
-    _run(rc.MLA, 1, 1, 20000, 20000, chunks, (16,))
+    _run(rc.GQA, 2, 64, 12, 2, chunks, (14,))
+    _run(rc.MLA_F32, 2, 32, 24, 2, chunks, (15,))
 
 
 def test_gather_registry_workload_sampled():
