@@ -39,6 +39,12 @@ def test_gather_small_mla(block_size):
     _run(rc.MLA, 3, block_size, n_dst, 5, chunks, (block_size, 11))
 
 
+def test_gather_block_size_not_a_power_of_two():
+    # 24-row blocks: the kernel divides slots by the block size instead of shifting
+    chunks = [(300, 60000, 5), (1, 0, 400), (129, 700, 700), (250, 31, 1000)]
+    _run(rc.MLA, 3, 24, 1280 // 24, 5, chunks, (24, 11))
+
+
 def test_gather_many_entries_multiple_launches():
     r = kvsynth.rng(12)
     chunks, pos = [], 3

@@ -66,6 +66,12 @@ def test_gqa_gather_patch_ranks(rank):
     _run(rc.GQA, 2, 16, 16, 2, chunks, rank, 1.0, (22, rank))
 
 
+def test_gqa_gather_patch_block_size_not_a_power_of_two():
+    # 24-row blocks take the register-tiled kernel, which divides slots by the block size
+    chunks = [(96, 30000, 5, None), (17, 0, 200, None), (130, 9000, 230, None)]
+    _run(rc.GQA, 2, 24, 16, 2, chunks, 16, 1.0, (25,))
+
+
 def test_gather_patch_keys_only_and_zero_shift():
     chunks = [(40, 40, 40, None), (70, 1000, 100, None)]     # first entry: delta = 0
     _run(rc.GQA, 2, 64, 4, 1, chunks, 16, 1.0, (23,), patch_pf=False)

@@ -69,6 +69,21 @@ def test_splice_delta_sweep_mla(block_size, delta):
     _run(rc.MLA, 2, block_size, bps, seqs, (block_size, delta + 1000))
 
 
+@pytest.mark.parametrize("delta", [-1, -30, -700, 2, 25, 130])
+def test_splice_block_size_not_a_power_of_two(delta):
+    # 24-row blocks: the kernels divide slots by the block size instead of shifting
+    cap = 24 * 43
+    seqs = []
+    for i, n in enumerate([1000, 801, 977]):
+        n = min(n, cap - max(delta, 0))
+        s_len = 50 + 7 * i
+        r_len = max(0, s_len + delta)
+        s_len = r_len - delta
+        s0 = min(90 + 31 * i, n - s_len)
+        seqs.append((n, s0, s0 + s_len, r_len, 0))
+    _run(rc.MLA, 2, 24, 43, seqs, (24, delta + 2000))
+
+
 def test_splice_gqa_layout():
     seqs = [(900, 10, 300, 17, 0), (1024 - 40, 500, 510, 50, 0), (513, 0, 513, 5, 0)]
     _run(rc.GQA, 2, 16, 64, seqs, (77,))
