@@ -32,6 +32,13 @@
  *   (0 <= id < n_blocks).  A bad entry is never dereferenced: the affected
  *   rows are skipped and a bit is set in the device error word, read (and
  *   cleared) with kvr_device_errors().
+ * - Debug checks (environment variable KVR_DEBUG_CHECKS=1): leyline_splice
+ *   and kv_relocate_gather first copy the block tables to the host, waiting
+ *   for `stream`.  They return KVR_E_OVERLAP if a block the call would write
+ *   is named by more than one logical block of the call's sequences (a
+ *   splice's sequence holds its first max(N, new_len) slots), and
+ *   KVR_E_RANGE for such a block id outside the pool, before enqueuing
+ *   anything.  Off by default: the copy synchronizes the stream.
  * - RoPE (the reading taken here; the pages give no formula): within each
  *   head of rotary dimension d, pairs (x_j, x_{j+d/2}), j < d/2, rotate by
  *   phi = p * theta_j with theta_j = base^(-2j/d) (or the caller's inv_freq):

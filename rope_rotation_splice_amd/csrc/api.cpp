@@ -6,6 +6,9 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <set>
+#include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "../../include/kvreloc.h"
@@ -149,6 +152,52 @@ struct SplicePlan {
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Optional ownership checks (environment KVR_DEBUG_CHECKS=1).  The host
+// cannot see the block tables, so the callers' preconditions -- every block a
+// call writes is held by that one logical block of one sequence, and no block
+// id is out of range -- are otherwise only caught (in part) by the kernels'
+// device error bits.  With the checks on, the tables are copied to the host,
+// which waits for the stream, before anything is enqueued.
+bool debug_checks() {
+    const char* e = std::getenv("KVR_DEBUG_CHECKS");
+    return e && std::atoi(e) != 0;
+}
+
+// Per table: the logical blocks [0, live) the sequence holds, and the ranges
+// [lo, hi) of logical blocks the call writes.
+struct TableUse {
+    int64_t live = 0;
+    std::vector<std::pair<int64_t, int64_t>> written;
+};
+
+kvr_status check_ownership(const int32_t* d_tables, int32_t stride, const std::vector<TableUse>& use,
+                           int32_t n_blocks, hipStream_t stream) {
+    if (use.empty()) return KVR_OK;
+    std::vector<int32_t> h((size_t)use.size() * stride);
+    hipError_t e = hipMemcpyAsync(h.data(), d_tables, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e);
+    std::unordered_map<int32_t, int> holders;    // physical block -> logical blocks naming it
+    std::vector<int32_t> written;
+    for (size_t b = 0; b < use.size(); ++b) {
+        std::set<int64_t> logical;
+        for (int64_t k = 0; k < use[b].live; ++k) logical.insert(k);
+        for (const auto& r : use[b].written)
+            for (int64_t k = r.first; k < r.second; ++k) {
+                logical.insert(k);
+                written.push_back(h[b * stride + k]);
+            }
+        for (int64_t k : logical) {
+            const int32_t id = h[b * stride + k];
+            if (id < 0 || id >= n_blocks) return KVR_E_RANGE;
+            ++holders[id];
+        }
+    }
+    for (int32_t id : written)
+        if (holders[id] > 1) return KVR_E_OVERLAP;
+    return KVR_OK;
+}
 
 kvr_status plan_splice(const kvr_cache* c, int32_t bt_stride, int32_t n_seq, const int64_t* seq_lens,
                        const kvr_directive* dirs, const kvr_rows* stubs, SplicePlan& pl) {
@@ -371,6 +420,19 @@ kvr_status leyline_splice(const kvr_cache* cache, const int32_t* d_block_tables,
     if (!pl.launches.empty()) {
         if (!d_ws || (reinterpret_cast<uintptr_t>(d_ws) % kAlign) || ws_bytes < need) return KVR_E_WORKSPACE;
     }
+    if (debug_checks()) {
+        // a sequence holds the blocks of max(N, new_len) slots and writes [s_start, new_len)
+        const int64_t B = cache->block_size;
+        std::vector<TableUse> use(n_seq);
+        for (int32_t b = 0; b < n_seq; ++b) {
+            const int64_t n = seq_lens[b], nl = pl.new_lens[b];
+            use[b].live = (std::max(n, nl) + B - 1) / B;
+            if (dirs[b].mode == KVR_AMORTIZE && nl > dirs[b].s_start)
+                use[b].written.push_back({dirs[b].s_start / B, (nl + B - 1) / B});
+        }
+        st = check_ownership(d_block_tables, bt_stride, use, cache->n_blocks, stream);
+        if (st != KVR_OK) return st;
+    }
     for (int32_t b = 0; b < n_seq; ++b) new_lens[b] = pl.new_lens[b];
     for (auto& L : pl.launches) {
         RelocArgs a;
@@ -427,6 +489,14 @@ kvr_status kv_relocate_gather(const kvr_cache* dst, const int32_t* d_block_table
     std::sort(rng.begin(), rng.end());
     for (size_t i = 1; i < rng.size(); ++i)
         if (rng[i].first < rng[i - 1].second) return KVR_E_OVERLAP;
+    if (debug_checks()) {
+        // the destination blocks must be distinct physical blocks
+        const int64_t B = dst->block_size;
+        std::vector<TableUse> use(1);
+        for (const auto& r : rng) use[0].written.push_back({r.first / B, (r.second + B - 1) / B});
+        st = check_ownership(d_block_table, bt_len, use, dst->n_blocks, stream);
+        if (st != KVR_OK) return st;
+    }
     bool any_patch = false;
     for (int32_t i = 0; i < n; ++i) {
         if (patch_rope && patch_rope[i].rank) any_patch = true;

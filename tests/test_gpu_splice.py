@@ -225,3 +225,40 @@ def test_splice_after_decode_on_the_same_stream():
     torch.cuda.synchronize()
     assert rrs.device_errors() == 0
     _run(rc.MLA, 2, 4, 16, [(64, 10, 30, 5, 0), (60, 0, 2, 4, 0)], keys=(12,))
+
+
+def test_debug_checks_refuse_shared_or_bad_written_blocks(monkeypatch):
+    """With KVR_DEBUG_CHECKS=1 the splice and the gather refuse, before
+    touching memory, a call whose written blocks are shared with another
+    logical block (KVR_E_OVERLAP) or lie outside the pool (KVR_E_RANGE); a
+    valid call still matches the oracle."""
+    import torch
+    import rope_rotation_splice_amd as rrs
+    monkeypatch.setenv("KVR_DEBUG_CHECKS", "1")
+    lay, B, n_blocks = rc.MLA, 16, 12
+    pf, rp = rc.random_image(lay, 1, n_blocks * B, (31,))
+    cache, keep = rc.to_device(lay, pf, rp, n_blocks, B)
+    lens = [60, 60]
+    dirs = [(20, 30, 5, 0), (0, 0, 0, 0)]          # sequence 0 writes slots [20, 55): blocks 1..3
+    cases = [
+        (np.array([[0, 1, 2, 3], [4, 5, 6, 2]], np.int32), -4),    # block 2 also held by sequence 1
+        (np.array([[0, 1, 2, 1], [4, 5, 6, 7]], np.int32), -4),    # block 1 held twice by sequence 0
+        (np.array([[0, 1, 99, 3], [4, 5, 6, 7]], np.int32), -2),   # outside the pool
+    ]
+    for bt, code in cases:
+        with pytest.raises(rrs.KVRError) as err:
+            rrs.leyline_splice(cache, torch.from_numpy(bt).cuda(), lens, dirs)
+        assert err.value.status == code
+    # the gather: two entries whose destination blocks alias one physical block
+    e = torch.zeros((1, 20, 576), dtype=torch.bfloat16, device="cuda")
+    ents = [rrs.Rows(e[..., :512], e[..., 512:], 0), rrs.Rows(e[..., :512], e[..., 512:], 0)]
+    with pytest.raises(rrs.KVRError) as err:
+        rrs.kv_relocate_gather(cache, torch.tensor([0, 1, 2, 1], dtype=torch.int32, device="cuda"), ents, [0, 40])
+    assert err.value.status == -4
+    torch.cuda.synchronize()
+    after = rc.from_device(lay, cache)
+    assert np.array_equal(after[0].view(np.uint16), pf.view(np.uint16))
+    assert np.array_equal(after[1].view(np.uint16), rp.view(np.uint16))
+    assert rrs.device_errors() == 0
+    # a valid batch passes the checks and the oracle
+    _run(rc.MLA, 2, 16, 16, [(250, 20, 30, 5, 0), (200, 64, 70, 40, 0), (100, 10, 50, 0, 1)], (32,))
