@@ -900,6 +900,19 @@ def main():
     if rrs.device_errors():
         raise SystemExit("device error flags set during the timed steps")
 
+    # Spread of single steps, outside the timed region: up to 20 more steps,
+    # each between its own events (host enqueue gaps included).
+    per_us = []
+    for _ in range(min(20, args.steps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        wl.step()
+        e1.record(stream)
+        e1.synchronize()
+        per_us.append(e0.elapsed_time(e1) * 1e3)
+    if rrs.device_errors():
+        raise SystemExit("device error flags set during the per-step timing")
+
     launches = args.steps * wl.launches
     kernel_s = gpu_s / launches
     bytes_per_launch = wl.bytes / wl.launches
@@ -931,6 +944,8 @@ def main():
                      "avg_launch_us": kernel_s * 1e6},
         "cpu_baseline": cpu,
     }
+    if per_us:
+        out["step_us"] = {"median": float(np.median(per_us)), "min": float(min(per_us)), "n": len(per_us)}
     out.update(extra)
     if hasattr(wl, "extra"):
         out.update(wl.extra())
