@@ -11,6 +11,7 @@ c_vp, c_size = ctypes.c_void_p, ctypes.c_size_t
 
 KVR_OK = 0
 KVR_FORGET_NEEDS_PREFILL = 1
+KVR_E_WORKSPACE = -6
 KVR_AMORTIZE, KVR_FORGET = 0, 1
 KVR_BF16, KVR_F32 = 0, 1
 KVR_DEV_BAD_BLOCK, KVR_DEV_SPIN_LIMIT, KVR_DEV_BAD_TICKET, KVR_DEV_RANGE, KVR_DEV_BAD_TOKEN = 1, 2, 4, 8, 16

@@ -14,7 +14,7 @@ import torch
 
 from . import _abi
 from ._abi import (kvr_cdc_params, KVR_AMORTIZE, KVR_BF16, KVR_F32, KVR_FORGET, KVR_FORGET_NEEDS_PREFILL,  # noqa: F401
-                   KVR_OK, kvr_cache, kvr_directive, kvr_lowrank, kvr_part, kvr_rows)
+                   KVR_E_WORKSPACE, KVR_OK, kvr_cache, kvr_directive, kvr_lowrank, kvr_part, kvr_rows)
 
 
 class KVRError(RuntimeError):
@@ -115,12 +115,12 @@ class LowRank:
 _workspaces = {}
 
 
-def _workspace(nbytes, device, kind):
+def _workspace(nbytes, device, kind, stream=None):
     """A workspace per (kind, device, stream).  Kinds never share memory: the
     splice's must stay zero-filled between calls (each call leaves it so),
     the decode's holds split partials."""
-    key = (kind, device.index if device.index is not None else torch.cuda.current_device(),
-           torch.cuda.current_stream().cuda_stream)
+    stream = stream if stream is not None else torch.cuda.current_stream()
+    key = (kind, device.index if device.index is not None else torch.cuda.current_device(), stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -201,11 +201,24 @@ def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, worksp
         for i, s in enumerate(stubs):
             if s is not None:
                 stub_arr[i] = s.c()
-    need = lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens.p, dirs.p)
-    ws = workspace if workspace is not None else _workspace(need, cache.pf.device, "splice")
-    st = lib.leyline_splice(ctypes.byref(cache.c), block_tables.data_ptr(), int(block_tables.stride(0)), n,
-                            lens.p, dirs.p, stub_arr, out.p, ws.data_ptr(), ws.numel() * ws.element_size(),
-                            _stream_handle())
+    stream = torch.cuda.current_stream()
+    handle = ctypes.c_void_p(stream.cuda_stream)
+
+    def call(ws):
+        return lib.leyline_splice(ctypes.byref(cache.c), block_tables.data_ptr(), int(block_tables.stride(0)), n,
+                                  lens.p, dirs.p, stub_arr, out.p, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                  handle)
+
+    if workspace is not None:
+        st = call(workspace)
+    else:
+        # The cached workspace usually fits; a call it does not fit fails
+        # validation before anything is enqueued, and is repeated once with
+        # a workspace of the queried size.
+        st = call(_workspace(0, cache.pf.device, "splice", stream))
+        if st == KVR_E_WORKSPACE:
+            need = lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens.p, dirs.p)
+            st = call(_workspace(need, cache.pf.device, "splice", stream))
     _check("leyline_splice", st)
     return out.values(n), st
 
