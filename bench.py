@@ -321,7 +321,8 @@ class SpliceLazy:
         s0 = d[:, 0] // B * B
         s1 = -(-d[:, 1] // B) * B
         rl = -(-d[:, 2] // B) * B
-        self.dirs = [(int(a), int(b), int(c), 0) for a, b, c in zip(s0, s1, rl)]
+        # host inputs as a serving loop keeps them: int64 arrays, not Python lists
+        self.dirs = np.stack([s0, s1, rl, np.zeros_like(s0)], axis=1).astype(np.int64)
         n = self.w.seq_lens.astype(np.int64)
         self.slots = int((n - s1).sum())
         nb_old = -(-n // B)
@@ -333,7 +334,8 @@ class SpliceLazy:
         self.launches = 1
         self.config = {"workload": "leyline_lazy_splices", "sequences": self.w.n_seq, "slots": self.w.capacity,
                        "block_size": B, "directives": "batched-splice draws widened to block boundaries",
-                       "slots_per_step": self.slots, "kv_bytes_moved": 0}
+                       "slots_per_step": self.slots, "kv_bytes_moved": 0,
+                       "host_inputs": "directives [64, 4] and lengths [64] as int64 numpy arrays"}
 
     def setup(self):
         import torch
@@ -341,9 +343,9 @@ class SpliceLazy:
         w = self.w
         self.bt = torch.from_numpy(w.block_tables.copy()).cuda()
         self.pend = torch.zeros_like(self.bt)
-        n_stub = sum(d[2] // w.block_size for d in self.dirs)
+        n_stub = int((self.dirs[:, 2] // w.block_size).sum())
         self.stubs = torch.arange(w.n_blocks, w.n_blocks + n_stub, dtype=torch.int32, device="cuda")
-        self.lens = w.seq_lens.tolist()
+        self.lens = w.seq_lens.astype(np.int64)
         self.rrs = rrs
 
     def step(self):
@@ -358,7 +360,7 @@ class SpliceLazy:
         rows, spent, units = 0, 0.0, 0
         stub = np.arange(64)
         while spent < budget_s:
-            for b, d in enumerate(self.dirs):
+            for b, d in enumerate(self.dirs.tolist()):
                 t0 = time.perf_counter()
                 olazy.lazy_splice_tables(w.block_tables[b], pend, int(w.seq_lens[b]), d[0], d[1], d[2], B,
                                          stub[: d[2] // B])
