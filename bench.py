@@ -418,10 +418,11 @@ class GatherLazy:
             n = int(self.nb[c])
             self.ents.append(rrs.LazyEntry(0, ids[off:off + n], n * B, int(w.base_pos[c]), int(self.tgt[c])))
             off += n
+        self.batch = rrs.LazyBatch(self.ents)       # packed once, as a caller placing them repeatedly would
         self.rrs = rrs
 
     def step(self):
-        self.rrs.kv_relocate_gather_lazy(self.bt, self.pend, self.w.block_size, self.ents)
+        self.rrs.kv_relocate_gather_lazy(self.bt, self.pend, self.w.block_size, self.batch)
 
     def cpu_baseline(self, budget_s):
         from oracle import lazy as olazy

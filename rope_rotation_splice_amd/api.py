@@ -286,14 +286,31 @@ class LazyEntry:
     p_target = property(lambda self: self._target)
 
 
+class LazyBatch:
+    """LazyEntry objects packed once into the host array the library reads,
+    for callers that place the same entries repeatedly (entries are
+    immutable, and the batch keeps its own tuple of them)."""
+    __slots__ = ("entries", "_host", "_totals")
+
+    def __init__(self, entries):
+        self.entries = tuple(entries)
+        arr = np.array([e._row for e in self.entries] or [(0, 0, 0, 0, 0, 0, 0)], dtype=_LAZY_DT)
+        self._host = _HostArray(arr, _abi.kvr_lazy_entry)
+        self._totals = {}          # block size -> checked block count
+
+    def __len__(self):
+        return len(self.entries)
+
+
 def kv_relocate_gather_lazy(block_tables, pending_delta, block_size, entries):
     """Registry entries placed at block-aligned targets as edits of the block
     table and of the per-block pending shifts (no KV bytes move); decode with
     mla_decode_rotate_on_read applies the shift on read.
 
     block_tables, pending_delta: int32 device tensors [n_seq, bt_stride],
-    edited in place.  Returns (replaced int32 device tensor: the ids each
-    entry's logical blocks held before, entry after entry; status).
+    edited in place.  entries: a list of LazyEntry, or a LazyBatch of them.
+    Returns (replaced int32 device tensor: the ids each entry's logical
+    blocks held before, entry after entry; status).
     """
     lib = _abi.load()
     for t in (block_tables, pending_delta):
@@ -301,16 +318,25 @@ def kv_relocate_gather_lazy(block_tables, pending_delta, block_size, entries):
             raise ValueError("block_tables and pending_delta must be int32 [n_seq, blocks] with unit last stride")
     if pending_delta.shape != block_tables.shape or pending_delta.stride(0) != block_tables.stride(0):
         raise ValueError("pending_delta must match block_tables in shape and row stride")
-    n = len(entries)
-    total = 0
+    batch = entries if isinstance(entries, LazyBatch) else None
+    items = batch.entries if batch is not None else entries
+    n = len(items)
     B = int(block_size)
-    for e in entries:
-        nb = -(-e._len // B) if e._len > 0 else 0
-        if e._n_blocks < nb or (e._n_pend is not None and e._n_pend < nb):
-            raise ValueError("entry blocks and pend need ceil(len / block_size) ids")
-        total += nb
-    arr = np.array([e._row for e in entries] or [(0, 0, 0, 0, 0, 0, 0)], dtype=_LAZY_DT)
-    ents = _HostArray(arr, _abi.kvr_lazy_entry)
+    total = batch._totals.get(B) if batch is not None else None
+    if total is None:
+        total = 0
+        for e in items:
+            nb = -(-e._len // B) if e._len > 0 else 0
+            if e._n_blocks < nb or (e._n_pend is not None and e._n_pend < nb):
+                raise ValueError("entry blocks and pend need ceil(len / block_size) ids")
+            total += nb
+        if batch is not None:
+            batch._totals[B] = total
+    if batch is not None:
+        ents = batch._host
+    else:
+        arr = np.array([e._row for e in items] or [(0, 0, 0, 0, 0, 0, 0)], dtype=_LAZY_DT)
+        ents = _HostArray(arr, _abi.kvr_lazy_entry)
     replaced = torch.empty(max(1, total), dtype=torch.int32, device=block_tables.device)
     st = lib.kv_relocate_gather_lazy(int(block_size), block_tables.data_ptr(), pending_delta.data_ptr(),
                                      int(block_tables.stride(0)), int(block_tables.shape[0]), ents.p, n,

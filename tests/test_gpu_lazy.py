@@ -315,3 +315,25 @@ def test_lazy_gather_workload_full_size():
     assert st == 0
     assert (bt_d.cpu().numpy() == bt2).all() and (pd_d.cpu().numpy() == pd2).all()
     assert list(rep) == list(rep2)
+
+
+def test_lazy_gather_packed_batch_matches_the_oracle_twice():
+    """A LazyBatch (entries packed once) gives the oracle's tables, and the
+    same batch placed again on fresh tables gives them again."""
+    import torch
+    import rope_rotation_splice_amd as rrs
+    B, bt_stride, n_seq = 16, 24, 3
+    bt, pend, ents, _ = _lazy_gather_case(B, bt_stride, n_seq, (41,))
+    want_bt, want_pd, want_rep = _lazy_gather_oracle(bt, pend, B, ents)
+    objs = [rrs.LazyEntry(s, torch.from_numpy(bl).cuda(), ln, base, p,
+                          None if own is None else torch.from_numpy(own).cuda())
+            for s, bl, own, ln, base, p in ents]
+    batch = rrs.LazyBatch(objs)
+    for _ in range(2):
+        bt_d, pd_d = torch.from_numpy(bt.copy()).cuda(), torch.from_numpy(pend.copy()).cuda()
+        replaced, st = rrs.kv_relocate_gather_lazy(bt_d, pd_d, B, batch)
+        torch.cuda.synchronize()
+        assert st == 0 and rrs.device_errors() == 0
+        assert np.array_equal(bt_d.cpu().numpy(), want_bt)
+        assert np.array_equal(pd_d.cpu().numpy(), want_pd)
+        assert np.array_equal(replaced.cpu().numpy(), want_rep)
