@@ -5,21 +5,24 @@
 
 A step is one call of the relocation path over one batch of synthetic,
 seeded input that is resident in HBM before the timed region starts.  The
-default workload is the registry gather: 32 registry entries (lengths
-U{256..2048}, base positions U{0..60000}) of a 61-layer MLA cache
-(cKV 512 + k_r 64, bf16) gathered into one 40960-slot paged sequence with
-64-slot blocks and a random block table, each entry rotated by its own
-delta = p_target - base_pos.  Other workloads: ``splice`` (one 4096-slot
-contiguous sequence, [1000, 1800) -> 16 stub slots), ``splice_batched``
-(64 x 32768 slots x 61 layers, one directive per sequence), ``gqa_patch``
-(GQA relocation with a rank-16 patch), ``decode`` (rotate-on-read MLA
-decode, batch 32 x 32768 tokens x 128 heads; ``decode_zero_delta`` is the
-same with every pending shift 0) and ``copy`` (a plain device copy).
+default workload is the batched in-place splice: 64 sequences of 32768 slots
+of a 61-layer MLA cache (cKV 512 + k_r 64, bf16; 147 GB resident) in 64-slot
+blocks under random block tables, one AMORTIZE directive per sequence (|S|
+U{64..8192}, |R| U{8..64}, random s_start): every downstream row moves by
+Delta = |R| - |S| and its k_r is rotated by R(Delta), then the prefilled stub
+rows are copied in.  Other workloads: ``gather`` (32 registry entries
+gathered into one 40960-slot paged sequence, each rotated by its own
+delta = p_target - base_pos), ``splice`` (one 4096-slot contiguous sequence,
+[1000, 1800) -> 16 stub slots), ``gqa_patch`` (GQA relocation with a rank-16
+patch), ``decode`` (rotate-on-read MLA decode, batch 32 x 32768 tokens x 128
+heads; ``decode_zero_delta`` is the same with every pending shift 0), the
+lazy and keying workloads, patch formation, and ``copy`` (a plain device
+copy).
 
 Prints one JSON line: slots relocated per second (a slot = one token
 position of one sequence, all layers), the roofline of the relocation
 kernel (algorithmic bytes / kernel time vs 8 TB/s), and the CPU oracle timed
-on a bounded sample of the same workload.
+on the host's cores on a bounded sample of the same workload.
 """
 
 import argparse
@@ -85,6 +88,65 @@ def stored_traffic(kernel, workload):
     return rec.get("traffic_bytes_per_launch")
 
 
+# ------------------------------------------------------------ CPU oracle ---
+#
+# The oracle runs on the host's cores before the GPU is touched: a pool of
+# worker processes (one per core of this process's CPU set, at most 16, the
+# host share of one GPU), each with single-threaded BLAS.  Worker w takes the
+# workload's oracle slabs w, w + n, w + 2n, ... (cycling when the workload has
+# fewer), regenerates each slab's inputs untimed and times only the oracle
+# call, until its own oracle time reaches the budget.  The reported rate is
+# the sum of the workers' rates, which ran side by side.
+
+def oracle_workers():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _oracle_worker(spec):
+    name, w, n, budget = spec
+    wl = WORKLOADS[name]()
+    total = wl.oracle_slabs()
+    units, spent, gen, slabs = 0, 0.0, 0.0, 0
+    i = w
+    while spent < budget:
+        u, s, g = wl.oracle_slab(i % total)
+        units += u
+        spent += s
+        gen += g
+        slabs += 1
+        i += n
+    return units, spent, gen, slabs
+
+
+def oracle_baseline(name, budget_s, unit, what):
+    """Run ``name``'s oracle slabs in a process pool; returns the cpu_baseline record."""
+    import multiprocessing as mp
+    n = oracle_workers()
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        t0 = time.perf_counter()
+        with mp.get_context("spawn").Pool(n) as pool:
+            res = pool.map(_oracle_worker, [(name, w, n, budget_s) for w in range(n)])
+        wall = time.perf_counter() - t0
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    units = sum(r[0] for r in res)
+    rate = sum(r[0] / r[1] for r in res if r[1] > 0)
+    slabs = sum(r[3] for r in res)
+    return {"value": rate, "unit": unit, "cores": n, "kind": "oracle",
+            "sample": f"{slabs} {what} ({units:.0f} {unit.split('/')[0]}) on {n} worker processes with "
+                      f"single-threaded BLAS, {budget_s:g} s of oracle time each; the rate is the sum of the "
+                      f"workers' rates; input generation excluded ({sum(r[2] for r in res):.1f} s in all); "
+                      f"pool wall time {wall:.1f} s",
+            "oracle_s": sum(r[1] for r in res)}
+
+
 # --------------------------------------------------------------- workloads ---
 
 class Gather:
@@ -126,34 +188,29 @@ class Gather:
     def step(self):
         self.rrs.kv_relocate_gather(self.cache, self.bt, self.ents, self.pt)
 
-    def cpu_baseline(self, budget_s):
-        """The oracle's gather on whole (entry, layer) slabs until the budget is spent."""
+    oracle_what = "(entry, layer) slabs of the same draw, gathered and rotated (numpy fp64)"
+
+    def oracle_slabs(self):
+        return len(self.w.lens) * self.w.shape.n_layers
+
+    def oracle_slab(self, i):
+        """One (entry, layer) slab through the oracle's gather: (slots, oracle s, generation s)."""
         import kvsynth
         from oracle import gather as og, rope as orope
-        th = orope.inv_freq(64, 10000.0)
         w = self.w
-        rows = 0
-        spent = 0.0
-        slabs = 0
-        for i, ln in enumerate(w.lens):
-            r = kvsynth.rng(2, 9, i)
-            d = og.chunk_delta(int(w.p_target[i]), int(w.base_pos[i]))
-            for l in range(w.shape.n_layers):
-                pf = kvsynth.bf16_normal(r, (int(ln), 512))
-                rp = kvsynth.bf16_normal(r, (int(ln), 64))
-                t0 = time.perf_counter()
-                og.relocate_rows(pf, rp, d, 1, 64, th)
-                spent += time.perf_counter() - t0
-                rows += int(ln)
-                slabs += 1
-                if spent >= budget_s:
-                    break
-            if spent >= budget_s:
-                break
-        slots = rows / w.shape.n_layers
-        return {"value": slots / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
-                "sample": f"{slabs} (entry, layer) slabs = {rows} layer-rows of the same draw "
-                          f"({slots:.0f} slots), generation excluded, numpy fp64, one process"}
+        L = w.shape.n_layers
+        e, l = i // L, i % L
+        ln = int(w.lens[e])
+        t0 = time.perf_counter()
+        r = kvsynth.rng(2, 9, e, l)
+        pf = kvsynth.bf16_normal(r, (ln, 512))
+        rp = kvsynth.bf16_normal(r, (ln, 64))
+        th = orope.inv_freq(64, 10000.0)
+        d = og.chunk_delta(int(w.p_target[e]), int(w.base_pos[e]))
+        t1 = time.perf_counter()
+        og.relocate_rows(pf, rp, d, 1, 64, th)
+        t2 = time.perf_counter()
+        return ln / L, t2 - t1, t1 - t0
 
 
 class Splice:
@@ -162,7 +219,6 @@ class Splice:
 
     def __init__(self):
         import kvsynth
-        from oracle import splice as osplice  # noqa: F401  (bookkeeping only via the library)
         self.w = kvsynth.single_splice()
         d = self.w.directives[0]
         moved = 4096 - int(d[1])
@@ -212,9 +268,15 @@ class Splice:
         del flush
         return {"latency_us": out}
 
-    def cpu_baseline(self, budget_s):
+    oracle_what = "whole single-sequence splices (numpy fp64)"
+
+    def oracle_slabs(self):
+        return 1
+
+    def oracle_slab(self, i):
         import kvsynth
         from oracle import splice as osplice, rope as orope
+        t0 = time.perf_counter()
         th = orope.inv_freq(64, 10000.0)
         d = self.w.directives[0]
         p = osplice.plan(4096, int(d[0]), int(d[1]), int(d[2]), 0)
@@ -223,14 +285,13 @@ class Splice:
         rp = kvsynth.bf16_normal(r, (4096, 64))
         spf = kvsynth.bf16_normal(r, (16, 512))
         srp = kvsynth.bf16_normal(r, (16, 64))
-        n, spent = 0, 0.0
-        while spent < min(budget_s, 3.0):
-            t0 = time.perf_counter()
+        t1 = time.perf_counter()
+        n = 0
+        while n == 0 or time.perf_counter() - t1 < 0.5:
             osplice.splice_sequence(p, pf, rp, spf, srp, 1, 64, th)
-            spent += time.perf_counter() - t0
             n += 1
-        return {"value": n * self.slots / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
-                "sample": f"{n} repetitions of the whole splice, numpy fp64, one process"}
+        t2 = time.perf_counter()
+        return n * self.slots, t2 - t1, t1 - t0
 
 
 class SpliceBatched:
@@ -276,31 +337,31 @@ class SpliceBatched:
     def step(self):
         self.rrs.leyline_splice(self.cache, self.bt, self.lens, self.dirs, self.stubs)
 
-    def cpu_baseline(self, budget_s):
+    oracle_what = "(sequence, layer) slabs of the same directives, spliced and rotated (numpy fp64)"
+
+    def oracle_slabs(self):
+        return self.w.n_seq * self.w.shape.n_layers
+
+    def oracle_slab(self, i):
+        """One (sequence, layer) slab: the whole sequence through the oracle's splice."""
         import kvsynth
         from oracle import splice as osplice, rope as orope
-        th = orope.inv_freq(64, 10000.0)
         w = self.w
-        rows, spent, units = 0, 0.0, 0
-        for b in range(w.n_seq):
-            d = w.directives[b]
-            p = osplice.plan(int(w.seq_lens[b]), int(d[0]), int(d[1]), int(d[2]), 0)
-            r = kvsynth.rng(3, 9, b)
-            pf = kvsynth.bf16_normal(r, (int(w.seq_lens[b]), 512))
-            rp = kvsynth.bf16_normal(r, (int(w.seq_lens[b]), 64))
-            spf = kvsynth.bf16_normal(r, (int(d[2]), 512))
-            srp = kvsynth.bf16_normal(r, (int(d[2]), 64))
-            t0 = time.perf_counter()
-            osplice.splice_sequence(p, pf, rp, spf, srp, 1, 64, th)
-            spent += time.perf_counter() - t0
-            rows += p.moved_rows if p.delta != 0 else 0
-            units += 1
-            if spent >= budget_s:
-                break
-        slots = rows / w.shape.n_layers
-        return {"value": slots / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
-                "sample": f"{units} (sequence, layer) units of the same directives ({rows} moved layer-rows), "
-                          f"generation excluded, numpy fp64, one process"}
+        b, l = i % w.n_seq, i // w.n_seq
+        d = w.directives[b]
+        t0 = time.perf_counter()
+        th = orope.inv_freq(64, 10000.0)
+        p = osplice.plan(int(w.seq_lens[b]), int(d[0]), int(d[1]), int(d[2]), 0)
+        r = kvsynth.rng(3, 9, b, l)
+        pf = kvsynth.bf16_normal(r, (int(w.seq_lens[b]), 512))
+        rp = kvsynth.bf16_normal(r, (int(w.seq_lens[b]), 64))
+        spf = kvsynth.bf16_normal(r, (int(d[2]), 512))
+        srp = kvsynth.bf16_normal(r, (int(d[2]), 64))
+        t1 = time.perf_counter()
+        osplice.splice_sequence(p, pf, rp, spf, srp, 1, 64, th)
+        t2 = time.perf_counter()
+        moved = p.moved_rows if p.delta != 0 else 0
+        return moved / w.shape.n_layers, t2 - t1, t1 - t0
 
 
 class SpliceLazy:
@@ -352,23 +413,26 @@ class SpliceLazy:
         # the same directives on the same lengths each step: same table work
         self.rrs.leyline_splice_lazy(self.bt, self.pend, self.w.block_size, self.lens, self.dirs, self.stubs)
 
-    def cpu_baseline(self, budget_s):
+    oracle_what = "sequence table edits of the step's directives (numpy)"
+
+    def oracle_slabs(self):
+        return self.w.n_seq
+
+    def oracle_slab(self, i):
         from oracle import lazy as olazy
         w = self.w
         B = w.block_size
         pend = np.zeros(w.block_tables.shape[1], np.int64)
-        rows, spent, units = 0, 0.0, 0
         stub = np.arange(64)
-        while spent < budget_s:
-            for b, d in enumerate(self.dirs.tolist()):
-                t0 = time.perf_counter()
-                olazy.lazy_splice_tables(w.block_tables[b], pend, int(w.seq_lens[b]), d[0], d[1], d[2], B,
-                                         stub[: d[2] // B])
-                spent += time.perf_counter() - t0
-                rows += int(w.seq_lens[b]) - d[1]
-                units += 1
-        return {"value": rows / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
-                "sample": f"{units} sequence table edits (the step's 64, repeated), numpy, one process"}
+        d = self.dirs[i].tolist()
+        t1 = time.perf_counter()
+        n = 0
+        while n == 0 or time.perf_counter() - t1 < 0.2:
+            olazy.lazy_splice_tables(w.block_tables[i], pend, int(w.seq_lens[i]), d[0], d[1], d[2], B,
+                                     stub[: d[2] // B])
+            n += 1
+        t2 = time.perf_counter()
+        return n * (int(w.seq_lens[i]) - d[1]), t2 - t1, 0.0
 
 
 class GatherLazy:
@@ -424,7 +488,12 @@ class GatherLazy:
     def step(self):
         self.rrs.kv_relocate_gather_lazy(self.bt, self.pend, self.w.block_size, self.batch)
 
-    def cpu_baseline(self, budget_s):
+    oracle_what = "table edits of the step's placements (numpy)"
+
+    def oracle_slabs(self):
+        return 1
+
+    def oracle_slab(self, i):
         from oracle import lazy as olazy
         w, B = self.w, self.w.block_size
         bt = np.arange(self.bt_stride)
@@ -434,15 +503,13 @@ class GatherLazy:
             n = int(self.nb[c])
             pl.append((np.arange(off, off + n), None, n * B, int(w.base_pos[c]), int(self.tgt[c])))
             off += n
-        slots, spent, steps = 0, 0.0, 0
-        while spent < budget_s:
-            t0 = time.perf_counter()
+        t1 = time.perf_counter()
+        n = 0
+        while n == 0 or time.perf_counter() - t1 < 0.2:
             olazy.lazy_gather_tables(bt, pend, B, pl)
-            spent += time.perf_counter() - t0
-            slots += self.slots
-            steps += 1
-        return {"value": slots / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
-                "sample": f"{steps} table edits of the step's {len(pl)} placements, numpy, one process"}
+            n += 1
+        t2 = time.perf_counter()
+        return n * self.slots, t2 - t1, 0.0
 
 
 class Keys:
@@ -483,19 +550,18 @@ class Keys:
         w = self.w
         self.rrs.registry_chunk_keys(self.tok, self.off, self.gear, w.threshold, w.min_len, w.max_len, w.s1_window)
 
-    def cpu_baseline(self, budget_s):
+    oracle_what = "whole token streams of the same draw (pure Python)"
+
+    def oracle_slabs(self):
+        return self.w.tokens.shape[0]
+
+    def oracle_slab(self, i):
         from oracle import keying as ok
         w = self.w
-        toks, spent = 0, 0.0
-        for s in range(w.tokens.shape[0]):
-            t0 = time.perf_counter()
-            ok.chunk_keys(w.tokens[s], w.gear, w.threshold, w.min_len, w.max_len, w.s1_window, w.seed)
-            spent += time.perf_counter() - t0
-            toks += w.tokens.shape[1]
-            if spent >= budget_s:
-                break
-        return {"value": toks / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                "sample": f"{toks // w.tokens.shape[1]} whole streams of the same draw, pure Python, one process"}
+        t1 = time.perf_counter()
+        ok.chunk_keys(w.tokens[i], w.gear, w.threshold, w.min_len, w.max_len, w.s1_window, w.seed)
+        t2 = time.perf_counter()
+        return w.tokens.shape[1], t2 - t1, 0.0
 
 
 class GqaPatch:
@@ -555,33 +621,29 @@ class GqaPatch:
     def step(self):
         self.rrs.kv_relocate_gather(self.cache, self.bt, self.ents, self.pt, self.fk, self.fv)
 
-    def cpu_baseline(self, budget_s):
+    oracle_what = "(chunk, layer) slabs, K rotated and patched, V patched (numpy fp64)"
+
+    def oracle_slabs(self):
+        return len(self.w.deltas) * self.w.shape.n_layers
+
+    def oracle_slab(self, j):
         import kvsynth
         from oracle import patch as opatch, rope as orope, bf16 as ob
         w = self.w
+        L = w.shape.n_layers
+        i, l = j // L, j % L
+        t0 = time.perf_counter()
         th = orope.inv_freq(w.shape.head_dim, w.shape.rope_base)
-        rows, spent, units = 0, 0.0, 0
-        for i in range(len(w.deltas)):
-            r = kvsynth.rng(4, 9, i)
-            for l in range(w.shape.n_layers):
-                k = ob.to_f64(kvsynth.bf16_normal(r, (w.chunk_len, w.shape.width)))
-                v = ob.to_f64(kvsynth.bf16_normal(r, (w.chunk_len, w.shape.width)))
-                U = kvsynth.f32_normal(r, (w.chunk_len, w.rank), w.factor_std)
-                V = kvsynth.f32_normal(r, (w.shape.width, w.rank), w.factor_std)
-                t0 = time.perf_counter()
-                opatch.relocate_and_patch_keys(k, int(w.deltas[i]), w.shape.heads, w.shape.head_dim, th, U, V)
-                opatch.patch_values(v, U, V)
-                spent += time.perf_counter() - t0
-                rows += w.chunk_len
-                units += 1
-                if spent >= budget_s:
-                    break
-            if spent >= budget_s:
-                break
-        slots = rows / w.shape.n_layers
-        return {"value": slots / spent, "unit": "slots/s", "cores": 1, "kind": "oracle",
-                "sample": f"{units} (chunk, layer) units ({rows} layer-rows, K and V), generation excluded, "
-                          f"numpy fp64 (matmul through numpy's BLAS, single-threaded here)"}
+        r = kvsynth.rng(4, 9, i, l)
+        k = ob.to_f64(kvsynth.bf16_normal(r, (w.chunk_len, w.shape.width)))
+        v = ob.to_f64(kvsynth.bf16_normal(r, (w.chunk_len, w.shape.width)))
+        U = kvsynth.f32_normal(r, (w.chunk_len, w.rank), w.factor_std)
+        V = kvsynth.f32_normal(r, (w.shape.width, w.rank), w.factor_std)
+        t1 = time.perf_counter()
+        opatch.relocate_and_patch_keys(k, int(w.deltas[i]), w.shape.heads, w.shape.head_dim, th, U, V)
+        opatch.patch_values(v, U, V)
+        t2 = time.perf_counter()
+        return w.chunk_len / L, t2 - t1, t1 - t0
 
 
 class Decode:
@@ -639,31 +701,27 @@ class Decode:
         self.rrs.mla_decode_rotate_on_read(self.qn, self.qr, self.cache, 0, self.bt, self.pend, self.lens, w.scale,
                                            max_seq_len=w.ctx, out=self.out, lse=self.lse)
 
-    def cpu_baseline(self, budget_s):
+    oracle_what = "whole sequences (128 heads) attended on explicitly re-rotated keys (numpy fp64)"
+
+    def oracle_slabs(self):
+        return self.w.batch
+
+    def oracle_slab(self, b):
         import kvsynth
         from oracle import decode as odec, rope as orope, bf16 as ob
         w = self.w
+        t0 = time.perf_counter()
         th = orope.inv_freq(64, 10000.0)
-        keys, spent, seqs = 0, 0.0, 0
-        for b in range(w.batch):
-            r = kvsynth.rng(5, 9, b)
-            ckv = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, 512)))
-            kr = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, 64)))
-            qn = ob.to_f64(kvsynth.bf16_normal(r, (w.heads, 512)))
-            qr = ob.to_f64(kvsynth.bf16_normal(r, (w.heads, 64)))
-            d = odec.token_deltas(w.pending_delta[b], w.ctx, 64)
-            t0 = time.perf_counter()
-            odec.mla_decode(qn, qr, ckv, kr, d, w.scale, th, round_keys=True)
-            spent += time.perf_counter() - t0
-            keys += w.ctx
-            seqs += 1
-            if spent >= budget_s:
-                break
-        import os as _os
-        thr = int(_os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(_os.sched_getaffinity(0))
-        return {"value": keys / spent, "unit": "keys/s", "cores": thr, "kind": "oracle",
-                "sample": f"{seqs} whole sequences ({keys} keys, 128 heads), generation excluded, numpy fp64 "
-                          f"(its two matmuls go through numpy's BLAS, which may use up to {thr} threads)"}
+        r = kvsynth.rng(5, 9, b)
+        ckv = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, 512)))
+        kr = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, 64)))
+        qn = ob.to_f64(kvsynth.bf16_normal(r, (w.heads, 512)))
+        qr = ob.to_f64(kvsynth.bf16_normal(r, (w.heads, 64)))
+        d = odec.token_deltas(w.pending_delta[b], w.ctx, 64)
+        t1 = time.perf_counter()
+        odec.mla_decode(qn, qr, ckv, kr, d, w.scale, th)
+        t2 = time.perf_counter()
+        return w.ctx, t2 - t1, t1 - t0
 
 
 class GqaDecode:
@@ -719,32 +777,27 @@ class GqaDecode:
         self.rrs.gqa_decode_rotate_on_read(self.q, self.cache, 0, self.bt, self.pend, self.lens, w.scale,
                                            max_seq_len=w.ctx, out=self.out, lse=self.lse)
 
-    def cpu_baseline(self, budget_s):
+    oracle_what = "whole sequences attended on explicitly re-rotated keys (numpy fp64)"
+
+    def oracle_slabs(self):
+        return self.w.batch
+
+    def oracle_slab(self, b):
         import kvsynth
         from oracle import decode as odec, rope as orope, bf16 as ob
         w = self.w
         G, D = w.shape.heads, w.shape.head_dim
+        t0 = time.perf_counter()
         th = orope.inv_freq(D, 500000.0)
-        keys, spent, seqs = 0, 0.0, 0
-        for b in range(w.batch):
-            r = kvsynth.rng(7, 9, b)
-            k = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, G * D)))
-            v = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, G * D)))
-            q = ob.to_f64(kvsynth.bf16_normal(r, (w.q_heads, D)))
-            d = odec.token_deltas(w.pending_delta[b], w.ctx, 64)
-            t0 = time.perf_counter()
-            odec.gqa_decode(q, k, v, d, w.scale, th, G)
-            spent += time.perf_counter() - t0
-            keys += w.ctx * G
-            seqs += 1
-            if spent >= budget_s:
-                break
-        import os as _os
-        thr = int(_os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(_os.sched_getaffinity(0))
-        return {"value": keys / spent, "unit": "keys/s", "cores": thr, "kind": "oracle",
-                "sample": f"{seqs} whole sequences ({keys} keys over {G} KV heads, {w.q_heads} query heads), "
-                          f"generation excluded, numpy fp64 (its matrix-vector products go through numpy's BLAS, "
-                          f"which may use up to {thr} threads)"}
+        r = kvsynth.rng(7, 9, b)
+        k = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, G * D)))
+        v = ob.to_f64(kvsynth.bf16_normal(r, (w.ctx, G * D)))
+        q = ob.to_f64(kvsynth.bf16_normal(r, (w.q_heads, D)))
+        d = odec.token_deltas(w.pending_delta[b], w.ctx, 64)
+        t1 = time.perf_counter()
+        odec.gqa_decode(q, k, v, d, w.scale, th, G)
+        t2 = time.perf_counter()
+        return w.ctx * G, t2 - t1, t1 - t0
 
 
 class PatchForm:
@@ -796,26 +849,25 @@ class PatchForm:
     def step(self):
         self.rrs.kamera_patch_factors(self.d, self.w.rank, self.omega, out=self.out)
 
-    def cpu_baseline(self, budget_s):
+    oracle_what = "deficits factored by float64 SVD (numpy LAPACK)"
+
+    def oracle_slabs(self):
+        return self.w.n
+
+    def oracle_slab(self, i):
         import torch
         import kvsynth
         from oracle import svd
         w = self.w
-        done, spent = 0, 0.0
-        while spent < budget_s and done < w.n:
-            shape = (1, w.orders, w.rows, w.cols) if w.orders > 1 else (1, w.rows, w.cols)
-            d = torch.empty(shape, dtype=torch.float32)
-            kvsynth.deficit_batch_(d, w.energy_dirs, w.decay, w.noise, *w.seed_keys, 9, done)
-            x = d[0].double().numpy()
-            t0 = time.perf_counter()
-            svd.truncated_factors(svd.orbit_deficit(x) if w.orders > 1 else x, w.rank)
-            spent += time.perf_counter() - t0
-            done += 1
-        import os as _os
-        thr = int(_os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(_os.sched_getaffinity(0))
-        return {"value": done / spent, "unit": "deficits/s", "cores": thr, "kind": "oracle",
-                "sample": f"{done} deficits of {w.rows} x {w.cols} (float64 SVD through numpy's LAPACK, which may "
-                          f"use up to {thr} threads), generation excluded"}
+        t0 = time.perf_counter()
+        shape = (1, w.orders, w.rows, w.cols) if w.orders > 1 else (1, w.rows, w.cols)
+        d = torch.empty(shape, dtype=torch.float32)
+        kvsynth.deficit_batch_(d, w.energy_dirs, w.decay, w.noise, *w.seed_keys, 9, i)
+        x = d[0].double().numpy()
+        t1 = time.perf_counter()
+        svd.truncated_factors(svd.orbit_deficit(x) if w.orders > 1 else x, w.rank)
+        t2 = time.perf_counter()
+        return 1, t2 - t1, t1 - t0
 
 
 class Copy:
@@ -846,8 +898,7 @@ class Copy:
     def step(self):
         self.b.copy_(self.a)
 
-    def cpu_baseline(self, budget_s):
-        return None
+    oracle_what = None
 
 
 WORKLOADS = {"gather": Gather, "splice": Splice, "splice_batched": SpliceBatched, "splice_lazy": SpliceLazy,
@@ -863,8 +914,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gather", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--workload", default="splice_batched", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=4.0,
+                    help="seconds of oracle time per worker process for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -875,7 +927,9 @@ def main():
     wl = WORKLOADS[args.workload]()
     unit = getattr(wl, "unit", "keys/s" if isinstance(wl, (Decode, GqaDecode)) else "slots/s")
     # the CPU oracle runs before the GPU is touched
-    cpu = None if args.no_cpu_baseline else wl.cpu_baseline(args.cpu_budget)
+    cpu = None
+    if not args.no_cpu_baseline and wl.oracle_what:
+        cpu = oracle_baseline(args.workload, args.cpu_budget, unit, wl.oracle_what)
 
     import torch
     torch.cuda.set_device(0)

@@ -12,7 +12,7 @@ GPU with torch's seeded generator instead (see ``fill_normal_``).
 """
 
 from .workloads import (  # noqa: F401
-    BASE_SEED, rng, bf16_normal, f32_normal, fill_normal_,
+    BASE_SEED, rng, bf16_normal, f32_normal, fill_normal_, normal_range_,
     MLA, GQA, SpliceWorkload, GatherWorkload, PatchWorkload, DecodeWorkload, GqaDecodeWorkload,
     KeyingWorkload, single_splice, batched_splice, registry_gather, gqa_patch, rotate_on_read_decode,
     gqa_rotate_on_read_decode, registry_streams, PatchFormationWorkload, patch_formation, deficit_batch_,

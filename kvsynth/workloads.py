@@ -40,6 +40,17 @@ def f32_normal(r, shape, std=1.0):
     return (r.standard_normal(shape, dtype=np.float64) * std).astype(np.float32)
 
 
+def _slab_seed(keys):
+    return int(rng(*keys).integers(0, 2 ** 62))
+
+
+def _normal_slab(flat_slab, seed, std):
+    import torch
+    g = torch.Generator(device=flat_slab.device)
+    g.manual_seed(seed)
+    flat_slab.normal_(0.0, std, generator=g)
+
+
 def fill_normal_(t, *keys, std=1.0, slab_elems=1 << 28):
     """Fill a device tensor with seeded N(0, std^2) values, slab by slab.
 
@@ -47,16 +58,33 @@ def fill_normal_(t, *keys, std=1.0, slab_elems=1 << 28):
     (BASE_SEED, keys, slab index), so the contents do not depend on the slab
     size of earlier calls.
     """
-    import torch
     flat = t.view(-1)
     n = flat.numel()
-    seed0 = int(rng(*keys).integers(0, 2 ** 62))
+    seed0 = _slab_seed(keys)
     for i, s in enumerate(range(0, n, slab_elems)):
-        e = min(n, s + slab_elems)
-        g = torch.Generator(device=t.device)
-        g.manual_seed(seed0 + i)
-        flat[s:e].normal_(0.0, std, generator=g)
+        _normal_slab(flat[s:min(n, s + slab_elems)], seed0 + i, std)
     return t
+
+
+def normal_range_(out, lo, total, *keys, std=1.0, slab_elems=1 << 28):
+    """Regenerate flat elements [lo, lo + out.numel()) of what
+    ``fill_normal_(t, *keys)`` writes into a tensor of ``total`` elements,
+    into ``out`` (contiguous, same dtype and device as that tensor).  Each
+    generator slab that overlaps the range is redrawn whole, at its own size
+    and seed, into a scratch tensor and the overlap copied out."""
+    import torch
+    flat = out.view(-1)
+    hi = lo + flat.numel()
+    seed0 = _slab_seed(keys)
+    i0, i1 = lo // slab_elems, -(-hi // slab_elems)
+    scratch = torch.empty(min(slab_elems, total), dtype=out.dtype, device=out.device)
+    for i in range(i0, i1):
+        s, e = i * slab_elems, min(total, (i + 1) * slab_elems)
+        tmp = scratch[: e - s]
+        _normal_slab(tmp, seed0 + i, std)
+        a, b = max(s, lo), min(e, hi)
+        flat[a - lo:b - lo] = tmp[a - s:b - s]
+    return out
 
 
 @dataclass(frozen=True)

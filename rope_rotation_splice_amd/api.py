@@ -36,6 +36,40 @@ def _check(fn, st):
 _DT = {torch.bfloat16: KVR_BF16, torch.float32: KVR_F32}
 
 
+# Argument checks made before any library call.  The library sees only raw
+# addresses, so a host tensor, a tensor on another GPU, a wrong dtype or a
+# short table would make its kernels read or write the wrong memory; these
+# raise ValueError instead.  Structure (dtype, shape) is checked before the
+# device, so that the checks can be exercised without a GPU.
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on(t, device, name):
+    _need(t.is_cuda, f"{name} must be a CUDA tensor")
+    _need(t.device == device, f"{name} is on {t.device}, expected {device}")
+
+
+def _i32(t, name, dims=None, contiguous=True):
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(t.dtype == torch.int32, f"{name} must be int32, got {t.dtype}")
+    if dims is not None:
+        _need(t.dim() == dims, f"{name} must have {dims} dimensions")
+    if contiguous:
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _tensor(t, name, dtype, shape):
+    """dtype, exact shape (None entries free) and contiguity."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(t.dim() == len(shape) and all(s is None or int(a) == s for a, s in zip(t.shape, shape)),
+          f"{name} has shape {tuple(t.shape)}, expected {tuple('*' if s is None else s for s in shape)}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
 def _stream_handle():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -56,7 +90,12 @@ class KVCache:
             raise ValueError("pf and rope views must share layers, blocks and rows")
         if rope.shape[3] != rope_heads * rope_dim:
             raise ValueError("rope width must be rope_heads * rope_dim")
+        if pf.dtype not in _DT or rope.dtype not in _DT:
+            raise ValueError("cache parts must be bfloat16 or float32")
+        if pf.device != rope.device:
+            raise ValueError("pf and rope views must live on one device")
         self.pf, self.rope = pf, rope
+        self.device = pf.device
         self.n_layers, self.n_blocks, self.block_size = (int(x) for x in pf.shape[:3])
         self.rope_heads, self.rope_dim, self.rope_base = rope_heads, rope_dim, float(rope_base)
         self._inv = None
@@ -87,6 +126,20 @@ class Rows:
     rope: torch.Tensor
     base_pos: int = 0
 
+    def check(self, cache, name="rows", device=True):
+        """Layers, widths, dtypes and (with ``device``) device must match the cache's parts."""
+        pf, rp = self.pf, self.rope
+        _need(pf.dim() == 3 and rp.dim() == 3, f"{name}: pf and rope must be [layers, len, width]")
+        _need(int(pf.shape[0]) == cache.n_layers and int(rp.shape[0]) == cache.n_layers,
+              f"{name}: {int(pf.shape[0])} layers, the cache has {cache.n_layers}")
+        _need(int(pf.shape[1]) == int(rp.shape[1]), f"{name}: pf and rope lengths differ")
+        _need(int(pf.shape[2]) == int(cache.pf.shape[3]) and int(rp.shape[2]) == int(cache.rope.shape[3]),
+              f"{name}: widths {int(pf.shape[2])}/{int(rp.shape[2])} differ from the cache's")
+        _need(pf.dtype == cache.pf.dtype and rp.dtype == cache.rope.dtype, f"{name}: dtypes differ from the cache's")
+        if device and int(pf.shape[1]):
+            _on(pf, cache.device, f"{name}.pf")
+            _on(rp, cache.device, f"{name}.rope")
+
     def c(self):
         if self.pf.shape[1] == 0:
             return kvr_rows()             # no rows: nothing to copy
@@ -102,6 +155,16 @@ class LowRank:
     """fp32 factors for every layer: U [layers, len, rank], V [layers, width, rank]."""
     U: torch.Tensor
     V: torch.Tensor
+
+    def check(self, device, layers, rows, width, name="factors", on_device=True):
+        U, V = self.U, self.V
+        _need(U.dim() == 3 and V.dim() == 3, f"{name}: U and V must be [layers, n, rank]")
+        r = int(U.shape[2])
+        _tensor(U, f"{name}.U", torch.float32, (layers, rows, r))
+        _tensor(V, f"{name}.V", torch.float32, (layers, width, r))
+        if on_device and U.numel():
+            _on(U, device, f"{name}.U")
+            _on(V, device, f"{name}.V")
 
     def c(self):
         r = int(self.U.shape[-1])
@@ -194,12 +257,21 @@ def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, worksp
     dirs, n = _directives(directives)
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.stride(1) != 1:
         raise ValueError("block_tables must be an int32 [n_seq, blocks] tensor with unit last stride")
+    _need(int(block_tables.shape[0]) >= n, "block_tables needs a row per directive")
+    _need(len(seq_lens) == n, "seq_lens needs one length per directive")
+    if stubs is not None:
+        _need(len(stubs) == n, "stubs needs one entry (Rows or None) per directive")
+        for i, s in enumerate(stubs):
+            if s is not None:
+                s.check(cache, f"stubs[{i}]", device=False)
+    _on(block_tables, cache.device, "block_tables")
     lens, out = _i64(seq_lens, n), _i64(np.zeros(n, np.int64), n)
     stub_arr = None
     if stubs is not None:
         stub_arr = (kvr_rows * max(1, n))()
         for i, s in enumerate(stubs):
             if s is not None:
+                s.check(cache, f"stubs[{i}]")
                 stub_arr[i] = s.c()
     stream = torch.cuda.current_stream()
     handle = ctypes.c_void_p(stream.cuda_stream)
@@ -240,6 +312,10 @@ def leyline_splice_lazy(block_tables, pending_delta, block_size, seq_lens, direc
             raise ValueError("block_tables and pending_delta must be int32 [n_seq, blocks] with unit last stride")
     if pending_delta.shape != block_tables.shape or pending_delta.stride(0) != block_tables.stride(0):
         raise ValueError("pending_delta must match block_tables in shape and row stride")
+    _need(int(block_tables.shape[0]) >= n, "block_tables needs a row per directive")
+    _need(len(seq_lens) == n, "seq_lens needs one length per directive")
+    _on(block_tables, block_tables.device, "block_tables")
+    _on(pending_delta, block_tables.device, "pending_delta")
     if n > _FEW:
         da = dirs.a
         n_free = int(((da["s_end"] - da["s_start"]) // block_size)[da["mode"] == 0].sum())
@@ -247,6 +323,8 @@ def leyline_splice_lazy(block_tables, pending_delta, block_size, seq_lens, direc
         n_free = sum(int((d[1] - d[0]) // block_size) for d in directives if int(d[3]) == KVR_AMORTIZE)
     if stub_blocks is not None and (stub_blocks.dtype != torch.int32 or not stub_blocks.is_contiguous()):
         raise ValueError("stub_blocks must be a contiguous int32 tensor")
+    if stub_blocks is not None and stub_blocks.numel():
+        _on(stub_blocks, block_tables.device, "stub_blocks")
     freed = torch.empty(max(1, n_free), dtype=torch.int32, device=block_tables.device)
     lens, out = _i64(seq_lens, n), _i64(np.zeros(n, np.int64), n)
     st = lib.leyline_splice_lazy(int(block_size), block_tables.data_ptr(), pending_delta.data_ptr(),
@@ -264,12 +342,16 @@ class LazyEntry:
     already owe (int32 device tensor of the same length) or None.  The
     tensors are checked and their addresses taken once, here: an entry is
     immutable, and its tensors must not be resized while it is in use."""
-    __slots__ = ("_seq", "_blocks", "_pend", "_len", "_base", "_target", "_row", "_n_blocks", "_n_pend")
+    __slots__ = ("_seq", "_blocks", "_pend", "_len", "_base", "_target", "_row", "_n_blocks", "_n_pend",
+                 "_device")
 
     def __init__(self, seq, blocks, length, base_pos, p_target, pend=None):
         for t in (blocks, pend):
             if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
                 raise ValueError("entry blocks and pend must be contiguous int32 tensors")
+        if blocks is not None and pend is not None and blocks.device != pend.device:
+            raise ValueError("entry blocks and pend must live on one device")
+        self._device = blocks.device if blocks is not None else None
         self._seq, self._blocks, self._pend, self._len = int(seq), blocks, pend, int(length)
         self._base, self._target = int(base_pos), int(p_target)
         self._n_blocks = blocks.numel() if blocks is not None else 0
@@ -318,20 +400,26 @@ def kv_relocate_gather_lazy(block_tables, pending_delta, block_size, entries):
             raise ValueError("block_tables and pending_delta must be int32 [n_seq, blocks] with unit last stride")
     if pending_delta.shape != block_tables.shape or pending_delta.stride(0) != block_tables.stride(0):
         raise ValueError("pending_delta must match block_tables in shape and row stride")
+    _on(block_tables, block_tables.device, "block_tables")
+    _on(pending_delta, block_tables.device, "pending_delta")
     batch = entries if isinstance(entries, LazyBatch) else None
     items = batch.entries if batch is not None else entries
     n = len(items)
     B = int(block_size)
-    total = batch._totals.get(B) if batch is not None else None
+    key = (B, block_tables.device, int(block_tables.shape[0]))
+    total = batch._totals.get(key) if batch is not None else None
     if total is None:
         total = 0
         for e in items:
             nb = -(-e._len // B) if e._len > 0 else 0
             if e._n_blocks < nb or (e._n_pend is not None and e._n_pend < nb):
                 raise ValueError("entry blocks and pend need ceil(len / block_size) ids")
+            _need(0 <= e._seq < int(block_tables.shape[0]), "entry sequence outside the block tables")
+            if nb:
+                _need(e._device == block_tables.device, "entry blocks must live on the block tables' device")
             total += nb
         if batch is not None:
-            batch._totals[B] = total
+            batch._totals[key] = total
     if batch is not None:
         ents = batch._host
     else:
@@ -362,6 +450,10 @@ def registry_chunk_keys(tokens, offsets, gear, threshold, min_len, max_len, s1_w
         raise ValueError("tokens must be a contiguous int32 tensor")
     if gear.element_size() != 8 or not gear.is_contiguous():
         raise ValueError("gear must be a contiguous tensor of 64-bit values")
+    _need(len(offsets) >= 1, "offsets needs n_streams + 1 entries")
+    _need(int(tokens.numel()) >= int(offsets[-1]), "tokens is shorter than the last offset")
+    _on(tokens, tokens.device, "tokens")
+    _on(gear, tokens.device, "gear")
     off = [int(x) for x in offsets]
     n = len(off) - 1
     lens = [off[i + 1] - off[i] for i in range(n)]
@@ -393,10 +485,24 @@ def kv_relocate_gather(cache, block_table, entries, p_targets, patch_rope=None, 
     n = len(entries)
     if block_table.dtype != torch.int32 or block_table.dim() != 1 or block_table.stride(0) != 1:
         raise ValueError("block_table must be a contiguous int32 [blocks] tensor")
+    _need(len(p_targets) == n, "p_targets needs one target per entry")
+    patches = ((patch_rope, int(cache.rope.shape[3]), "patch_rope"), (patch_pf, int(cache.pf.shape[3]), "patch_pf"))
+    for on_device in (False, True):
+        for i, e in enumerate(entries):
+            e.check(cache, f"entries[{i}]", device=on_device)
+        for lst, width, name in patches:
+            if lst is None:
+                continue
+            _need(len(lst) == n, f"{name} needs one entry (LowRank or None) per registry entry")
+            for i, f in enumerate(lst):
+                if f is not None:
+                    f.check(cache.device, cache.n_layers, int(entries[i].pf.shape[1]), width, f"{name}[{i}]",
+                            on_device=on_device)
+    _on(block_table, cache.device, "block_table")
     ents = (kvr_rows * max(1, n))(*[e.c() for e in entries])
     pt = (ctypes.c_int64 * max(1, n))(*[int(x) for x in p_targets])
 
-    def lr(lst):
+    def lr(lst, width, name):
         if lst is None:
             return None
         arr = (kvr_lowrank * max(1, n))()
@@ -406,7 +512,8 @@ def kv_relocate_gather(cache, block_table, entries, p_targets, patch_rope=None, 
         return arr
 
     st = lib.kv_relocate_gather(ctypes.byref(cache.c), block_table.data_ptr(), int(block_table.numel()), ents,
-                                pt, n, lr(patch_rope), lr(patch_pf), _stream_handle())
+                                pt, n, lr(patch_rope, int(cache.rope.shape[3]), "patch_rope"),
+                                lr(patch_pf, int(cache.pf.shape[3]), "patch_pf"), _stream_handle())
     return _check("kv_relocate_gather", st)
 
 
@@ -415,6 +522,14 @@ def kv_patch_lowrank(cache, block_table, part, p_starts, lens, factors):
     logical slots [p_starts[i], p_starts[i] + lens[i]) of every layer."""
     lib = _abi.load()
     n = len(factors)
+    _i32(block_table, "block_table", 1)
+    _need(part in (0, 1), "part must be 0 (position-free) or 1 (rotary)")
+    _need(len(p_starts) == n and len(lens) == n, "p_starts and lens need one value per factor set")
+    width = int((cache.rope if part else cache.pf).shape[3])
+    for on_device in (False, True):
+        for i, f in enumerate(factors):
+            f.check(cache.device, cache.n_layers, int(lens[i]), width, f"factors[{i}]", on_device=on_device)
+    _on(block_table, cache.device, "block_table")
     ps = (ctypes.c_int64 * max(1, n))(*[int(x) for x in p_starts])
     ln = (ctypes.c_int64 * max(1, n))(*[int(x) for x in lens])
     fs = (kvr_lowrank * max(1, n))(*[f.c() for f in factors])
@@ -423,16 +538,42 @@ def kv_patch_lowrank(cache, block_table, part, p_starts, lens, factors):
     return _check("kv_patch_lowrank", st)
 
 
+def _decode_tables(device, b, block_tables, pending_delta, seq_lens, on_device):
+    _i32(block_tables, "block_tables", 2, contiguous=False)
+    _need(block_tables.stride(1) == 1, "block_tables needs a unit last stride")
+    _need(int(block_tables.shape[0]) >= b, "block_tables needs a row per sequence")
+    _i32(pending_delta, "pending_delta", 2, contiguous=False)
+    _need(pending_delta.shape == block_tables.shape and pending_delta.stride() == block_tables.stride(),
+          "pending_delta must match block_tables in shape and strides")
+    _i32(seq_lens, "seq_lens", 1)
+    _need(int(seq_lens.numel()) >= b, "seq_lens needs a length per sequence")
+    if on_device:
+        for t, nm in ((block_tables, "block_tables"), (pending_delta, "pending_delta"), (seq_lens, "seq_lens")):
+            _on(t, device, nm)
+
+
 def mla_decode_rotate_on_read(q_nope, q_rope, cache, layer, block_tables, pending_delta, seq_lens, scale,
                               max_seq_len=None, out=None, lse=None, workspace=None):
     """One absorbed-MLA decode step with per-block pending shifts applied to k_r on load.
     Returns (out bf16 [b, h, 512], lse f32 [b, h])."""
     lib = _abi.load()
+    _need(q_nope.dim() == 3, "q_nope must be [batch, heads, 512]")
     b, h = int(q_nope.shape[0]), int(q_nope.shape[1])
+    _tensor(q_nope, "q_nope", torch.bfloat16, (b, h, 512))
+    _tensor(q_rope, "q_rope", torch.bfloat16, (b, h, 64))
+    _decode_tables(cache.device, b, block_tables, pending_delta, seq_lens, False)
+    if out is not None:
+        _tensor(out, "out", torch.bfloat16, (b, h, 512))
+    if lse is not None:
+        _tensor(lse, "lse", torch.float32, (b, h))
+    _decode_tables(cache.device, b, block_tables, pending_delta, seq_lens, True)
+    for t, nm in ((q_nope, "q_nope"), (q_rope, "q_rope"), (out, "out"), (lse, "lse")):
+        if t is not None:
+            _on(t, cache.device, nm)
     if max_seq_len is None:
         max_seq_len = int(block_tables.shape[1]) * cache.block_size
     if out is None:
-        out = torch.empty((b, h, int(q_nope.shape[2])), dtype=torch.bfloat16, device=q_nope.device)
+        out = torch.empty((b, h, 512), dtype=torch.bfloat16, device=q_nope.device)
     if lse is None:
         lse = torch.empty((b, h), dtype=torch.float32, device=q_nope.device)
     need = int(lib.kvr_decode_workspace_bytes(b, h, int(max_seq_len)))
@@ -456,6 +597,16 @@ def gqa_decode_rotate_on_read(q, cache, layer, block_tables, pending_delta, seq_
         raise ValueError("q must be a contiguous bf16 [batch, heads, dim] tensor")
     b, h = int(q.shape[0]), int(q.shape[1])
     kv = int(cache.c.rope_heads)
+    _tensor(q, "q", torch.bfloat16, (b, h, 128))
+    _decode_tables(cache.device, b, block_tables, pending_delta, seq_lens, False)
+    if out is not None:
+        _tensor(out, "out", torch.bfloat16, (b, h, 128))
+    if lse is not None:
+        _tensor(lse, "lse", torch.float32, (b, h))
+    _decode_tables(cache.device, b, block_tables, pending_delta, seq_lens, True)
+    for t, nm in ((q, "q"), (out, "out"), (lse, "lse")):
+        if t is not None:
+            _on(t, cache.device, nm)
     if max_seq_len is None:
         max_seq_len = int(block_tables.shape[1]) * cache.block_size
     if out is None:
@@ -490,6 +641,11 @@ def kamera_patch_factors(deficits, rank, omega, out=None, workspace=None):
                torch.empty((n, cols, rank), dtype=torch.float32, device=dev),
                torch.empty((n, rank), dtype=torch.float32, device=dev))
     U, V, s = out
+    _tensor(U, "U", torch.float32, (n, rows, int(rank)))
+    _tensor(V, "V", torch.float32, (n, cols, int(rank)))
+    _tensor(s, "sigma", torch.float32, (n, int(rank)))
+    for t, nm in ((deficits, "deficits"), (omega, "omega"), (U, "U"), (V, "V"), (s, "sigma")):
+        _on(t, dev, nm)
     need = int(lib.kvr_patch_factors_workspace_bytes(n, orders, rows, cols))
     ws = workspace if workspace is not None else _workspace(need, dev, "form")
     st = lib.kamera_patch_factors(d4.data_ptr(), n, orders, rows, cols, int(rank), omega.data_ptr(), U.data_ptr(),
@@ -500,8 +656,18 @@ def kamera_patch_factors(deficits, rank, omega, out=None, workspace=None):
 
 
 def device_errors():
-    """Synchronize and return (then clear) the library's device error bits."""
+    """Synchronize and return (then clear) the library's device error bits.
+
+    After a ticket or wait error of the ticketed splice, the cached splice
+    workspaces may hold nonzero counters or stale flags; they are zeroed here,
+    so that the next splice starts from a clean workspace."""
     lib = _abi.load()
     v = ctypes.c_uint32(0)
     _check("kvr_device_errors", lib.kvr_device_errors(ctypes.byref(v)))
-    return int(v.value)
+    bits = int(v.value)
+    if bits & (_abi.KVR_DEV_SPIN_LIMIT | _abi.KVR_DEV_BAD_TICKET):
+        for key, ws in _workspaces.items():
+            if key[0] == "splice":
+                ws.zero_()
+        torch.cuda.synchronize()
+    return bits

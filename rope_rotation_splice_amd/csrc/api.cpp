@@ -83,30 +83,55 @@ kvr_status make_pool(const kvr_cache* c, Pool& P, double* omega) {
 // Tile shape: rows per tile T, and the per-thread counts of position-free
 // chunks (pfi) and rotation items (rs) it needs, both powers of two <= 16.
 // Measured on MI355X (61-layer MLA rows): the gather streams best with about
-// 9 KB of row data per workgroup (many short-lived workgroups), the in-place
-// splice with about 36 KB (its per-tile ticket and flag round trips need
-// more bytes per workgroup to hide).  KVR_TILE_ROWS overrides T (tuning).
+// 9 KB of row data per workgroup (many short-lived workgroups), the ticketed
+// in-place splice with about 36 KB (its per-tile ticket and flag round trips
+// need more bytes per workgroup to hide).
 struct TileShape { int T, pfi, rs; };
 
 int pow2_at_least(int v) { int p = 1; while (p < v) p *= 2; return p; }
 int pow2_at_most(int v) { int p = 1; while (p * 2 <= v) p *= 2; return p; }
 
-TileShape choose_tile(const Pool& P, bool rope_f32, bool splice) {
-    const int row_bytes = 16 * (P.pf_chunks + 2 * P.rope_items);
-    int T = pow2_at_most(std::max(1, (splice ? 36864 : 9216) / row_bytes));
-    if (const char* e = std::getenv("KVR_TILE_ROWS")) {
-        const int v = std::atoi(e);
-        if (v > 0) T = v;
-    }
-    T = std::min(T, kMaxTileRows);
-    if (rope_f32) T = std::min(kMaxTileRows, (kThreads * kPfItems) / P.pf_chunks);
+TileShape shape_for(const Pool& P, int T) {
     for (;;) {
         TileShape s{T, pow2_at_least((T * P.pf_chunks + kThreads - 1) / kThreads),
                     pow2_at_least((T * P.rope_items + kThreads - 1) / kThreads)};
-        if (rope_f32) s.pfi = kPfItems;          // fp32 keys: one register shape only
         s.pfi = std::max(s.pfi, s.rs);
         if (s.pfi <= kPfItems || T == 1) return s;
         T = std::max(1, T / 2);
+    }
+}
+
+TileShape choose_tile(const Pool& P, bool rope_f32, bool splice) {
+    const int row_bytes = 16 * (P.pf_chunks + 2 * P.rope_items);
+    int T = pow2_at_most(std::max(1, (splice ? 36864 : 9216) / row_bytes));
+    T = std::min(T, kMaxTileRows);
+    if (rope_f32) T = std::min(kMaxTileRows, (kThreads * kPfItems) / P.pf_chunks);
+    TileShape s = shape_for(P, T);
+    if (rope_f32) s.pfi = kPfItems;          // fp32 keys: one register shape only
+    return s;
+}
+
+// Chain tiles of the band mover hold about 36 KB of rows (as the ticketed
+// splice) and at most a block of rows, so that the rows a tile takes from one
+// band span at most two blocks.
+constexpr int kBandBytes = 36864;
+// Calls that move fewer rows than this (all layers; 256 compute units x 8
+// workgroups x 32 rows) are bound by latency and take the band mover; larger
+// ones stream through the ticketed mover.  Measured on MI355X: the single
+// 4096-slot splice (2,296 rows) takes 8.0 us in chain tiles against 10.0 us
+// ticketed; the 64-sequence batch takes 21.5 ms ticketed against 25.2 ms in
+// chain tiles.
+constexpr int64_t kBandMaxRows = 65536;
+
+TileShape choose_band(const Pool& P, bool rope_f32) {
+    const int row_bytes = 16 * (P.pf_chunks + 2 * P.rope_items);
+    int T = pow2_at_most(std::max(1, kBandBytes / row_bytes));
+    T = std::min({T, kMaxTileRows, pow2_at_most(P.block_size)});
+    // the band kernel is built for at most 4 rotation items per thread (2 for fp32 keys)
+    for (;;) {
+        const TileShape s = shape_for(P, T);
+        if (s.rs <= (rope_f32 ? 2 : 4) || T == 1) return s;
+        T /= 2;
     }
 }
 
@@ -143,8 +168,10 @@ struct SpliceSeq {
 struct SplicePlan {
     Pool pool;
     double omega[kMaxPairs];
-    TileShape tile{1, 1, 1};
-    std::vector<std::vector<SpliceSeq>> launches;
+    TileShape tile{1, 1, 1};          // ticketed tiles
+    TileShape band{1, 1, 1};          // band mover (chain tiles)
+    std::vector<std::vector<SpliceSeq>> launches;        // ticketed launches
+    std::vector<std::vector<SpliceSeq>> band_launches;
     size_t counters_bytes = 0, flags_bytes = 0;
     bool forget = false;
     std::vector<int64_t> new_lens;
@@ -199,6 +226,25 @@ kvr_status check_ownership(const int32_t* d_tables, int32_t stride, const std::v
     return KVR_OK;
 }
 
+// Group items into launches of at most kMaxItems items and < 2^31 workgroups;
+// wg_off is each item's first workgroup within its launch.
+void pack_launches(std::vector<SpliceSeq>& items, int n_layers, std::vector<std::vector<SpliceSeq>>& out) {
+    std::vector<SpliceSeq> cur;
+    int64_t wg = 0;
+    for (SpliceSeq& s : items) {
+        const int64_t add = (int64_t)s.item.tiles * n_layers;
+        if ((int)cur.size() == kMaxItems || wg + add >= ((int64_t)1 << 31)) {
+            out.push_back(cur);
+            cur.clear();
+            wg = 0;
+        }
+        s.item.wg_off = (int32_t)wg;
+        wg += add;
+        cur.push_back(s);
+    }
+    if (!cur.empty()) out.push_back(cur);
+}
+
 kvr_status plan_splice(const kvr_cache* c, int32_t bt_stride, int32_t n_seq, const int64_t* seq_lens,
                        const kvr_directive* dirs, const kvr_rows* stubs, SplicePlan& pl) {
     kvr_status st = make_pool(c, pl.pool, pl.omega);
@@ -210,8 +256,15 @@ kvr_status plan_splice(const kvr_cache* c, int32_t bt_stride, int32_t n_seq, con
     pl.tile = choose_tile(pl.pool, c->rope_dtype == KVR_F32, true);
     const int T = pl.tile.T;
     pl.new_lens.assign(n_seq, 0);
-    std::vector<SpliceSeq> cur;
-    int32_t wg = 0;
+    std::vector<SpliceSeq> ticketed, banded;
+    std::vector<int64_t> bands;                       // per banded item: bands its chains hold
+    // rows the call moves, all layers: a small call takes the band mover
+    int64_t rows = 0;
+    for (int32_t b = 0; b < n_seq; ++b)
+        if (dirs[b].mode == KVR_AMORTIZE && dirs[b].s_end >= 0 && dirs[b].s_end <= seq_lens[b] &&
+            dirs[b].r_len != dirs[b].s_end - dirs[b].s_start)
+            rows += seq_lens[b] - dirs[b].s_end;
+    const bool small = rows * c->n_layers < kBandMaxRows;
     for (int32_t b = 0; b < n_seq; ++b) {
         const kvr_directive& d = dirs[b];
         const int64_t N = seq_lens[b];
@@ -239,21 +292,44 @@ kvr_status plan_splice(const kvr_cache* c, int32_t bt_stride, int32_t n_seq, con
         it.shift = (int32_t)delta;
         it.moved = (int32_t)(N - d.s_end);
         it.r_len = has_stub ? (int32_t)d.r_len : 0;
-        it.move_tiles = (delta != 0 && it.moved > 0) ? (it.moved + T - 1) / T : 0;
-        it.tiles = it.move_tiles + (it.r_len + T - 1) / T;
         it.bt_off = b * bt_stride;
-        if (it.tiles == 0) continue;
-        const int64_t add = (int64_t)it.tiles * c->n_layers;
-        if ((int)cur.size() == kMaxItems || wg + add >= ((int64_t)1 << 31)) {
-            pl.launches.push_back(cur);
-            cur.clear();
-            wg = 0;
+        const int64_t L = delta < 0 ? -delta : delta;
+        const bool moves = delta != 0 && it.moved > 0;
+        // the band mover takes a sequence whose chains are at most
+        // kBandMaxBands rows long; shorter shifts go through tickets
+        const int64_t K = moves ? (it.moved + L - 1) / L : 0;
+        // the band mover addresses rows with 32-bit block and row strides
+        const bool strides32 = pl.pool.pf_b < ((int64_t)1 << 32) && pl.pool.pf_r < ((int64_t)1 << 32) &&
+                               pl.pool.rp_b < ((int64_t)1 << 32) && pl.pool.rp_r < ((int64_t)1 << 32);
+        if (small && K <= kBandMaxBands && strides32) {
+            if (!moves && it.r_len == 0) continue;
+            banded.push_back({b, it});
+            bands.push_back(K);
+        } else {
+            it.move_tiles = (it.moved + T - 1) / T;
+            it.tiles = it.move_tiles + (it.r_len + T - 1) / T;
+            ticketed.push_back({b, it});
         }
-        it.wg_off = wg;
-        wg += (int32_t)add;
-        cur.push_back({b, it});
     }
-    if (!cur.empty()) pl.launches.push_back(cur);
+    // chain tiles take all K bands of max(1, TB / K) offsets each
+    pl.band = choose_band(pl.pool, c->rope_dtype == KVR_F32);
+    const int TB = pl.band.T;
+    for (size_t i = 0; i < banded.size(); ++i) {
+        Item& it = banded[i].item;
+        const int64_t K = bands[i];
+        const int64_t L = it.shift < 0 ? -(int64_t)it.shift : it.shift;
+        const int64_t TO = K >= TB ? 1 : TB / std::max<int64_t>(K, 1);
+        it.move_tiles = K ? (int32_t)((std::min<int64_t>(L, it.moved) + TO - 1) / TO) : 0;
+        it.tiles = it.move_tiles + (it.r_len + TB - 1) / TB;
+    }
+    // longest chains first, so that they do not trail at the end of a launch
+    std::vector<size_t> order(banded.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return bands[x] > bands[y]; });
+    std::vector<SpliceSeq> sorted;
+    for (size_t i : order) sorted.push_back(banded[i]);
+    pack_launches(sorted, c->n_layers, pl.band_launches);
+    pack_launches(ticketed, c->n_layers, pl.launches);
     size_t maxc = 0, maxf = 0;
     for (auto& L : pl.launches) {
         size_t nwg = 0;
@@ -261,8 +337,8 @@ kvr_status plan_splice(const kvr_cache* c, int32_t bt_stride, int32_t n_seq, con
         maxc = std::max(maxc, L.size() * (size_t)c->n_layers * 4);
         maxf = std::max(maxf, nwg * 4);
     }
-    pl.counters_bytes = round_up(maxc);
-    pl.flags_bytes = round_up(maxf);
+    pl.counters_bytes = maxc ? round_up(maxc) : 0;
+    pl.flags_bytes = maxf ? round_up(maxf) : 0;
     return KVR_OK;
 }
 
@@ -373,10 +449,11 @@ kvr_status kvr_device_errors(uint32_t* flags) {
     const uint32_t y = read_and_clear_errors_lazy();
     const uint32_t z = read_and_clear_errors_keys();
     const uint32_t u = read_and_clear_errors_gqa_decode();
+    const uint32_t b = read_and_clear_errors_band();
     if (v == 0xffffffffu || w == 0xffffffffu || x == 0xffffffffu || y == 0xffffffffu || z == 0xffffffffu ||
-        u == 0xffffffffu)
+        u == 0xffffffffu || b == 0xffffffffu)
         return hip_fail(hipErrorUnknown);
-    *flags = v | w | x | y | z | u;
+    *flags = v | w | x | y | z | u | b;
     return KVR_OK;
 }
 
@@ -434,6 +511,25 @@ kvr_status leyline_splice(const kvr_cache* cache, const int32_t* d_block_tables,
         if (st != KVR_OK) return st;
     }
     for (int32_t b = 0; b < n_seq; ++b) new_lens[b] = pl.new_lens[b];
+    for (auto& L : pl.band_launches) {
+        RelocArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.pool = pl.pool;
+        a.bt = d_block_tables;
+        a.n_items = (int32_t)L.size();
+        a.tile_rows = pl.band.T;
+        std::memcpy(a.omega, pl.omega, sizeof(a.omega));
+        int64_t nwg = 0;
+        for (int i = 0; i < kMaxItems; ++i) a.offs[i] = INT32_MAX;
+        for (size_t i = 0; i < L.size(); ++i) {
+            a.items[i] = L[i].item;
+            a.offs[i] = L[i].item.wg_off;
+            nwg += (int64_t)L[i].item.tiles * cache->n_layers;
+        }
+        a.n_wg = (int32_t)nwg;
+        hipError_t e = launch_band(a, pl.band.pfi, pl.band.rs, cache->rope_dtype == KVR_F32, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
     for (auto& L : pl.launches) {
         RelocArgs a;
         std::memset(&a, 0, sizeof(a));

@@ -13,6 +13,7 @@ constexpr int kPfItems = 16;         // max 16-byte position-free chunks held pe
 constexpr int kMaxTileRows = 128;    // rows per tile (LDS row tables)
 constexpr int kMaxPairs = 128;       // rotation pairs per head (rope_dim <= 256)
 constexpr int kMaxItems = 32;        // sequences / entries per launch
+constexpr int kBandMaxBands = 64;    // bands one band-mover workgroup walks (4 block ids each in LDS)
 
 // Byte-addressed view of the two parts of a paged pool.
 struct Pool {
@@ -233,6 +234,10 @@ static_assert(sizeof(RelocArgs) <= 4000, "relocation kernel arguments too large"
 // of 16-byte position-free chunks and of rotation items a tile needs (powers
 // of two up to 16, rope_slots <= pf_slots); rope_f32 selects fp32 keys.
 hipError_t launch_splice(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
+// Band mover (in-place splice without cross-workgroup ordering): tile_rows
+// is the band height (<= block size), the slot counts as above.
+hipError_t launch_band(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
+uint32_t read_and_clear_errors_band();
 hipError_t launch_gather(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 uint32_t read_and_clear_errors_relocate();

@@ -9,17 +9,23 @@
 // thread without shuffles.  The whole tile is held in registers between the
 // loads and the stores.
 //
-// In-place splice ordering.  Downstream rows move by Delta within their own
-// sequence, so a tile's destination may overlap the sources of other tiles.
-// Tiles of a unit are ordered in the safe direction (increasing slots for
-// Delta < 0, decreasing for Delta > 0) by a ticket taken from a per-unit
-// atomic counter when the workgroup starts -- so a ticket holder is resident.
-// A tile loads its whole source first, publishes "sources read" (flag =
-// launch epoch), then waits only for the earlier tiles whose sources overlap
-// its destination, and stores.  No tile waits before publishing, so every
-// wait ends; waits are bounded anyway and report KVR_DEV_SPIN_LIMIT instead
-// of hanging.  Stub tiles take the last tickets and wait for the move tiles
-// whose sources overlap the stub's destination (only possible when Delta > 0).
+// In-place splice ordering (ticket form).  Downstream rows move by Delta
+// within their own sequence, so a tile's destination may overlap the sources
+// of other tiles.  Tiles of a unit are ordered in the safe direction
+// (increasing slots for Delta < 0, decreasing for Delta > 0) by a ticket
+// taken from a per-unit atomic counter when the workgroup starts -- so a
+// ticket holder is resident.  Every workgroup takes exactly one ticket, and
+// the one that takes the last resets the counter, so a launch always leaves
+// its counters zeroed.  A tile loads its whole source first, publishes
+// "sources read" (flag = launch epoch), then waits only for the earlier tiles
+// whose sources overlap its destination, and stores.  No tile waits before
+// publishing, so every wait ends; waits are bounded anyway.  A ticket out of
+// range (a workspace that was not zeroed) or a wait that runs out raises a
+// device error bit and marks the launch aborted (g_abort_epoch = epoch):
+// from then on its tiles skip their stores, so no tile overwrites a source
+// that may not have been read.  Stub tiles take the last tickets and wait
+// for the move tiles whose sources overlap the stub's destination (only
+// possible when Delta > 0).
 #include "kvr_device.h"
 #include "kvr_internal.h"
 
@@ -28,6 +34,7 @@
 namespace kvr {
 
 __device__ uint32_t g_errors_relocate;
+__device__ uint32_t g_abort_epoch;      // epoch of a splice launch that hit a ticket or wait error
 
 namespace {
 
@@ -35,6 +42,11 @@ constexpr uint32_t kSpinLimit = 1u << 22;   // polls (each ~1-2 us with the slee
 
 __device__ __forceinline__ void raise_error(uint32_t bit) {
     __hip_atomic_fetch_or(&g_errors_relocate, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool aborted(uint32_t epoch) { return ld_dev(&g_abort_epoch) == epoch; }
+__device__ __forceinline__ void abort_launch(uint32_t bit, uint32_t epoch) {
+    raise_error(bit);
+    st_dev(&g_abort_epoch, epoch);
 }
 
 __device__ __forceinline__ int floor_div(int a, int b) {
@@ -51,6 +63,7 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
     __shared__ int32_t s_src_blk[kMaxTileRows], s_src_row[kMaxTileRows];
     __shared__ int32_t s_dst_blk[kMaxTileRows], s_dst_row[kMaxTileRows];
     __shared__ int32_t s_ticket;
+    __shared__ int32_t s_store;      // splice: 0 when this tile must not store
 
     const int tid = threadIdx.x;
     const int bid = blockIdx.x;
@@ -80,14 +93,12 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
         const int local = bid - I.wg_off;
         layer = local / I.tiles;
         if (tid == 0) {
-            int tk = -1;
-            if ((__hip_atomic_load(&g_errors_relocate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
-                 (KVR_DEV_SPIN_LIMIT | KVR_DEV_BAD_TICKET)) == 0) {
-                uint32_t* cnt = A.counters + it * P.n_layers + layer;
-                tk = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (tk == I.tiles - 1) st_dev(cnt, 0u);     // all tickets taken: leave it zeroed
-                if (tk < 0 || tk >= I.tiles) { raise_error(KVR_DEV_BAD_TICKET); tk = -1; }
-            }
+            // every workgroup takes exactly one ticket, whatever happened
+            // before, so the counter returns to zero at the end of the launch
+            uint32_t* cnt = A.counters + it * P.n_layers + layer;
+            int tk = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tk == I.tiles - 1) st_dev(cnt, 0u);     // all tickets taken: leave it zeroed
+            if (tk < 0 || tk >= I.tiles) { abort_launch(KVR_DEV_BAD_TICKET, A.epoch); tk = -1; }
             s_ticket = tk;
         }
         __syncthreads();
@@ -279,20 +290,21 @@ __global__ __launch_bounds__(kThreads) void reloc_kernel(const RelocArgs A) {
                 j1 = min(j1, I.move_tiles - 1);
             }
             const uint32_t* f = A.flags + (I.wg_off + layer * I.tiles);
-            for (int j = j0; j <= j1; ++j) {
+            bool ok = true;
+            for (int j = j0; j <= j1 && ok; ++j) {
                 uint32_t n = 0;
                 while (ld_dev(f + j) != A.epoch) {
                     __builtin_amdgcn_s_sleep(2);
-                    if (++n >= kSpinLimit ||
-                        (__hip_atomic_load(&g_errors_relocate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
-                         (KVR_DEV_SPIN_LIMIT | KVR_DEV_BAD_TICKET))) {
-                        raise_error(KVR_DEV_SPIN_LIMIT);
-                        break;
-                    }
+                    if (aborted(A.epoch)) { ok = false; break; }
+                    if (++n >= kSpinLimit) { abort_launch(KVR_DEV_SPIN_LIMIT, A.epoch); ok = false; break; }
                 }
             }
+            // a tile whose wait did not end normally, or of an aborted
+            // launch, stores nothing: its destination may hold unread sources
+            s_store = ok && !aborted(A.epoch);
         }
         __syncthreads();
+        if (!s_store) return;
     }
 
     // ---- stores -----------------------------------------------------------

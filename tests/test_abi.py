@@ -89,10 +89,12 @@ def test_splice_bad_cache_descriptors():
 
 
 def test_splice_workspace_checked():
+    # Delta = -1 over 488 moved rows: chains longer than 64 bands take the
+    # ticketed mover, which needs the workspace
     c = mla_cache()
-    assert splice(c, [(10, 300, 5, 0)], [500], ws=None)[0] == -6
-    assert splice(c, [(10, 300, 5, 0)], [500], ws=FAKE + 16)[0] == -6
-    assert splice(c, [(10, 300, 5, 0)], [500], ws_bytes=8)[0] == -6
+    assert splice(c, [(10, 12, 1, 0)], [500], ws=None)[0] == -6
+    assert splice(c, [(10, 12, 1, 0)], [500], ws=FAKE + 16)[0] == -6
+    assert splice(c, [(10, 12, 1, 0)], [500], ws_bytes=8)[0] == -6
 
 
 def test_forget_only_needs_no_launch():
@@ -103,11 +105,15 @@ def test_forget_only_needs_no_launch():
 def test_splice_workspace_query():
     lib = _abi.load()
     c = mla_cache()
-    D = (_abi.kvr_directive * 2)(_abi.kvr_directive(10, 300, 5, 0, 0), _abi.kvr_directive(0, 0, 0, 0, 0))
+    D = (_abi.kvr_directive * 2)(_abi.kvr_directive(10, 12, 1, 0, 0), _abi.kvr_directive(0, 0, 0, 0, 0))
     Ls = (ctypes.c_int64 * 2)(500, 500)
     nbytes = lib.kvr_splice_workspace_bytes(ctypes.byref(c), 2, Ls, D)
-    # 2 layers x (ceil(200/64) move + 1 stub tile) flags, one counter per unit, 256-byte rounded
+    # ticketed (Delta = -1, 488 moved rows in 32-row tiles): 2 layers x (16 move
+    # + 1 stub tile) flags, one counter per (sequence, layer), 256-byte rounded
     assert nbytes == 256 + 256
+    # a shift of 285 over 200 moved rows walks one band: no workspace at all
+    D[0] = _abi.kvr_directive(10, 300, 5, 0, 0)
+    assert lib.kvr_splice_workspace_bytes(ctypes.byref(c), 2, Ls, D) == 0
 
 
 def gather(c, ents, pts, bt_len=8):

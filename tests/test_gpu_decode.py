@@ -48,8 +48,12 @@ def _run(devs, scale, max_len):
     return ob.to_f64(o), lse.cpu().numpy().astype(np.float64)
 
 
-def _oracle(host, b, scale, pend=None):
-    """(O, LSE, eps_s) of sequence b from the fp64 oracle."""
+def _oracle(host, b, scale, pend=None, round_keys=False):
+    """(O, LSE, eps_s) of sequence b from the fp64 oracle: keys explicitly
+    re-rotated and kept unrounded (or, with round_keys, rounded to bf16 as a
+    stored shifted key would be).  eps_s bounds the score change from a key
+    one bf16 ulp away; only the planted-needle tests, whose keys are 40x
+    larger than the rest, add it to the LSE bar."""
     n = int(host["lens"][b])
     slots = np.arange(n)
     phys = osplice.physical_rows(slots, host["bt"][b], 64)
@@ -59,7 +63,7 @@ def _oracle(host, b, scale, pend=None):
     p = host["pend"] if pend is None else pend
     d = odec.token_deltas(p[b], n, 64)
     qr = ob.to_f64(host["qr"][b])
-    o, lse = odec.mla_decode(ob.to_f64(host["qn"][b]), qr, ckv, kr, d, scale, TH, round_keys=True)
+    o, lse = odec.mla_decode(ob.to_f64(host["qn"][b]), qr, ckv, kr, d, scale, TH, round_keys=round_keys)
     return o, lse, odec.score_bound(qr, kr, d, scale, TH)
 
 
@@ -70,22 +74,28 @@ def test_decode_small(heads):
     scale = 1.0 / math.sqrt(576.0)
     o, lse = _run(devs, scale, max_len=40 * 64)
     for b in range(len(lens)):
-        o_ref, l_ref, eps = _oracle(host, b, scale)
-        ok = tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps)
+        o_ref, l_ref, _ = _oracle(host, b, scale)
+        ok = tolerance.decode_close(o[b], o_ref, lse[b], l_ref)
         assert ok.all(), f"seq {b}: {(~ok).sum()} heads outside tolerance; worst lse err " \
                          f"{np.abs(lse[b] - l_ref).max():.3g}"
 
 
 def test_decode_layer_offset_and_many_splits():
+    """Layer 2 of 3, sequences long enough for several splits, and a
+    one-token sequence.  A single key is not averaged by the softmax: its LSE
+    is its score, so the bf16 rounding of its rotated k_r (a matrix-core
+    operand) shows in full -- up to scale * 2^-9 * sum |q_r| |k_r|, 3e-3 here
+    at scale 0.07.  That sequence is compared with the oracle variant whose
+    shifted keys are rounded to bf16; the long ones with the unrounded one."""
     lens = [3000, 1, 2500]
     host, devs = _setup(3, 128, lens, bt_stride=50, n_layers=3, layer=2, keys=(2,))
     devs["layer"] = 2
     scale = 0.07
     o, lse = _run(devs, scale, max_len=50 * 64)
     for b in range(len(lens)):
-        o_ref, l_ref, eps = _oracle(host, b, scale)
+        o_ref, l_ref, _ = _oracle(host, b, scale, round_keys=lens[b] == 1)
         rel = np.linalg.norm(o[b] - o_ref, axis=1) / np.linalg.norm(o_ref, axis=1)
-        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps).all(), \
+        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref).all(), \
             f"seq {b}: max rel-L2 {rel.max():.3g}, max |dLSE| {np.abs(lse[b] - l_ref).max():.3g}"
 
 
@@ -100,8 +110,8 @@ def test_decode_empty_sequence():
     for b in (0, 2):
         assert (o[b] == 0).all() and np.isneginf(lse[b]).all()
     for b in (1, 3):
-        o_ref, l_ref, eps = _oracle(host, b, scale)
-        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps).all()
+        o_ref, l_ref, _ = _oracle(host, b, scale)
+        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref).all()
     assert rrs.device_errors() == 0
 
 
@@ -122,17 +132,17 @@ def test_decode_large_logits_restart():
         torch.bfloat16).cuda()
     scale = 1.0 / math.sqrt(576.0)
     o, lse = _run(devs, scale, max_len=2048)
-    o_ref, l_ref, eps = _oracle(host, b, scale)
+    o_ref, l_ref, eps = _oracle(host, b, scale, round_keys=True)
     assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps).all()
     ckv_needle = ob.to_f64(host["pool"][0][phys, :512])
     cos = float(o[b][0] @ ckv_needle / np.linalg.norm(o[b][0]) / np.linalg.norm(ckv_needle))
     assert cos > 0.9
 
 
-def test_decode_bf16_key_drift_small():
-    """Against keys kept unrounded in float64 the device stays within the
-    drift the bf16 keys allow: LSE within 2e-3 + eps_s, O within tolerance on
-    unplanted random data."""
+def test_decode_rounded_key_variant_small():
+    """Against the oracle variant whose shifted keys are rounded to bf16 (the
+    keys an eager relocation would have stored) the device is within the same
+    flat bar: the kernel's own bf16 key operands sit between the two."""
     lens = [1000, 2000]
     host, devs = _setup(2, 128, lens, bt_stride=32, keys=(6,))
     scale = 1.0 / math.sqrt(576.0)
@@ -144,9 +154,8 @@ def test_decode_bf16_key_drift_small():
         d = odec.token_deltas(host["pend"][b], n, 64)
         qr = ob.to_f64(host["qr"][b])
         o_ref, l_ref = odec.mla_decode(ob.to_f64(host["qn"][b]), qr, ob.to_f64(rows[:, :512]),
-                                       ob.to_f64(rows[:, 512:]), d, scale, TH)
-        eps = odec.score_bound(qr, ob.to_f64(rows[:, 512:]), d, scale, TH)
-        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps).all()
+                                       ob.to_f64(rows[:, 512:]), d, scale, TH, round_keys=True)
+        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref).all()
 
 
 def test_decode_negative_control_zero_delta():
@@ -159,16 +168,19 @@ def test_decode_negative_control_zero_delta():
     devs["pend"] = torch.zeros_like(devs["pend"])
     o, lse = _run(devs, scale, max_len=24 * 64)
     for b in range(2):
-        o_ref, l_ref, eps = _oracle(host, b, scale)
-        assert not tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps).all()
-        o0, l0, eps0 = _oracle(host, b, scale, pend=np.zeros_like(host["pend"]))
-        assert tolerance.decode_close(o[b], o0, lse[b], l0, eps0).all()
+        o_ref, l_ref, _ = _oracle(host, b, scale)
+        assert not tolerance.decode_close(o[b], o_ref, lse[b], l_ref).all()
+        o0, l0, _ = _oracle(host, b, scale, pend=np.zeros_like(host["pend"]))
+        assert tolerance.decode_close(o[b], o0, lse[b], l0).all()
 
 
 def test_decode_workload_sampled():
     """The full decode workload (batch 32, 32768 tokens, 128 heads, pending
     delta ~ U{-1e5..1e5} per 64-token block) in the launch configuration the
-    benchmark times; sequences 0, 13 and 31 are compared with the oracle."""
+    benchmark times; sequences 0, 13 and 31 are compared with the oracle on
+    explicitly re-rotated, unrounded keys at the flat bar (relative L2 2^-8,
+    max 2^-7, |dLSE| 2e-3), and with the rounded-key variant at the same bar.
+    The measured errors are printed."""
     import torch
     import rope_rotation_splice_amd as rrs
     w = kvsynth.rotate_on_read_decode()
@@ -194,11 +206,15 @@ def test_decode_workload_sampled():
         rows = h16(pool[0].reshape(-1, 576)[torch.from_numpy(phys).cuda()])
         d = odec.token_deltas(w.pending_delta[b], w.ctx, 64)
         kr = ob.to_f64(rows[:, 512:])
-        o_ref, l_ref = odec.mla_decode(ob.to_f64(qn_h[b]), ob.to_f64(qr_h[b]), ob.to_f64(rows[:, :512]),
-                                       kr, d, w.scale, TH, round_keys=True)
-        eps = odec.score_bound(ob.to_f64(qr_h[b]), kr, d, w.scale, TH)
-        ok = tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps)
-        assert ok.all(), f"seq {b}: {(~ok).sum()} heads outside tolerance"
+        for rk in (False, True):
+            o_ref, l_ref = odec.mla_decode(ob.to_f64(qn_h[b]), ob.to_f64(qr_h[b]), ob.to_f64(rows[:, :512]),
+                                           kr, d, w.scale, TH, round_keys=rk)
+            rel = np.linalg.norm(o[b] - o_ref, axis=1) / np.linalg.norm(o_ref, axis=1)
+            dl = np.abs(lse[b] - l_ref)
+            print(f"seq {b} keys {'rounded' if rk else 'unrounded'}: max rel-L2 {rel.max():.3e}, "
+                  f"max |dLSE| {dl.max():.3e}, mean |dLSE| {dl.mean():.3e}")
+            ok = tolerance.decode_close(o[b], o_ref, lse[b], l_ref)
+            assert ok.all(), f"seq {b} ({'rounded' if rk else 'unrounded'} keys): {(~ok).sum()} heads outside"
 
 
 def test_decode_nan_rows_past_length():
@@ -218,5 +234,6 @@ def test_decode_nan_rows_past_length():
     o, lse = _run(devs, scale, max_len=8 * 64)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     for b in range(len(lens)):
-        o_ref, l_ref, eps = _oracle(host, b, scale)
-        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps).all(), f"seq {b}"
+        # a one-token sequence is checked against rounded keys (see the layer-offset test)
+        o_ref, l_ref, _ = _oracle(host, b, scale, round_keys=lens[b] == 1)
+        assert tolerance.decode_close(o[b], o_ref, lse[b], l_ref).all(), f"seq {b}"

@@ -65,8 +65,8 @@ def _oracle(host, b, scale, pend=None, skip_blocks=()):
 
 def _check(o, lse, host, scale, seqs, **kw):
     for b in seqs:
-        o_ref, l_ref, eps = _oracle(host, b, scale, **kw)
-        ok = tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps)
+        o_ref, l_ref, _ = _oracle(host, b, scale, **kw)
+        ok = tolerance.decode_close(o[b], o_ref, lse[b], l_ref)
         rel = np.linalg.norm(o[b] - o_ref, axis=1) / np.linalg.norm(o_ref, axis=1)
         assert ok.all(), f"seq {b}: {(~ok).sum()} heads outside tolerance; max rel-L2 {rel.max():.3g}, " \
                          f"max |dLSE| {np.abs(lse[b] - l_ref).max():.3g}"
@@ -114,8 +114,8 @@ def test_gqa_decode_negative_control_zero_delta():
     devs["pend"] = torch.zeros_like(devs["pend"])
     o, lse = _run(devs, scale, max_len=24 * 64)
     for b in range(2):
-        o_ref, l_ref, eps = _oracle(host, b, scale)
-        assert not tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps).all()
+        o_ref, l_ref, _ = _oracle(host, b, scale)
+        assert not tolerance.decode_close(o[b], o_ref, lse[b], l_ref).all()
     _check(o, lse, host, scale, range(2), pend=np.zeros_like(host["pend"]))
 
 
@@ -208,7 +208,7 @@ def test_gqa_decode_workload_sampled():
         d = odec.token_deltas(w.pending_delta[b], w.ctx, 64)
         qb = ob.to_f64(q_h[b])
         o_ref, l_ref = odec.gqa_decode(qb, k, v, d, w.scale, TH, G)
-        eps = odec.gqa_score_bound(qb, k, d, w.scale, TH, G)
-        ok = tolerance.decode_close(o[b], o_ref, lse[b], l_ref, eps)
+        ok = tolerance.decode_close(o[b], o_ref, lse[b], l_ref)
         rel = np.linalg.norm(o[b] - o_ref, axis=1) / np.linalg.norm(o_ref, axis=1)
+        print(f"seq {b}: max rel-L2 {rel.max():.3e}, max |dLSE| {np.abs(lse[b] - l_ref).max():.3e}")
         assert ok.all(), f"seq {b}: {(~ok).sum()} heads outside tolerance; max rel-L2 {rel.max():.3g}"

@@ -69,6 +69,59 @@ def test_splice_delta_sweep_mla(block_size, delta):
     _run(rc.MLA, 2, block_size, bps, seqs, (block_size, delta + 1000))
 
 
+@pytest.mark.parametrize("delta", [-4096, -8184, 4096])
+def test_splice_shifts_of_the_batched_workload(delta):
+    """Shifts as large as the batched workload draws (|Delta| up to 8184),
+    on two layers with 16K-slot sequences."""
+    cap, B = 16384, 64
+    seqs = []
+    for i, n in enumerate([16000, 12345]):
+        n = min(n, cap - max(delta, 0))
+        s_len = (-delta if delta < 0 else 0) + 40 + 9 * i
+        r_len = s_len + delta
+        s0 = 300 + 77 * i
+        seqs.append((n, s0, s0 + s_len, r_len, 0))
+    _run(rc.MLA, 2, B, cap // B, seqs, (B, delta + 10000))
+
+
+@pytest.mark.parametrize("block_size", [16, 64])
+@pytest.mark.parametrize("delta", [-3000, -700, 700, 3000])
+def test_splice_large_call_and_small_call_paths(block_size, delta):
+    """The same directives as one call of four layers (over 65,536 moved
+    rows in all: the ticketed mover streams it) and as a one-layer call (few
+    rows: chain tiles of the band mover), both checked against the oracle."""
+    cap = 12288
+    seqs = []
+    for i, n in enumerate([12000, 9999, 11111]):
+        n = min(n, cap - max(delta, 0))
+        s_len = max(0, -delta) + 30 + 11 * i
+        r_len = s_len + delta
+        s0 = 200 + 91 * i
+        seqs.append((n, s0, s0 + s_len, r_len, 0))
+    moved = sum(n - s1 for n, s0, s1, r, m in seqs)
+    assert moved * 4 >= 65536 > moved
+    for layers in (4, 1):
+        _run(rc.MLA, layers, block_size, cap // block_size, seqs, (block_size, delta + 20000, layers))
+
+
+@pytest.mark.parametrize("delta", [-65536, 65536, -100000, 100000])
+def test_splice_large_shifts(delta):
+    """|Delta| of 2^16 and 1e5 on one layer: the rotation angle Delta*theta_j
+    must be reduced in double precision (an fp32 angle at 1e5 rad is off by
+    ~4e-3 rad, far outside the 1-ulp bar).  Growth takes a stub of |R| =
+    |S| + Delta rows; a shrink replaces |S| = |R| - Delta rows."""
+    B = 64
+    if delta < 0:
+        s_len, r_len = -delta + 31, 31
+        n = s_len + 3000 + 17
+    else:
+        s_len, r_len = 13, 13 + delta
+        n = 2900
+    cap = -(-(max(n, n + delta)) // B) * B
+    seqs = [(n, 1000, 1000 + s_len, r_len, 0)]
+    _run(rc.MLA, 1, B, cap // B, seqs, (B, abs(delta) % 9973, delta > 0))
+
+
 @pytest.mark.parametrize("delta", [-1, -30, -700, 2, 25, 130])
 def test_splice_block_size_not_a_power_of_two(delta):
     # 24-row blocks: the kernels divide slots by the block size instead of shifting
@@ -161,55 +214,128 @@ def test_single_sequence_workload_with_drift():
     assert rel <= 4.7e-3, rel
 
 
-def test_batched_splice_full_workload_sampled():
-    """The batched-splice workload at full size (64 sequences x 32768 slots x
-    61 layers, 64-row blocks, 147 GB resident), in the launch configuration
-    the benchmark times.  Four (sequence, layer) slabs are compared with the
-    oracle over the whole new length: moved rows, stub rows, untouched prefix."""
+def _check_every_slab(w, cfg):
+    """Splice workload ``w`` (pool filled from seed keys (cfg, 1), stubs from
+    (cfg, 2, b)) and check every (sequence, layer) slab.
+
+    The pool is not copied before the splice: each layer's pre-splice
+    contents are regenerated from their seeds on the device (the same seeded
+    draws that filled the pool), one layer at a time.  Per slab, the oracle's
+    splice (oracle.splice.splice_sequence on the slab's rotary column, with
+    the oracle's slot map) gives the expected rotary words: prefix and stub
+    bit-exact, moved keys within one bf16 ulp of R(Delta) x in fp64.  The
+    position-free words of every new slot are compared bit for bit, on the
+    device, with the old row (or stub row) the oracle's slot map names."""
+    import concurrent.futures as cf
+    import os
     import torch
     import rope_rotation_splice_amd as rrs
     from oracle import splice as osplice, tolerance
-    w = kvsynth.batched_splice()
-    L = w.shape.n_layers
-    pool = torch.empty((L, w.n_blocks, w.block_size, 576), dtype=torch.bfloat16, device="cuda")
-    kvsynth.fill_normal_(pool, 3, 1)
+    L, B = w.shape.n_layers, w.block_size
+    shape = (L, w.n_blocks, B, 576)
+    total = int(np.prod(shape))
+    per_layer = total // L
+    pool = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    kvsynth.fill_normal_(pool, cfg, 1)
     cache = rrs.KVCache.mla(pool)
     bt = torch.from_numpy(w.block_tables).cuda()
     stubs_t, stubs = [], []
     for b in range(w.n_seq):
         st = torch.empty((L, int(w.directives[b, 2]), 576), dtype=torch.bfloat16, device="cuda")
-        kvsynth.fill_normal_(st, 3, 2, b)
+        kvsynth.fill_normal_(st, cfg, 2, b)
         stubs_t.append(st)
         stubs.append(rrs.Rows(st[..., :512], st[..., 512:]))
-    samples = [(0, 0), (29, 30), (63, 60), (13, 7)]
-    h16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    old = torch.empty((w.n_blocks * B, 576), dtype=torch.bfloat16, device="cuda")
+    kvsynth.normal_range_(old, 0, total, cfg, 1)
+    assert torch.equal(old.view(torch.int16), pool[0].reshape(-1, 576).view(torch.int16)), \
+        "regenerating the seeded fill does not reproduce it"
 
-    def rows(b, l):
-        n = int(w.seq_lens[b])
-        phys = osplice.physical_rows(np.arange(n), w.block_tables[b], w.block_size)
-        return h16(pool[l].reshape(-1, 576)[torch.from_numpy(phys).cuda()])
-
-    before = {s: rows(*s) for s in samples}
     new_lens, st = rrs.leyline_splice(cache, bt, w.seq_lens.tolist(),
                                       [tuple(int(x) for x in d) for d in w.directives], stubs)
     torch.cuda.synchronize()
     assert st == 0 and rrs.device_errors() == 0
     th = orope.inv_freq(64, 10000.0)
-    for (b, l) in samples:
+    plans, maps = [], []
+    for b in range(w.n_seq):
         d = w.directives[b]
         p = osplice.plan(int(w.seq_lens[b]), int(d[0]), int(d[1]), int(d[2]), int(d[3]))
         assert new_lens[b] == p.new_len
-        r0 = before[(b, l)]
-        stub = h16(stubs_t[b][l])
-        ex = osplice.splice_sequence(p, r0[:, :512], r0[:, 512:], stub[:, :512], stub[:, 512:], 1, 64, th,
-                                     rope_is_bf16=True)
-        phys = osplice.physical_rows(np.arange(p.new_len), w.block_tables[b], w.block_size)
-        got = h16(pool[l].reshape(-1, 576)[torch.from_numpy(phys).cuda()])
-        assert (got[:, :512] == ex.pf_bits).all(), f"seq {b} layer {l}: position-free words differ"
+        is_stub, idx = osplice.sources(p, np.arange(p.new_len))
+        phys_new = osplice.physical_rows(np.arange(p.new_len), w.block_tables[b], B)
+        phys_old = osplice.physical_rows(np.arange(p.n), w.block_tables[b], B)
+        src_old = osplice.physical_rows(idx[~is_stub], w.block_tables[b], B)
+        plans.append(p)
+        maps.append(tuple(torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in
+                          (phys_new, phys_old, src_old, np.flatnonzero(~is_stub), np.flatnonzero(is_stub),
+                           idx[is_stub])))
+    h16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def rope_check(b, l, old_rp, new_rp, stub_rp):
+        p = plans[b]
+        ex = osplice.splice_sequence(p, np.zeros((p.n, 0), np.uint16), old_rp, np.zeros((len(stub_rp), 0), np.uint16),
+                                     stub_rp, 1, 64, th, rope_is_bf16=True)
         plain = ~ex.rotated
-        assert (got[plain, 512:] == ex.rope_bits[plain]).all(), f"seq {b} layer {l}: unrotated rotary words differ"
-        ok = tolerance.bf16_close(got[ex.rotated, 512:], ex.rope_ref[ex.rotated], ex.pair_norm[ex.rotated])
-        assert ok.all(), f"seq {b} layer {l}: {(~ok).sum()} rotated words outside tolerance"
+        bad = int((new_rp[plain] != ex.rope_bits[plain]).sum())
+        ok = tolerance.bf16_close(new_rp[ex.rotated], ex.rope_ref[ex.rotated], ex.pair_norm[ex.rotated])
+        return b, l, bad, int((~ok).sum()), int(ex.rotated.sum())
+
+    checked, rotated = 0, 0
+    failures = []
+
+    def drain(fs):
+        nonlocal checked, rotated
+        for f in fs:
+            b, l, bad, out, n_rot = f.result()
+            checked += 1
+            rotated += n_rot
+            if bad or out:
+                failures.append(f"seq {b} layer {l}: {bad} unrotated words differ, {out} rotated outside tolerance")
+
+    with cf.ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+        futs = []
+        for l in range(L):
+            if l >= 2:                  # bound the host backlog to two layers of slabs
+                drain(futs[:w.n_seq])
+                futs = futs[w.n_seq:]
+            if l:
+                kvsynth.normal_range_(old, l * per_layer, total, cfg, 1)
+            cur = pool[l].reshape(-1, 576)
+            for b in range(w.n_seq):
+                phys_new, phys_old, src_old, at_old, at_stub, stub_idx = maps[b]
+                got = cur[phys_new]
+                # position-free words of every new slot, bit for bit, on the device
+                pf_ok = torch.equal(got[at_old, :512].view(torch.int16), old[src_old, :512].view(torch.int16))
+                st_ok = torch.equal(got[at_stub, :512].view(torch.int16),
+                                    stubs_t[b][l][stub_idx, :512].view(torch.int16))
+                if not (pf_ok and st_ok):
+                    failures.append(f"seq {b} layer {l}: position-free words differ")
+                futs.append(ex.submit(rope_check, b, l, h16(old[phys_old, 512:]), h16(got[:, 512:]),
+                                      h16(stubs_t[b][l][:, 512:])))
+            print(f"layer {l}: {w.n_seq} slabs queued, {checked} checked", flush=True)
+        drain(futs)
+    print(f"checked {checked} (sequence, layer) slabs, {rotated} rotated rows", flush=True)
+    assert checked == w.n_seq * L
+    assert not failures, failures[:8]
+    return checked
+
+
+@pytest.mark.parametrize("layers", [3, 12])
+def test_batched_splice_every_slab_small(layers):
+    """The every-slab check on a small batched draw (growth allowed, so both
+    shift directions), blocks of 16: three layers take the band mover, twelve
+    the ticketed one."""
+    w = kvsynth.batched_splice(n_seq=6, capacity=4096, n_layers=layers, block_size=16, s_range=(1, 700),
+                               r_range=(0, 900), cfg=31, allow_growth=True)
+    assert _check_every_slab(w, 31) == 6 * layers
+
+
+@pytest.mark.timeout(900)
+def test_batched_splice_full_workload_every_slab():
+    """The batched-splice workload at full size (64 sequences x 32768 slots x
+    61 layers, 64-row blocks, 147 GB resident), in the launch configuration
+    the benchmark times: all 3904 (sequence, layer) slabs checked."""
+    w = kvsynth.batched_splice()
+    assert _check_every_slab(w, 3) == 64 * 61
 
 
 def test_splice_after_decode_on_the_same_stream():
@@ -262,3 +388,35 @@ def test_debug_checks_refuse_shared_or_bad_written_blocks(monkeypatch):
     assert rrs.device_errors() == 0
     # a valid batch passes the checks and the oracle
     _run(rc.MLA, 2, 16, 16, [(250, 20, 30, 5, 0), (200, 64, 70, 40, 0), (100, 10, 50, 0, 1)], (32,))
+
+
+def test_ticket_counter_left_nonzero_is_reported_and_recovered():
+    """The ticketed mover on a workspace whose ticket counter was left
+    nonzero: every workgroup of that (sequence, layer) draws a ticket past
+    its tile count, raises KVR_DEV_BAD_TICKET and returns; the launch is
+    marked aborted, so no tile stores over sources that may not have been
+    read, and every workgroup exits (none waits on a tile that will never
+    publish).  device_errors() reports the bit and zeroes the cached splice
+    workspaces, after which the same splice on a fresh image matches the
+    oracle."""
+    import torch
+    import rope_rotation_splice_amd as rrs
+    from rope_rotation_splice_amd import _abi, api
+    lay, B = rc.MLA, 64
+    seqs = [(1000, 50, 52, 1, 0), (900, 10, 12, 0, 0)]      # Delta -1 and -2: chains of 64+ bands, ticketed
+    lens, dirs = [s[0] for s in seqs], [s[1:] for s in seqs]
+    pf, rp = rc.random_image(lay, 2, 2 * 16 * B, (83,))
+    cache, keep = rc.to_device(lay, pf, rp, 32, B)
+    bt = torch.arange(32, dtype=torch.int32, device="cuda").reshape(2, 16)
+    assert rrs.device_errors() == 0
+    need = rrs.splice_workspace_bytes(cache, lens, dirs)
+    assert need > 0
+    ws = api._workspace(need, cache.device, "splice")
+    ws.view(torch.int32)[0] = 1 << 20          # counter of (sequence 0, layer 0) past its tile count
+    rrs.leyline_splice(cache, bt, lens, dirs)
+    torch.cuda.synchronize()
+    bits = rrs.device_errors()
+    assert bits & _abi.KVR_DEV_BAD_TICKET
+    assert not ws.any(), "device_errors() must zero the cached splice workspace"
+    assert rrs.device_errors() == 0
+    _run(lay, 2, B, 16, [s for s in seqs], (83,), stubs_on=False)

@@ -48,3 +48,16 @@ def test_decode_draws():
     assert w.block_tables.shape == (32, 512) and w.pending_delta.shape == (32, 512)
     assert np.abs(w.pending_delta).max() <= 100000
     assert abs(w.scale - 1 / 24.0) < 1e-15
+
+
+def test_normal_range_regenerates_any_slice_of_a_fill():
+    """normal_range_ reproduces every element range of fill_normal_, across
+    slab boundaries and in the ragged last slab (the full-size parity tests
+    regenerate pre-splice contents this way instead of keeping a copy)."""
+    import torch
+    t = torch.empty(10_000, dtype=torch.bfloat16)
+    kvsynth.fill_normal_(t, 3, 1, slab_elems=1024)
+    for lo, n in [(0, 10000), (5, 17), (1000, 2000), (9000, 1000), (1023, 2), (9999, 1)]:
+        out = torch.empty(n, dtype=torch.bfloat16)
+        kvsynth.normal_range_(out, lo, 10000, 3, 1, slab_elems=1024)
+        assert torch.equal(out, t[lo:lo + n]), (lo, n)
