@@ -73,6 +73,7 @@ typedef int32_t kvr_status;
 #define KVR_E_HIP                (-5) /* HIP runtime/launch error: kvr_last_hip_error() */
 #define KVR_E_WORKSPACE          (-6) /* workspace missing, misaligned or too small */
 #define KVR_E_UNSUPPORTED        (-7) /* valid request this build does not implement */
+#define KVR_E_SCRATCH            (-8) /* leyline_splice_noalloc: call needs more than its scratch */
 
 /* Device error word bits (kvr_device_errors). */
 #define KVR_DEV_BAD_BLOCK   1u  /* a block-table entry was outside [0, n_blocks) */
@@ -210,6 +211,27 @@ kvr_status leyline_splice(const kvr_cache* cache, const int32_t* d_block_tables,
                           const kvr_directive* dirs, const kvr_rows* stubs,
                           int64_t* new_lens, void* d_workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * leyline_splice_noalloc -- leyline_splice for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same splices, arguments and results, with no
+ * workspace argument.  The ticketed mover's counters and flags live in a
+ * device array of the library, kvr_noalloc_scratch_bytes() bytes (8 MiB:
+ * ~2M workgroups per launch, e.g. 64 sequences x 32K slots x 61 layers) that
+ * each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing: it clears the part of the array it uses with a kernel
+ * and launches as leyline_splice does.  Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (different streams, other
+ * host threads) race and must be ordered by the caller.
+ * Errors: as leyline_splice, and KVR_E_SCRATCH when the call needs more than
+ * the array holds.
+ * ---------------------------------------------------------------------- */
+kvr_status leyline_splice_noalloc(const kvr_cache* cache, const int32_t* d_block_tables,
+                                  int32_t bt_stride, int32_t n_seq, const int64_t* seq_lens,
+                                  const kvr_directive* dirs, const kvr_rows* stubs,
+                                  int64_t* new_lens, hipStream_t stream);
+size_t     kvr_noalloc_scratch_bytes(void);
 
 /* ------------------------------------------------------------------------
  * kv_relocate_gather -- copy n registry entries into one paged destination

@@ -8,6 +8,7 @@ loads the library and fails loudly if it has not been built.
 from . import _abi
 from .api import (KVCache, KVRError, LowRank, Rows, device_errors, kv_patch_lowrank,  # noqa: F401
                   kv_relocate_gather, kv_relocate_gather_lazy, LazyBatch, LazyEntry, leyline_splice, leyline_splice_lazy,
+                  leyline_splice_noalloc,
                   mla_decode_rotate_on_read, gqa_decode_rotate_on_read, kamera_patch_factors,
                   registry_chunk_keys,
                   splice_workspace_bytes,

@@ -12,6 +12,7 @@ c_vp, c_size = ctypes.c_void_p, ctypes.c_size_t
 KVR_OK = 0
 KVR_FORGET_NEEDS_PREFILL = 1
 KVR_E_WORKSPACE = -6
+KVR_E_SCRATCH = -8
 KVR_AMORTIZE, KVR_FORGET = 0, 1
 KVR_BF16, KVR_F32 = 0, 1
 KVR_DEV_BAD_BLOCK, KVR_DEV_SPIN_LIMIT, KVR_DEV_BAD_TICKET, KVR_DEV_RANGE, KVR_DEV_BAD_TOKEN = 1, 2, 4, 8, 16
@@ -64,6 +65,9 @@ SIGNATURES = {
     "kvr_splice_workspace_bytes": (c_size, [P(kvr_cache), c_i32, P(c_i64), P(kvr_directive)]),
     "leyline_splice": (c_i32, [P(kvr_cache), c_vp, c_i32, c_i32, P(c_i64), P(kvr_directive), P(kvr_rows),
                                P(c_i64), c_vp, c_size, c_vp]),
+    "leyline_splice_noalloc": (c_i32, [P(kvr_cache), c_vp, c_i32, c_i32, P(c_i64), P(kvr_directive), P(kvr_rows),
+                                       P(c_i64), c_vp]),
+    "kvr_noalloc_scratch_bytes": (c_size, []),
     "kv_relocate_gather": (c_i32, [P(kvr_cache), c_vp, c_i32, P(kvr_rows), P(c_i64), c_i32,
                                    P(kvr_lowrank), P(kvr_lowrank), c_vp]),
     "kv_patch_lowrank": (c_i32, [P(kvr_cache), c_vp, c_i32, c_i32, P(c_i64), P(c_i64), P(kvr_lowrank),

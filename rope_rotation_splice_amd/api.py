@@ -246,14 +246,9 @@ def splice_workspace_bytes(cache, seq_lens, directives):
     return int(lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens.p, dirs.p))
 
 
-def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, workspace=None):
-    """In-place AMORTIZE/FORGET splices, one directive (s_start, s_end, r_len, mode) per sequence.
-
-    block_tables: int32 device tensor [n_seq, blocks_per_seq].  stubs: list of
-    Rows (or None per sequence) holding the prefilled replacement rows.
-    Returns (new_lens int64 array, status) -- status 1 means a FORGET was seen.
-    """
-    lib = _abi.load()
+def _splice_args(cache, block_tables, seq_lens, directives, stubs):
+    """Checked host arrays for leyline_splice and leyline_splice_noalloc:
+    (directives, n, lengths, new-length output, stub array)."""
     dirs, n = _directives(directives)
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.stride(1) != 1:
         raise ValueError("block_tables must be an int32 [n_seq, blocks] tensor with unit last stride")
@@ -273,6 +268,18 @@ def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, worksp
             if s is not None:
                 s.check(cache, f"stubs[{i}]")
                 stub_arr[i] = s.c()
+    return dirs, n, lens, out, stub_arr
+
+
+def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, workspace=None):
+    """In-place AMORTIZE/FORGET splices, one directive (s_start, s_end, r_len, mode) per sequence.
+
+    block_tables: int32 device tensor [n_seq, blocks_per_seq].  stubs: list of
+    Rows (or None per sequence) holding the prefilled replacement rows.
+    Returns (new_lens int64 array, status) -- status 1 means a FORGET was seen.
+    """
+    lib = _abi.load()
+    dirs, n, lens, out, stub_arr = _splice_args(cache, block_tables, seq_lens, directives, stubs)
     stream = torch.cuda.current_stream()
     handle = ctypes.c_void_p(stream.cuda_stream)
 
@@ -292,6 +299,19 @@ def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, worksp
             need = lib.kvr_splice_workspace_bytes(ctypes.byref(cache.c), n, lens.p, dirs.p)
             st = call(_workspace(need, cache.pf.device, "splice", stream))
     _check("leyline_splice", st)
+    return out.values(n), st
+
+
+def leyline_splice_noalloc(cache, block_tables, seq_lens, directives, stubs=None):
+    """leyline_splice without any workspace or allocation: the library's own
+    per-GPU device scratch holds the ordering state (see
+    kvr_noalloc_scratch_bytes).  Calls that overlap on one GPU race.
+    Returns (new_lens int64 array, status)."""
+    lib = _abi.load()
+    dirs, n, lens, out, stub_arr = _splice_args(cache, block_tables, seq_lens, directives, stubs)
+    st = lib.leyline_splice_noalloc(ctypes.byref(cache.c), block_tables.data_ptr(), int(block_tables.stride(0)), n,
+                                    lens.p, dirs.p, stub_arr, out.p, _stream_handle())
+    _check("leyline_splice_noalloc", st)
     return out.values(n), st
 
 

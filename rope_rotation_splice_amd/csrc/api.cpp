@@ -418,6 +418,8 @@ kvr_status run_patch(const Pool& pool, const double* omega, const int32_t* d_bt,
 
 }  // namespace
 
+int32_t kvr::record_hip_error(hipError_t e) { return hip_fail(e); }
+
 extern "C" {
 
 int32_t kvr_abi_version(void) { return KVR_ABI_VERSION; }
@@ -433,6 +435,7 @@ const char* kvr_status_str(kvr_status s) {
         case KVR_E_HIP: return "HIP runtime error";
         case KVR_E_WORKSPACE: return "workspace missing, misaligned or too small";
         case KVR_E_UNSUPPORTED: return "unsupported configuration";
+        case KVR_E_SCRATCH: return "call needs more device scratch than the no-allocation entry point holds";
         default: return "unknown status";
     }
 }

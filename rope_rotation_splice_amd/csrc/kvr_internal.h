@@ -230,6 +230,15 @@ static_assert(sizeof(KeyArgs) <= 4000, "keying arguments too large");
 // Kernel arguments must stay within the 4 KB kernarg budget.
 static_assert(sizeof(RelocArgs) <= 4000, "relocation kernel arguments too large");
 
+// Device scratch of the no-allocation splice (noalloc.hip): the ticketed
+// mover's counters and flags for up to ~2M workgroups per launch.
+#ifndef KVR_NOALLOC_SCRATCH_BYTES
+#define KVR_NOALLOC_SCRATCH_BYTES (8u << 20)
+#endif
+
+// Records a HIP error for kvr_last_hip_error() and returns KVR_E_HIP (api.cpp).
+int32_t record_hip_error(hipError_t e);
+
 // Launchers (relocate.hip).  pf_slots / rope_slots are the per-thread counts
 // of 16-byte position-free chunks and of rotation items a tile needs (powers
 // of two up to 16, rope_slots <= pf_slots); rope_f32 selects fp32 keys.

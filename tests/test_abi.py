@@ -34,7 +34,7 @@ def test_header_functions_exported():
 
 def test_status_strings():
     lib = _abi.load()
-    for s in range(-7, 2):
+    for s in range(-8, 2):
         assert lib.kvr_status_str(s)
     assert lib.kvr_abi_version() == 1
 
