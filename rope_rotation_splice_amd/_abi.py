@@ -93,13 +93,17 @@ _lib = None
 
 
 def load():
-    """Load libkvreloc.so (built in-tree); fail loudly if it is missing."""
+    """Load libkvreloc.so (built in-tree); fail loudly if it is missing.
+
+    KVR_LIBRARY may name another build of the same library (the sanitized
+    host build of the ABI check loads one this way)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python rope_rotation_splice_amd/build.py`")
-    lib = ctypes.CDLL(LIB_PATH)
+    path = os.environ.get("KVR_LIBRARY") or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python rope_rotation_splice_amd/build.py`")
+    lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res

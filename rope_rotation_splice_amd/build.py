@@ -67,5 +67,49 @@ def build(verbose=False):
     return OUT
 
 
+SANITIZED = os.path.join(BUILD_DIR, "sanitized", "libkvreloc.so")
+
+
+def build_sanitized(verbose=False):
+    """A copy of the library whose host code (api.cpp: validation, planning,
+    launches) is built with AddressSanitizer and UndefinedBehaviorSanitizer;
+    the device objects of the last build() are linked in unchanged.  Load it
+    with the sanitizer runtime preloaded (see sanitizer_runtime())."""
+    hipcc = _hipcc()
+    out_dir = os.path.dirname(SANITIZED)
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_obj = os.path.join(out_dir, "api.cpp.o")
+    cmds = [[hipcc, *FLAGS, "-g", *san, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj]]
+    objs = [api_obj] + [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in sources()
+                        if not s.endswith("api.cpp")]
+    cmds.append([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *san, *objs, "-o", SANITIZED])
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitized build failed:\n{r.stdout}\n{r.stderr}")
+    return SANITIZED
+
+
+def sanitizer_runtime():
+    """Path of the AddressSanitizer runtime of the compiler that built the
+    sanitized library (to preload into the process that loads it)."""
+    hipcc = _hipcc()
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc)), "..", "lib", "llvm", "bin", "clang")
+    for c in (clang, "/opt/rocm/llvm/bin/clang"):
+        if os.path.exists(c):
+            r = subprocess.run([c, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+            p = r.stdout.strip()
+            if r.returncode == 0 and os.path.isabs(p) and os.path.exists(p):
+                return p
+    raise RuntimeError("AddressSanitizer runtime not found")
+
+
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    if "--sanitized" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        build(verbose="-v" in sys.argv)
