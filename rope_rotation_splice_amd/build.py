@@ -82,8 +82,10 @@ def build_sanitized(verbose=False):
            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
     api_obj = os.path.join(out_dir, "api.cpp.o")
     cmds = [[hipcc, *FLAGS, "-g", *san, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj]]
-    objs = [api_obj] + [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in sources()
-                        if not s.endswith("api.cpp")]
+    dev = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in sources() if not s.endswith("api.cpp")]
+    if not all(os.path.exists(o) for o in dev):
+        build(verbose)                   # the device objects come from the regular build
+    objs = [api_obj] + dev
     cmds.append([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *san, *objs, "-o", SANITIZED])
     for cmd in cmds:
         if verbose:
