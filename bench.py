@@ -46,6 +46,7 @@ MLA_ROW_BYTES = 1152
 # HBM counters stale (the shared headers and the host side count for all)
 KERNEL_SOURCES = {
     "reloc_kernel": ["relocate.hip"],
+    "band_kernel": ["band.hip"],
     "patch_dma_kernel": ["patch.hip"],
     "patch_kernel": ["patch.hip"],
     "mla_decode_kernel": ["decode.hip", "kvr_lds.h"],
@@ -215,7 +216,7 @@ class Gather:
 
 class Splice:
     name = "single_splice"
-    kernel = "reloc_kernel<splice>"
+    kernel = "band_kernel"
 
     def __init__(self):
         import kvsynth

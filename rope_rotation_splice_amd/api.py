@@ -43,31 +43,37 @@ _DT = {torch.bfloat16: KVR_BF16, torch.float32: KVR_F32}
 # device, so that the checks can be exercised without a GPU.
 
 def _need(cond, msg):
+    """Raise ValueError(msg) unless cond; msg may be a callable that builds
+    the message, so that passing checks format nothing."""
     if not cond:
-        raise ValueError(msg)
+        raise ValueError(msg() if callable(msg) else msg)
 
 
 def _on(t, device, name):
-    _need(t.is_cuda, f"{name} must be a CUDA tensor")
-    _need(t.device == device, f"{name} is on {t.device}, expected {device}")
+    _need(t.is_cuda, lambda: f"{name} must be a CUDA tensor")
+    _need(t.device == device, lambda: f"{name} is on {t.device}, expected {device}")
 
 
 def _i32(t, name, dims=None, contiguous=True):
-    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
-    _need(t.dtype == torch.int32, f"{name} must be int32, got {t.dtype}")
+    _need(isinstance(t, torch.Tensor), lambda: f"{name} must be a torch tensor")
+    _need(t.dtype == torch.int32, lambda: f"{name} must be int32, got {t.dtype}")
     if dims is not None:
-        _need(t.dim() == dims, f"{name} must have {dims} dimensions")
+        _need(t.dim() == dims, lambda: f"{name} must have {dims} dimensions")
     if contiguous:
-        _need(t.is_contiguous(), f"{name} must be contiguous")
+        _need(t.is_contiguous(), lambda: f"{name} must be contiguous")
 
 
 def _tensor(t, name, dtype, shape):
     """dtype, exact shape (None entries free) and contiguity."""
-    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
-    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    if isinstance(t, torch.Tensor) and t.dtype == dtype:
+        sh = t.shape
+        if len(sh) == len(shape) and all(s is None or a == s for a, s in zip(sh, shape)) and t.is_contiguous():
+            return
+    _need(isinstance(t, torch.Tensor), lambda: f"{name} must be a torch tensor")
+    _need(t.dtype == dtype, lambda: f"{name} must be {dtype}, got {t.dtype}")
     _need(t.dim() == len(shape) and all(s is None or int(a) == s for a, s in zip(t.shape, shape)),
-          f"{name} has shape {tuple(t.shape)}, expected {tuple('*' if s is None else s for s in shape)}")
-    _need(t.is_contiguous(), f"{name} must be contiguous")
+          lambda: f"{name} has shape {tuple(t.shape)}, expected {tuple('*' if s is None else s for s in shape)}")
+    _need(t.is_contiguous(), lambda: f"{name} must be contiguous")
 
 
 def _stream_handle():
@@ -129,13 +135,21 @@ class Rows:
     def check(self, cache, name="rows", device=True):
         """Layers, widths, dtypes and (with ``device``) device must match the cache's parts."""
         pf, rp = self.pf, self.rope
-        _need(pf.dim() == 3 and rp.dim() == 3, f"{name}: pf and rope must be [layers, len, width]")
+        ps, rs = pf.shape, rp.shape
+        if (len(ps) == 3 and len(rs) == 3 and ps[0] == cache.n_layers and rs[0] == cache.n_layers and ps[1] == rs[1]
+                and ps[2] == cache.pf.shape[3] and rs[2] == cache.rope.shape[3]
+                and pf.dtype == cache.pf.dtype and rp.dtype == cache.rope.dtype):
+            if device and ps[1]:
+                _on(pf, cache.device, f"{name}.pf")
+                _on(rp, cache.device, f"{name}.rope")
+            return
+        _need(pf.dim() == 3 and rp.dim() == 3, lambda: f"{name}: pf and rope must be [layers, len, width]")
         _need(int(pf.shape[0]) == cache.n_layers and int(rp.shape[0]) == cache.n_layers,
-              f"{name}: {int(pf.shape[0])} layers, the cache has {cache.n_layers}")
-        _need(int(pf.shape[1]) == int(rp.shape[1]), f"{name}: pf and rope lengths differ")
+              lambda: f"{name}: {int(pf.shape[0])} layers, the cache has {cache.n_layers}")
+        _need(int(pf.shape[1]) == int(rp.shape[1]), lambda: f"{name}: pf and rope lengths differ")
         _need(int(pf.shape[2]) == int(cache.pf.shape[3]) and int(rp.shape[2]) == int(cache.rope.shape[3]),
-              f"{name}: widths {int(pf.shape[2])}/{int(rp.shape[2])} differ from the cache's")
-        _need(pf.dtype == cache.pf.dtype and rp.dtype == cache.rope.dtype, f"{name}: dtypes differ from the cache's")
+              lambda: f"{name}: widths {int(pf.shape[2])}/{int(rp.shape[2])} differ from the cache's")
+        _need(pf.dtype == cache.pf.dtype and rp.dtype == cache.rope.dtype, lambda: f"{name}: dtypes differ from the cache's")
         if device and int(pf.shape[1]):
             _on(pf, cache.device, f"{name}.pf")
             _on(rp, cache.device, f"{name}.rope")
@@ -158,7 +172,16 @@ class LowRank:
 
     def check(self, device, layers, rows, width, name="factors", on_device=True):
         U, V = self.U, self.V
-        _need(U.dim() == 3 and V.dim() == 3, f"{name}: U and V must be [layers, n, rank]")
+        if isinstance(U, torch.Tensor) and isinstance(V, torch.Tensor):
+            us, vs = U.shape, V.shape
+            if (len(us) == 3 and len(vs) == 3 and us[0] == layers and us[1] == rows and vs[0] == layers
+                    and vs[1] == width and vs[2] == us[2] and U.dtype == torch.float32 and V.dtype == torch.float32
+                    and U.is_contiguous() and V.is_contiguous()):
+                if on_device and us[0] * us[1] * us[2]:
+                    _on(U, device, f"{name}.U")
+                    _on(V, device, f"{name}.V")
+                return
+        _need(U.dim() == 3 and V.dim() == 3, lambda: f"{name}: U and V must be [layers, n, rank]")
         r = int(U.shape[2])
         _tensor(U, f"{name}.U", torch.float32, (layers, rows, r))
         _tensor(V, f"{name}.V", torch.float32, (layers, width, r))
@@ -513,7 +536,7 @@ def kv_relocate_gather(cache, block_table, entries, p_targets, patch_rope=None, 
         for lst, width, name in patches:
             if lst is None:
                 continue
-            _need(len(lst) == n, f"{name} needs one entry (LowRank or None) per registry entry")
+            _need(len(lst) == n, lambda: f"{name} needs one entry (LowRank or None) per registry entry")
             for i, f in enumerate(lst):
                 if f is not None:
                     f.check(cache.device, cache.n_layers, int(entries[i].pf.shape[1]), width, f"{name}[{i}]",

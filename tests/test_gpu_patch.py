@@ -72,6 +72,13 @@ def test_gqa_gather_patch_block_size_not_a_power_of_two():
     _run(rc.GQA, 2, 24, 16, 2, chunks, 16, 1.0, (25,))
 
 
+def test_gqa_gather_patch_long_entries():
+    # entries of more than 64 sixteen-row stages span several row chunks of
+    # the streaming kernel (1500 rows: 94 stages, the last one ragged)
+    chunks = [(1500, 1234, 64, None), (1025, 0, 2000, None), (16, 70000, 3100, None)]
+    _run(rc.GQA, 2, 64, 52, 2, chunks, 16, 1.0, (26,))
+
+
 def test_gather_patch_keys_only_and_zero_shift():
     chunks = [(40, 40, 40, None), (70, 1000, 100, None)]     # first entry: delta = 0
     _run(rc.GQA, 2, 64, 4, 1, chunks, 16, 1.0, (23,), patch_pf=False)
@@ -83,18 +90,19 @@ def test_mla_gather_patch_both_channels():
     _run(rc.MLA, 3, 64, 6, 2, chunks, 16, 1.0, (24,))
 
 
-@pytest.mark.parametrize("part", [0, 1])
-def test_patch_in_place(part):
+@pytest.mark.parametrize("part,ranges", [(0, [(5, 96), (200, 64), (300, 17), (400, 0)]),
+                                         (1, [(5, 96), (200, 64), (300, 17), (400, 0)]),
+                                         (0, [(3, 1100), (1200, 33)]), (1, [(40, 1041)])])
+def test_patch_in_place(part, ranges):
     import torch
     import rope_rotation_splice_amd as rrs
     lay = rc.GQA
-    L, B, n_dst, spare = 2, 16, 40, 3
-    r = kvsynth.rng(25, part)
+    L, B, n_dst, spare = 2, 16, 80, 3
+    r = kvsynth.rng(25, part, len(ranges))
     n_blocks = n_dst + spare
     bt = r.permutation(n_blocks)[:n_dst].astype(np.int32)
     pf, rp = rc.random_image(lay, L, n_blocks * B, (25, part))
     cache, keep = rc.to_device(lay, pf, rp, n_blocks, B)
-    ranges = [(5, 96), (200, 64), (300, 17), (400, 0)]
     width = lay.pf_width if part == 0 else lay.rope_width
     fh, fd = [], []
     for i, (p, n) in enumerate(ranges):
