@@ -111,16 +111,17 @@ TileShape choose_tile(const Pool& P, bool rope_f32, bool splice) {
     return s;
 }
 
-// Chain tiles of the band mover hold about 36 KB of rows (as the ticketed
-// splice) and at most a block of rows, so that the rows a tile takes from one
-// band span at most two blocks.
-constexpr int kBandBytes = 36864;
+// Chain tiles of the band mover hold about 9 KB of rows (8 MLA rows), and at
+// most a block of rows, so that the rows a tile takes from one band span at
+// most two blocks.  Latency-bound calls finish sooner in many small tiles:
+// the single 4096-slot splice (2,296 rows) took 8.2, 6.6, 6.4, 6.7 and 7.2 us
+// on MI355X with tiles of 32, 16, 8, 4 and 2 rows.
+constexpr int kBandBytes = 9216;
 // Calls that move fewer rows than this (all layers; 256 compute units x 8
 // workgroups x 32 rows) are bound by latency and take the band mover; larger
 // ones stream through the ticketed mover.  Measured on MI355X: the single
-// 4096-slot splice (2,296 rows) takes 8.0 us in chain tiles against 10.0 us
-// ticketed; the 64-sequence batch takes 21.5 ms ticketed against 25.2 ms in
-// chain tiles.
+// splice takes 10.0 us ticketed; the 64-sequence batch takes 21.5 ms ticketed
+// against 25.2 ms in chain tiles.
 constexpr int64_t kBandMaxRows = 65536;
 
 TileShape choose_band(const Pool& P, bool rope_f32) {
