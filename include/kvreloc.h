@@ -161,7 +161,7 @@ typedef struct kvr_lowrank {
     int64_t      u_layer_stride;
     const float* V;
     int64_t      v_layer_stride;
-    int32_t      rank;       /* 0 or 1..64 */
+    int32_t      rank;       /* 0, or a multiple of 4 up to 64 (else KVR_E_ARG) */
     int32_t      reserved;
 } kvr_lowrank;
 

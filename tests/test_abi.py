@@ -140,6 +140,24 @@ def test_gather_validation_errors():
     assert gather(c, [rows(10, base=-(1 << 40))], [0]) == -2       # shift does not fit 32 bits
 
 
+def patch(c, ranks, part=1, bt_len=8):
+    lib = _abi.load()
+    n = len(ranks)
+    F = (_abi.kvr_lowrank * n)(*[_abi.kvr_lowrank(FAKE, 0, FAKE + 4096, 0, r, 0) for r in ranks])
+    P = (ctypes.c_int64 * n)(*[64 * i for i in range(n)])
+    L = (ctypes.c_int64 * n)(*[32] * n)
+    return lib.kv_patch_lowrank(ctypes.byref(c), FAKE, bt_len, part, P, L, F, n, None)
+
+
+def test_patch_rank_validation():
+    c = mla_cache()
+    # ranks must be 0 (no patch) or a multiple of 4 up to 64; these fail before any launch
+    for r in (-4, 1, 5, 18, 66, 68):
+        assert patch(c, [0, r]) == -1, r
+    assert patch(c, [4], part=2) == -1
+    assert patch(c, [4, 4], bt_len=1) == -2        # 64-slot capacity: the second item ends at 96
+
+
 def lazy(dirs, lens, B=64, bt_stride=512, stubs=FAKE, freed=FAKE):
     lib = _abi.load()
     n = len(dirs)
