@@ -76,8 +76,21 @@ def _tensor(t, name, dtype, shape):
     _need(t.is_contiguous(), lambda: f"{name} must be contiguous")
 
 
+# The current device's current stream as a raw handle.  torch's private
+# accessor skips building a Stream object (about 3 us per call); the public
+# route is kept for builds without it.
+_raw_stream_of = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_get_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
+def _raw_stream():
+    if _raw_stream_of is not None and _get_device is not None:
+        return _raw_stream_of(_get_device())
+    return torch.cuda.current_stream().cuda_stream
+
+
 def _stream_handle():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(_raw_stream())
 
 
 def _part(t):
@@ -102,6 +115,8 @@ class KVCache:
             raise ValueError("pf and rope views must live on one device")
         self.pf, self.rope = pf, rope
         self.device = pf.device
+        self.pf_width, self.rope_width = int(pf.shape[3]), int(rope.shape[3])
+        self.pf_dtype, self.rope_dtype = pf.dtype, rope.dtype
         self.n_layers, self.n_blocks, self.block_size = (int(x) for x in pf.shape[:3])
         self.rope_heads, self.rope_dim, self.rope_base = rope_heads, rope_dim, float(rope_base)
         self._inv = None
@@ -137,9 +152,10 @@ class Rows:
         pf, rp = self.pf, self.rope
         ps, rs = pf.shape, rp.shape
         if (len(ps) == 3 and len(rs) == 3 and ps[0] == cache.n_layers and rs[0] == cache.n_layers and ps[1] == rs[1]
-                and ps[2] == cache.pf.shape[3] and rs[2] == cache.rope.shape[3]
-                and pf.dtype == cache.pf.dtype and rp.dtype == cache.rope.dtype):
-            if device and ps[1]:
+                and ps[2] == cache.pf_width and rs[2] == cache.rope_width
+                and pf.dtype == cache.pf_dtype and rp.dtype == cache.rope_dtype):
+            if device and ps[1] and not (pf.is_cuda and rp.is_cuda and pf.device == cache.device
+                                         and rp.device == cache.device):
                 _on(pf, cache.device, f"{name}.pf")
                 _on(rp, cache.device, f"{name}.rope")
             return
@@ -201,12 +217,12 @@ class LowRank:
 _workspaces = {}
 
 
-def _workspace(nbytes, device, kind, stream=None):
+def _workspace(nbytes, device, kind, raw_stream=None):
     """A workspace per (kind, device, stream).  Kinds never share memory: the
     splice's must stay zero-filled between calls (each call leaves it so),
     the decode's holds split partials."""
-    stream = stream if stream is not None else torch.cuda.current_stream()
-    key = (kind, device.index if device.index is not None else torch.cuda.current_device(), stream.cuda_stream)
+    raw_stream = raw_stream if raw_stream is not None else _raw_stream()
+    key = (kind, device.index if device.index is not None else torch.cuda.current_device(), raw_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -287,9 +303,14 @@ def _splice_args(cache, block_tables, seq_lens, directives, stubs):
     stub_arr = None
     if stubs is not None:
         stub_arr = (kvr_rows * max(1, n))()
+        dev = cache.device
         for i, s in enumerate(stubs):
             if s is not None:
-                s.check(cache, f"stubs[{i}]")
+                # structure passed above; now the device
+                if s.pf.shape[1] and not (s.pf.is_cuda and s.rope.is_cuda and s.pf.device == dev
+                                          and s.rope.device == dev):
+                    _on(s.pf, dev, f"stubs[{i}].pf")
+                    _on(s.rope, dev, f"stubs[{i}].rope")
                 stub_arr[i] = s.c()
     return dirs, n, lens, out, stub_arr
 
@@ -303,8 +324,8 @@ def leyline_splice(cache, block_tables, seq_lens, directives, stubs=None, worksp
     """
     lib = _abi.load()
     dirs, n, lens, out, stub_arr = _splice_args(cache, block_tables, seq_lens, directives, stubs)
-    stream = torch.cuda.current_stream()
-    handle = ctypes.c_void_p(stream.cuda_stream)
+    stream = _raw_stream()
+    handle = ctypes.c_void_p(stream)
 
     def call(ws):
         return lib.leyline_splice(ctypes.byref(cache.c), block_tables.data_ptr(), int(block_tables.stride(0)), n,
