@@ -10,10 +10,12 @@
 //    previous tile's last h shifted by lane + 1 where no start intervenes.
 //    Candidates (h_i below the threshold) become a bitmask, one wave ballot
 //    per 64 tokens.
-// 2. cut_kernel: one wave per stream walks the chunk rule; the first
-//    candidate in [p + min_len - 1, p + max_len - 1] is found by scanning 64
-//    bitmask words (4096 tokens) per step, from a window of the bitmask
-//    staged in LDS.
+// 2. cut_kernel: one wave per stream walks the chunk rule (the first
+//    candidate in [p + min_len - 1, p + max_len - 1] ends the chunk from p).
+//    The chunk that follows each candidate is found for all candidates at
+//    once, so the walk reads one table entry per chunk; streams with too many
+//    candidates or too long for the LDS window scan 64 bitmask words per step
+//    instead.
 // 3. fp_kernel: one wave per chunk computes xxHash64 of its tokens' ids
 //    (little-endian int32 bytes) and of its S1 windows, four lanes (the four
 //    stripe accumulators) per hash, 16 hashes side by side.  xxHash64 follows
@@ -167,73 +169,177 @@ __global__ __launch_bounds__(256) void gear_kernel(const KeyArgs A) {
     }
 }
 
-// The walk reads the stream's bitmask from an LDS window of kCutWords words,
-// refilled (coalesced) whenever the scan needs words past it.  Positions are
-// 32-bit and relative to the stream start (a stream is shorter than 2^31
-// tokens); the word found by the ballot is read with readlane, so the walk's
-// state stays wave-uniform (scalar).
+// The walk reads the stream's bitmask from an LDS window of kCutWords words.
+// A stream whose bitmask fits the window and has at most kCutCands
+// candidates is walked through a table: for every candidate c, the chunk end
+// that follows a cut at c (the first candidate in [c + min_len, c + max_len],
+// plus one, else the forced end) is found in parallel by binary search over
+// the sorted candidate positions, and the walk then reads one table entry per
+// chunk.  Other streams take the scan: from the window, refilled (coalesced)
+// whenever it needs words past it, 64 words per step by ballot.  Positions
+// are 32-bit and relative to the stream start (a stream is shorter than 2^31
+// tokens); the walk's state stays wave-uniform.
 constexpr int kCutWords = 4096;
+constexpr int kCutCands = 4096;
 
 __global__ __launch_bounds__(64) void cut_kernel(const KeyArgs A) {
     __shared__ uint64_t win[kCutWords];
+    __shared__ int32_t cpos[kCutCands];      // candidate token positions, ascending
+    __shared__ int2 cnext[kCutCands];        // after a cut at candidate i: (next candidate or -1, its chunk end)
     const int s = blockIdx.x, lane = threadIdx.x;
     const int64_t O = A.offsets[0], S = A.offsets[s];
     const int L = (int)(A.offsets[s + 1] - S);
     const int64_t ws = (S - O) >> 6;         // first bitmask word of the stream
     const int sh = (int)((S - O) & 63);      // bit of the stream's first token in it
     const int wlast = L > 0 ? (sh + L - 1) >> 6 : -1;    // last word, stream-relative
-    int wb = -kCutWords;                     // first word held in win (none yet)
+    const int minl = A.min_len, maxl = A.max_len;
     int32_t* ce = A.chunk_end + (int64_t)s * A.cap;
     int p = 0, k = 0;
-    while (p < L) {
-        const int lo = p + A.min_len - 1, hi = min(p + A.max_len, L) - 1;
-        int end = hi + 1;
-        if (lo <= hi) {
-            const int wlo = (sh + lo) >> 6, whi = (sh + hi) >> 6;
-            const int blo = (sh + lo) & 63, bhi = (sh + hi) & 63;
-            for (int w0 = wlo; w0 <= whi; w0 += 64) {
-                if (w0 < wb || w0 + 64 > wb + kCutWords) {
-                    __syncthreads();
-                    // 16 loads in flight per lane; batches past the stream's end are skipped
-                    for (int j0 = 0; j0 < kCutWords && w0 + j0 <= wlast; j0 += 64 * 16) {
-                        uint64_t r[16];
+
+    // ---- table walk -----------------------------------------------------------
+    int nc = -1;                             // candidates, or -1: take the scan
+    if (L > 0 && wlast < kCutWords) {
+        // the stream's words, bits outside [0, L) cleared
+        for (int w = lane; w <= wlast; w += 64) {
+            uint64_t v = A.cand[ws + w];
+            if (w == 0) v &= ~0ull << sh;
+            const int top = (sh + L - 1) & 63;
+            if (w == wlast && top < 63) v &= (2ull << top) - 1;
+            win[w] = v;
+        }
+        __syncthreads();
+        // lane l counts words [l m, (l + 1) m), then writes their candidates in order
+        const int m = (wlast + 64) >> 6;
+        const int w0 = lane * m, w1 = min(w0 + m, wlast + 1);
+        int cnt = 0;
+        for (int w = w0; w < w1; ++w) cnt += __popcll(win[w]);
+        int incl = cnt;
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {   // clamped: unconditional loads
-                            const int j = j0 + 64 * i + lane;
-                            r[i] = A.cand[ws + min(w0 + j, wlast)];
-                            if (w0 + j > wlast) r[i] = 0;
-                        }
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) win[j0 + 64 * i + lane] = r[i];
-                    }
-                    __syncthreads();
-                    wb = w0;
-                }
-                const int w = w0 + lane;
-                uint64_t bits = 0;
-                if (w <= whi) {
-                    bits = win[w - wb];
-                    if (w == wlo) bits &= ~0ull << blo;
-                    if (w == whi && bhi < 63) bits &= (2ull << bhi) - 1;
-                }
-                const uint64_t any = __ballot(bits != 0);
-                if (any) {
-                    const int first = __ffsll((unsigned long long)any) - 1;
-                    const uint32_t flo = __builtin_amdgcn_readlane((int)(uint32_t)bits, first);
-                    const uint32_t fhi = __builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), first);
-                    const int bit = flo ? __ffs(flo) - 1 : 31 + __ffs(fhi);
-                    end = ((w0 + first) << 6) + bit - sh + 1;
-                    break;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(incl, d);
+            if (lane >= d) incl += u;
+        }
+        nc = __shfl(incl, 63);
+        if (nc <= kCutCands) {
+            int o = incl - cnt;
+            for (int w = w0; w < w1; ++w) {
+                uint64_t v = win[w];
+                while (v) {
+                    const int bit = __ffsll((unsigned long long)v) - 1;
+                    v &= v - 1;
+                    cpos[o++] = (w << 6) + bit - sh;
                 }
             }
+            __syncthreads();
+            // first candidate index >= x among [from, nc)
+            auto first_at = [&](int from, int x) __attribute__((always_inline)) {
+                int lo = from, hi = nc;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (cpos[mid] < x) lo = mid + 1; else hi = mid;
+                }
+                return lo;
+            };
+            // the chunk that starts at q: (its ending candidate or -1, its end)
+            auto chunk_from = [&](int q, int from) __attribute__((always_inline)) -> int2 {
+                const int lo = q + minl - 1, hi = min(q + maxl, L) - 1;
+                if (lo > hi) return make_int2(-1, hi + 1);
+                const int j = first_at(from, lo);
+                if (j < nc && cpos[j] <= hi) return make_int2(j, cpos[j] + 1);
+                return make_int2(-1, hi + 1);
+            };
+            for (int i = lane; i < nc; i += 64) cnext[i] = chunk_from(cpos[i] + 1, i + 1);
+            __syncthreads();
+            // the walk: a table entry per chunk after a candidate cut, a search
+            // after the start and after a forced cut.  Chunk ends collect in
+            // LDS (the window's words are no longer needed) and leave in
+            // coalesced batches.
+            int32_t* ends = reinterpret_cast<int32_t*>(win);
+            constexpr int kEnds = kCutWords * 2;
+            int nb = 0, kb = 0;
+            auto flush = [&]() __attribute__((always_inline)) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                for (int i = lane; i < nb; i += 64) ce[kb + i] = ends[i];
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                kb += nb;
+                nb = 0;
+            };
+            // (the walk's state in scalar registers)
+            const int2 c0 = chunk_from(0, 0);
+            int cx = __builtin_amdgcn_readfirstlane(c0.x), cy = __builtin_amdgcn_readfirstlane(c0.y);
+            while (p < L) {
+                if (k >= A.cap) {            // cannot happen with a valid cap
+                    if (lane == 0) raise_error(KVR_DEV_RANGE);
+                    break;
+                }
+                ends[nb] = cy;               // every lane writes the same value
+                ++nb;
+                ++k;
+                p = cy;
+                if (nb == kEnds) flush();
+                if (p >= L) break;
+                const int2 v = cx >= 0 ? cnext[cx] : chunk_from(p, 0);
+                cx = __builtin_amdgcn_readfirstlane(v.x);
+                cy = __builtin_amdgcn_readfirstlane(v.y);
+            }
+            flush();
         }
-        if (k >= A.cap) {                    // cannot happen with a valid cap
-            if (lane == 0) raise_error(KVR_DEV_RANGE);
-            break;
+        __syncthreads();                     // the scan below refills the window
+    }
+
+    // ---- scan walk --------------------------------------------------------------
+    if (nc < 0 || nc > kCutCands) {
+        int wb = -kCutWords;                 // first word held in win (none yet)
+        while (p < L) {
+            const int lo = p + minl - 1, hi = min(p + maxl, L) - 1;
+            int end = hi + 1;
+            if (lo <= hi) {
+                const int wlo = (sh + lo) >> 6, whi = (sh + hi) >> 6;
+                const int blo = (sh + lo) & 63, bhi = (sh + hi) & 63;
+                for (int w0 = wlo; w0 <= whi; w0 += 64) {
+                    if (w0 < wb || w0 + 64 > wb + kCutWords) {
+                        __syncthreads();
+                        // 16 loads in flight per lane; batches past the stream's end are skipped
+                        for (int j0 = 0; j0 < kCutWords && w0 + j0 <= wlast; j0 += 64 * 16) {
+                            uint64_t r[16];
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) {   // clamped: unconditional loads
+                                const int j = j0 + 64 * i + lane;
+                                r[i] = A.cand[ws + min(w0 + j, wlast)];
+                                if (w0 + j > wlast) r[i] = 0;
+                            }
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) win[j0 + 64 * i + lane] = r[i];
+                        }
+                        __syncthreads();
+                        wb = w0;
+                    }
+                    const int w = w0 + lane;
+                    uint64_t bits = 0;
+                    if (w <= whi) {
+                        bits = win[w - wb];
+                        if (w == wlo) bits &= ~0ull << blo;
+                        if (w == whi && bhi < 63) bits &= (2ull << bhi) - 1;
+                    }
+                    const uint64_t any = __ballot(bits != 0);
+                    if (any) {
+                        const int first = __ffsll((unsigned long long)any) - 1;
+                        const uint32_t flo = __builtin_amdgcn_readlane((int)(uint32_t)bits, first);
+                        const uint32_t fhi = __builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), first);
+                        const int bit = flo ? __ffs(flo) - 1 : 31 + __ffs(fhi);
+                        end = ((w0 + first) << 6) + bit - sh + 1;
+                        break;
+                    }
+                }
+            }
+            if (k >= A.cap) {                // cannot happen with a valid cap
+                if (lane == 0) raise_error(KVR_DEV_RANGE);
+                break;
+            }
+            if (lane == 0) ce[k] = end;
+            ++k;
+            p = end;
         }
-        if (lane == 0) ce[k] = end;
-        ++k;
-        p = end;
     }
     if (lane == 0) A.n_chunks[s] = k;
 }

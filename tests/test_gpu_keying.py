@@ -131,3 +131,23 @@ def test_keys_long_stream_window_refill():
     off, out = _run(streams, gear, 1 << 56, 64, 2048, 128, with_hash=False)
     assert rrs.device_errors() == 0
     _check(streams, gear, 1 << 56, 64, 2048, 128, 0, off, out, check_hash=False)
+
+
+def test_keys_table_walk_limits():
+    """The cut walk's table covers at most 4096 candidates per stream: a
+    stream with ~10000 candidates takes the word scan instead, one with a few
+    hundred the table.  Forced two-token chunks over 40000 tokens (about
+    20000 chunks) fill the walk's on-chip list of chunk ends more than twice."""
+    import rope_rotation_splice_amd as rrs
+    r = kvsynth.rng(31, 5)
+    gear = r.integers(0, 2 ** 64, size=7000, dtype=np.uint64)
+    many = [r.integers(0, 7000, size=20000), r.integers(0, 7000, size=3000)]
+    off, out = _run(many, gear, 1 << 63, 1, 9, 4, seed=5, with_hash=False)
+    assert rrs.device_errors() == 0
+    assert int(out["n_chunks"][0]) > 4096
+    _check(many, gear, 1 << 63, 1, 9, 4, 5, off, out, check_hash=False)
+    forced = [r.integers(0, 7000, size=40000)]
+    off, out = _run(forced, gear, 1 << 40, 1, 2, 2, seed=6, with_hash=False)
+    assert rrs.device_errors() == 0
+    assert int(out["n_chunks"][0]) > 2 * 8192
+    _check(forced, gear, 1 << 40, 1, 2, 2, 6, off, out, check_hash=False)
