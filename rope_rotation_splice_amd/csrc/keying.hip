@@ -357,6 +357,7 @@ __global__ __launch_bounds__(64) void cut_kernel(const KeyArgs A) {
 constexpr int kFpPiece = 2048;
 constexpr int kFpHalo = 8;
 constexpr int kFpGrid = 4096;
+constexpr int kFpUnroll = 8;            // stripes whose words are read ahead of their rounds
 
 __global__ __launch_bounds__(64) void fp_kernel(const KeyArgs A) {
     __shared__ int32_t buf[kFpPiece + 2 * kFpHalo];
@@ -419,7 +420,17 @@ __global__ __launch_bounds__(64) void fp_kernel(const KeyArgs A) {
                 const int d0 = base - st, d1 = base + kFpPiece - st;
                 const int q0 = d0 <= 0 ? 0 : (d0 + 7) >> 3;
                 const int q1 = d1 <= 0 ? 0 : min(ns, (d1 + 7) >> 3);
-                for (int q = q0; q < q1; ++q) v = xround(v, two_tokens(b0 + st + 8 * q + 2 * acc));
+                // the lane words of kFpUnroll stripes are read from LDS before their
+                // rounds run, so the dependent rounds do not wait on each read
+                int q = q0;
+                for (; q + kFpUnroll <= q1; q += kFpUnroll) {
+                    uint64_t wv[kFpUnroll];
+#pragma unroll
+                    for (int u = 0; u < kFpUnroll; ++u) wv[u] = two_tokens(b0 + st + 8 * (q + u) + 2 * acc);
+#pragma unroll
+                    for (int u = 0; u < kFpUnroll; ++u) v = xround(v, wv[u]);
+                }
+                for (; q < q1; ++q) v = xround(v, two_tokens(b0 + st + 8 * q + 2 * acc));
                 const uint32_t vlo = (uint32_t)v, vhi = (uint32_t)(v >> 32);
                 uint64_t va[4];
 #pragma unroll
