@@ -6,7 +6,8 @@
 //    token's contribution out after 64 steps, so h_i is the sum over the
 //    last 64 tokens of gear[tok] * 2^age (clipped at the stream start).  A
 //    64-token tile is a segmented scan under (a, b) -> (a << d) + b, six
-//    shift-add steps across the wave that restart at stream starts, plus the
+//    shift-add steps across the wave (DPP row shifts, then row broadcasts)
+//    that restart at stream starts, plus the
 //    previous tile's last h shifted by lane + 1 where no start intervenes.
 //    Candidates (h_i below the threshold) become a bitmask, one wave ballot
 //    per 64 tokens.
@@ -89,8 +90,12 @@ __device__ __forceinline__ uint64_t xxh_tail(uint64_t h, const int32_t* t, int r
 // span's token ids and Gear values are loaded before the scans.
 constexpr int kGearTiles = 8;
 
-__device__ __forceinline__ uint64_t shfl_up64(uint64_t v, int d) {
-    const uint32_t lo = __shfl_up((uint32_t)v, d), hi = __shfl_up((uint32_t)(v >> 32), d);
+// A 64-bit DPP move: lane i takes the value the DPP control names (0 where
+// its source lane is outside the row or the wave).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
     return (uint64_t)lo | ((uint64_t)hi << 32);
 }
 
@@ -101,10 +106,15 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
 }
 
 __global__ __launch_bounds__(256) void gear_kernel(const KeyArgs A) {
+    // the stream starts, staged in LDS: the searches below read them there
+    // instead of through the scalar cache
+    __shared__ int64_t s_off[kKeyMaxStreams + 1];
+    for (int i = threadIdx.x; i <= A.n_streams; i += 256) s_off[i] = A.offsets[i];
     const int lane = threadIdx.x & 63;
     const int64_t O = A.offsets[0];
     const int64_t ntiles = (A.total - O + 63) >> 6;
     const int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kGearTiles;
+    __syncthreads();
     if (t0 >= ntiles) return;
     const int64_t tw = t0 > 0 ? t0 - 1 : 0;  // first tile scanned (the warm-up one unless t0 == 0)
     const int nt = (int)(min<int64_t>(t0 + kGearTiles, ntiles) - tw);
@@ -135,7 +145,7 @@ __global__ __launch_bounds__(256) void gear_kernel(const KeyArgs A) {
     int sidx = 0, shi = A.n_streams;
     while (sidx < shi) {
         const int mid = (sidx + shi) >> 1;
-        if (A.offsets[mid] < first) sidx = mid + 1; else shi = mid;
+        if (s_off[mid] < first) sidx = mid + 1; else shi = mid;
     }
     uint64_t carry = 0;                      // h just before the tile
 #pragma unroll
@@ -143,19 +153,29 @@ __global__ __launch_bounds__(256) void gear_kernel(const KeyArgs A) {
         if (j < nt) {
             const int64_t tile0 = O + ((tw + j) << 6);
             uint64_t F = 0;                      // stream starts inside the tile
-            while (sidx < A.n_streams && A.offsets[sidx] < tile0 + 64) {
-                F |= 1ull << (A.offsets[sidx] - tile0);
+            while (sidx < A.n_streams && s_off[sidx] < tile0 + 64) {
+                F |= 1ull << (s_off[sidx] - tile0);
                 ++sidx;
             }
             const uint64_t m = lane == 63 ? F : F & ((2ull << lane) - 1);
             const int hd = m ? 63 - __clzll((long long)m) : -1;    // this position's stream start in the tile
             // segmented scan: v = sum over [max(hd, 0), lane] of g_j 2^(lane - j)
+            // within each 16-lane row by row shifts (row_shr 1, 2, 4, 8), then
+            // across rows: lane 15 of rows 0 and 2 into rows 1 and 3
+            // (row_bcast 15), lane 31 into rows 2 and 3 (row_bcast 31); a
+            // source before this position's stream start adds nothing
             uint64_t v = gv[j];
-#pragma unroll
-            for (int dd = 1; dd < 64; dd <<= 1) {
-                const uint64_t u = shfl_up64(v, dd);
-                if (lane >= dd && lane - dd >= hd) v += u << dd;
+            const int li = lane & 15;
+            { const uint64_t u = dpp64<0x111>(v); if (li >= 1 && lane - 1 >= hd) v += u << 1; }
+            { const uint64_t u = dpp64<0x112>(v); if (li >= 2 && lane - 2 >= hd) v += u << 2; }
+            { const uint64_t u = dpp64<0x114>(v); if (li >= 4 && lane - 4 >= hd) v += u << 4; }
+            { const uint64_t u = dpp64<0x118>(v); if (li >= 8 && lane - 8 >= hd) v += u << 8; }
+            {
+                const uint64_t u = dpp64<0x142>(v);
+                const int src = (lane & ~15) - 1;
+                if (((lane >> 4) & 1) && src >= hd) v += u << (lane - src);
             }
+            { const uint64_t u = dpp64<0x143>(v); if (lane >= 32 && 31 >= hd) v += u << (lane - 31); }
             if (hd < 0 && lane < 63) v += carry << (lane + 1);
             carry = readlane64(v, 63);
             if (tw + j >= t0) {
