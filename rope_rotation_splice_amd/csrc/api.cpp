@@ -904,16 +904,30 @@ kvr_status kamera_patch_factors(const float* d_deficits, int32_t n, int32_t orde
     g.n = n;
     g.rows = rows;
     g.cols = cols;
-    // Y = D Omega; twice: Z = D^T Y, Z = orth(Z), Y = D Z
-    g.X = d_omega; g.x_stride = 0; g.Y = Y; g.y_stride = (int64_t)rows * kFormSketch;
-    if ((e = launch_form_gemm(g, false, stream)) != hipSuccess) return hip_fail(e);
-    for (int step = 0; step < 2; ++step) {
-        g.X = Y; g.x_stride = (int64_t)rows * kFormSketch; g.Y = Z; g.y_stride = (int64_t)cols * kFormSketch;
-        if ((e = launch_form_gemm(g, true, stream)) != hipSuccess) return hip_fail(e);
-        FormOrthArgs o{Z, cols};
+    // Y = D Omega; twice: Z = D^T Y, Z = orth(Z), Y = D Z.  For widths the
+    // one-pass kernel takes, each Z = D^T (D X) is one pass over D (X = Omega,
+    // then the orthonormalized Z) and only the last Y is formed.
+    const bool one_pass = cols % 256 == 0 && cols <= kFormPowerMaxCols;
+    FormOrthArgs o{Z, cols};
+    if (one_pass) {
+        g.X = d_omega; g.x_stride = 0; g.Y = Z; g.y_stride = (int64_t)cols * kFormSketch;
+        if ((e = launch_form_power(g, stream)) != hipSuccess) return hip_fail(e);
         if ((e = launch_form_orth(o, n, stream)) != hipSuccess) return hip_fail(e);
-        g.X = Z; g.x_stride = (int64_t)cols * kFormSketch; g.Y = Y; g.y_stride = (int64_t)rows * kFormSketch;
+        g.X = Z; g.x_stride = (int64_t)cols * kFormSketch;       // in place: a wave reads its rows of X
+        if ((e = launch_form_power(g, stream)) != hipSuccess) return hip_fail(e);   // before it writes them
+        if ((e = launch_form_orth(o, n, stream)) != hipSuccess) return hip_fail(e);
+        g.Y = Y; g.y_stride = (int64_t)rows * kFormSketch;
         if ((e = launch_form_gemm(g, false, stream)) != hipSuccess) return hip_fail(e);
+    } else {
+        g.X = d_omega; g.x_stride = 0; g.Y = Y; g.y_stride = (int64_t)rows * kFormSketch;
+        if ((e = launch_form_gemm(g, false, stream)) != hipSuccess) return hip_fail(e);
+        for (int step = 0; step < 2; ++step) {
+            g.X = Y; g.x_stride = (int64_t)rows * kFormSketch; g.Y = Z; g.y_stride = (int64_t)cols * kFormSketch;
+            if ((e = launch_form_gemm(g, true, stream)) != hipSuccess) return hip_fail(e);
+            if ((e = launch_form_orth(o, n, stream)) != hipSuccess) return hip_fail(e);
+            g.X = Z; g.x_stride = (int64_t)cols * kFormSketch; g.Y = Y; g.y_stride = (int64_t)rows * kFormSketch;
+            if ((e = launch_form_gemm(g, false, stream)) != hipSuccess) return hip_fail(e);
+        }
     }
     FormEigArgs ea{Y, Z, d_U, d_V, d_sigma, rows, cols, rank};
     e = launch_form_eig(ea, n, stream);

@@ -152,6 +152,7 @@ struct GqaDecodeArgs {
 // Patch formation (patch_form.hip).
 constexpr int kFormSketch = 32;       // columns of the range finder's sketch
 constexpr int kFormMaxRank = 16;
+constexpr int kFormPowerMaxCols = 1024;  // widest deficit the one-pass power step takes
 
 struct FormGemmArgs {
     const float* D; int64_t d_stride;          // deficits, [n][rows][cols], stride in floats
@@ -258,6 +259,7 @@ hipError_t launch_decode(const DecodeArgs& a, uint16_t* out, float* lse, hipStre
 uint32_t read_and_clear_errors_decode();
 // Patch formation (patch_form.hip).
 hipError_t launch_form_gemm(const FormGemmArgs& a, bool trans, hipStream_t s);
+hipError_t launch_form_power(const FormGemmArgs& a, hipStream_t s);   // Z = D^T (D X), cols 256 k, k <= 4
 hipError_t launch_form_orth(const FormOrthArgs& a, int count, hipStream_t s);
 hipError_t launch_form_eig(const FormEigArgs& a, int count, hipStream_t s);
 hipError_t launch_form_mean(const float* d, int orders, int64_t per, int64_t n, float* out, hipStream_t s);

@@ -11,9 +11,25 @@
 //   V_m = V W_m,  U_m Sigma_m = Y W_m,  sigma = sqrt(Lambda_m)
 // so that U V^T is the best rank-m approximation of Delta up to the
 // sketch's error ((sigma_33 / sigma_m)^5 per power step pair) and float32
-// rounding.  Omega is drawn by the caller.
+// rounding.  Omega is drawn by the caller.  For deficits of 256, 512, 768 or
+// 1024 columns each power step Z = Delta^T (Delta X) is one pass over Delta
+// (power_kernel, X = Omega and then the orthonormalized Z): three passes
+// over every deficit instead of five.
 //
 // Kernels:
+// * power_kernel<NCT>: Z = Delta^T (Delta X), cols = 256 NCT, Y never leaves
+//   the chip.  One workgroup of 8 waves per deficit; wave w owns the column
+//   slice c0 = 32 NCT w .. + 32 NCT - 1: its rows of X (B operand of the Y
+//   step) and of Z (accumulators) stay in registers for the whole deficit.
+//   Delta is walked in stages of 16 rows (all columns), global -> LDS
+//   directly, one stage ahead.  Per stage: each wave multiplies its
+//   16 x 32 NCT slice by its X rows (v_mfma_f32_16x16x4f32) into a partial
+//   Y; the 8 partials are summed through LDS; then Z[slice] += slice^T Y on
+//   v_mfma_f32_32x32x16_bf16 with both operands split exactly into three
+//   bf16 parts (six of the nine part products: float32 accuracy).  Stage
+//   rows are laid out in LDS with chunk c of row r at (c & ~15) |
+//   ((c & 15) ^ swz(r)), swz(r) = (r & 15) ^ 8 (r & 1): the row reads of the
+//   Y step and the column reads of the Z step touch every bank once.
 // * sketch_gemm_kernel<TRANS>: Y = Delta X (or Delta^T X) for every
 //   deficit, X with 32 columns.  One workgroup per (deficit, 64 output
 //   rows); K is walked in stages of 64 rows whose Delta block (16 KB) and X
@@ -31,13 +47,18 @@
 //   The direct loads come from inline assembly with exact vmcnt waits, and
 //   the loop holds no other memory access the compiler would wait on.
 // * orth_kernel: shifted CholeskyQR3 of Z (cols x 32) in place -- Gram on
-//   the matrix cores, Cholesky and the triangular inverse in the registers
-//   of one wave (a row per lane, other rows' entries broadcast by readlane),
-//   the update Z L^-T on the matrix cores; the first pass adds the shift
-//   11 (n k + k (k + 1)) u ||Z||_F^2 to the Gram diagonal, which keeps the
-//   Cholesky factorization defined for any conditioning, and columns whose
-//   pivot falls to 1e-8 of the largest are dropped (a deficit of rank below
-//   32 gives a sketch of lower rank: the basis then has zero columns).
+//   the matrix cores (float64 in the second pass), Cholesky and the
+//   triangular inverse in float64 in the registers of one wave (a row per
+//   lane, other rows' entries broadcast by readlane), the update Z L^-T on
+//   the float32 matrix cores;
+//   the first pass adds the shift 11 (n k + k (k + 1)) u ||Z||_F^2 to the
+//   Gram diagonal, and columns whose pivot falls to u^2 of the largest are
+//   dropped (a deficit of rank below 32 gives a sketch of lower rank: the
+//   basis then has zero columns).  A sketch that meets the test matrix
+//   badly is ill-conditioned (condition ~1e5 and more): after the shifted
+//   pass its weakest genuine direction leaves a pivot below float32
+//   rounding (~1e-8 of the largest), which a float32 factorization could
+//   turn negative and drop for good; in float64 it is kept.
 // * eig_kernel: Gram of Y, cyclic Jacobi (tournament ordering: 16 disjoint
 //   rotations per round, 31 rounds per sweep; each thread applies a round to
 //   one 2 x 2 block of the Gram matrix and to two entry pairs of W;
@@ -182,6 +203,188 @@ __global__ __launch_bounds__(256) void sketch_gemm_kernel(const FormGemmArgs A) 
     }
 }
 
+// One power step Z = Delta^T (Delta X) in a single pass over Delta
+// (power_kernel in the header).
+constexpr int kPwWaves = 8;
+constexpr int kPwRows = 16;                                   // Delta rows per stage
+constexpr int kPwStageB = kPwRows * kFormPowerMaxCols * 4;    // 64 KB
+constexpr int kPwEPitch = 36;                                 // floats per row of a partial Y
+constexpr int kPwEOff = 2 * kPwStageB;
+constexpr int kPwFOff = kPwEOff + kPwWaves * kPwRows * kPwEPitch * 4;
+constexpr int kPwFPitch = 20;                                // floats per column of Y (rows 0..15 used)
+constexpr int kPwSmem = kPwFOff + kSk * kPwFPitch * 4;
+static_assert(kPwSmem <= 160 * 1024, "LDS budget");
+
+// chunk permutation of stage row r (a bijection of 0..15)
+__device__ __forceinline__ uint32_t pw_swz(int r) { return (uint32_t)((r & 15) ^ ((r & 1) << 3)); }
+__device__ __forceinline__ uint32_t pw_pos(int c, int r) { return (uint32_t)(c & ~15) | (((uint32_t)c & 15u) ^ pw_swz(r)); }
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// The high halves of two floats as one pair of bf16 (a in the low half).
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// x = h + m + l exactly, each part a bf16: h keeps x's leading 8
+// significant bits (truncated), m the leading 8 of the remainder and l the
+// at most 8 bits left.  A product x y then equals the sum of the nine part
+// products; the six kept (hh, hm, mh, hl, lh, mm) leave out terms below
+// 2^-23 |x y|.
+__device__ __forceinline__ void split3(const float (&x)[8], v8bf& h, v8bf& m, v8bf& l) {
+    v4u H, M, L;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t xa = __float_as_uint(x[2 * p]), xb = __float_as_uint(x[2 * p + 1]);
+        const float ra = x[2 * p] - __uint_as_float(xa & 0xffff0000u);
+        const float rb = x[2 * p + 1] - __uint_as_float(xb & 0xffff0000u);
+        const uint32_t ma = __float_as_uint(ra), mb = __float_as_uint(rb);
+        const float la = ra - __uint_as_float(ma & 0xffff0000u);
+        const float lb = rb - __uint_as_float(mb & 0xffff0000u);
+        H[p] = hi_pair(xa, xb);
+        M[p] = hi_pair(ma, mb);
+        L[p] = hi_pair(__float_as_uint(la), __float_as_uint(lb));
+    }
+    h = as_bf(H);
+    m = as_bf(M);
+    l = as_bf(L);
+}
+
+template <int NCT>
+__global__ __launch_bounds__(kPwWaves * 64) void power_kernel(const FormGemmArgs A) {
+    __shared__ __attribute__((aligned(1024))) char smem[kPwSmem];
+    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
+    constexpr int kCols = 256 * NCT, kChunks = kCols / 4;        // 16-byte chunks per row
+    constexpr uint32_t kRowB = 4u * kCols;
+    typedef const __attribute__((address_space(3))) float* lds_f;
+    typedef const __attribute__((address_space(3))) v4f* lds_f4;
+    typedef __attribute__((address_space(3))) float* lds_fw;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i = lane & 15, q = lane >> 4;          // 16 x 16 x 4 operand coordinates
+    const int n32 = lane & 31, h = lane >> 5;        // 32 x 32 x 2 operand coordinates
+    const int b = blockIdx.x;
+    const char* D = reinterpret_cast<const char*>(A.D + (int64_t)b * A.d_stride);
+    const float* X = A.X + (int64_t)b * A.x_stride;
+    const int c0 = 32 * NCT * w;
+    const int nst = A.rows / kPwRows;
+
+    // X rows of the slice, B operand of the Y step: lane (i, q) supplies
+    // K index c0 + 16 kb + 4 q + kk of columns i and 16 + i
+    float xb[2][2 * NCT][4];
+#pragma unroll
+    for (int kb = 0; kb < 2 * NCT; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const float* xr = X + (int64_t)(c0 + 16 * kb + 4 * q + kk) * kSk;
+            xb[0][kb][kk] = xr[i];
+            xb[1][kb][kk] = xr[16 + i];
+        }
+    // every load so far has landed (a wait the compiler also accounts for,
+    // so it adds none later that would drain the direct loads)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    // Direct loads of stage s: the stage (16 rows, all columns) is 4 KB x
+    // NCT per row; wave w's load u fills LDS slots 64 (8 u + w) .. + 63, slot
+    // g holding chunk pw_pos(g % kChunks, r) of row r = g / kChunks.
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        const uint32_t buf = lds0 + (uint32_t)(s & 1) * kPwStageB;
+        const char* base = D + (int64_t)s * kPwRows * kRowB;
+#pragma unroll
+        for (int u = 0; u < 2 * NCT; ++u) {
+            const int g = 64 * (8 * u + w) + lane;
+            const int r = g / kChunks, p = g - r * kChunks;
+            dma16(base, (uint32_t)r * kRowB + 16u * pw_pos(p, r), buf + 1024u * (uint32_t)(8 * u + w));
+        }
+    };
+
+    v16f zacc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) zacc[ct] = v16f{};
+    lds_fw E = (lds_fw)(size_t)(lds0 + kPwEOff);
+    lds_fw F = (lds_fw)(size_t)(lds0 + kPwFOff);
+
+    issue(0);
+    for (int s = 0; s < nst; ++s) {
+        wait_vmcnt<0>();                 // this wave's part of stage s landed
+        __syncthreads();                 // every wave's part; stage s - 1's buffer is free
+        if (s + 1 < nst) issue(s + 1);
+        const uint32_t buf = lds0 + (uint32_t)(s & 1) * kPwStageB;
+
+        // Y step: partial Y (16 x 32) of this slice; lane (i, q) reads a float4
+        // of row i covering K indices c0 + 16 kb + 4 q .. + 3
+        v4f y0 = {0, 0, 0, 0}, y1 = y0;
+        {
+            v4f av[2 * NCT];
+            const uint32_t arow = buf + (uint32_t)i * kRowB;
+#pragma unroll
+            for (int kb = 0; kb < 2 * NCT; ++kb)
+                av[kb] = *(lds_f4)(size_t)(arow + 16u * pw_pos(c0 / 4 + 4 * kb + q, i));
+#pragma unroll
+            for (int kb = 0; kb < 2 * NCT; ++kb)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    y0 = mfma4(av[kb][kk], xb[0][kb][kk], y0);
+                    y1 = mfma4(av[kb][kk], xb[1][kb][kk], y1);
+                }
+        }
+        // rows 4 q + r, columns i and 16 + i of this wave's partial
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            E[(w * kPwRows + 4 * q + r) * kPwEPitch + i] = y0[r];
+            E[(w * kPwRows + 4 * q + r) * kPwEPitch + 16 + i] = y1[r];
+        }
+        __syncthreads();
+        // Y = the sum of the 8 partials; thread (w, lane) forms row w + 8 h, column n32
+        {
+            const int rr = w + 8 * h;
+            float acc = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < kPwWaves; ++w2) acc += E[(w2 * kPwRows + rr) * kPwEPitch + n32];
+            F[n32 * kPwFPitch + rr] = acc;
+        }
+        __syncthreads();
+
+        // Z step: Z[slice] += slice^T Y, K = the 16 rows, on
+        // v_mfma_f32_32x32x16_bf16 with both operands split in three (six
+        // products per tile).  Lane (n32, h) supplies rows 8 h .. 8 h + 7 of
+        // column c0 + 32 ct + n32 (A) and of Y's column n32 (B).
+        v8bf bh, bm, bl;
+        {
+            const v4f y0v = *(lds_f4)(size_t)(lds0 + kPwFOff + 4u * (uint32_t)(n32 * kPwFPitch + 8 * h));
+            const v4f y1v = *(lds_f4)(size_t)(lds0 + kPwFOff + 4u * (uint32_t)(n32 * kPwFPitch + 8 * h + 4));
+            const float yv[8] = {y0v[0], y0v[1], y0v[2], y0v[3], y1v[0], y1v[1], y1v[2], y1v[3]};
+            split3(yv, bh, bm, bl);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            float a[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int r = 8 * h + t;
+                a[t] = *(lds_f)(size_t)(buf + (uint32_t)r * kRowB +
+                                        16u * pw_pos(c0 / 4 + 8 * ct + (n32 >> 2), r) + 4u * (uint32_t)(n32 & 3));
+            }
+            v8bf ah, am, al;
+            split3(a, ah, am, al);
+            v16f z = zacc[ct];
+            z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bm, z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bh, z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bm, z, 0, 0, 0);
+            zacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, z, 0, 0, 0);
+        }
+    }
+    wait_vmcnt<0>();                     // no direct load may land after the workgroup ends
+
+    // Z rows c0 + 32 ct + 8 (e / 4) + 4 h + e % 4, column n32
+    float* Z = A.Y + (int64_t)b * A.y_stride;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            Z[(int64_t)(c0 + 32 * ct + 8 * (e >> 2) + 4 * h + (e & 3)) * kSk + n32] = zacc[ct][e];
+}
+
 // Gram G = Z^T Z of a [n x 32] matrix (n a multiple of 64) into sG
 // (32 x 33): wave w computes the 16 x 16 tile (w / 2, w % 2); the loads of
 // 64 rows are in flight together.
@@ -204,74 +407,118 @@ __device__ __forceinline__ void gram32(const float* Z, int n, float (*sG)[33], i
     for (int r = 0; r < 4; ++r) sG[16 * (w >> 1) + 4 * q + r][16 * (w & 1) + i] = acc[r];
 }
 
+// The same Gram matrix accumulated in float64 (v_mfma_f64_16x16x4f64, the
+// products of the float32 entries are exact): its pivots keep their
+// meaning far below float32 rounding.  That instruction leaves output rows
+// q + 4 r (not 4 q + r) of column i in lane (i, q).
+typedef double v4d __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void gram32_f64(const float* Z, int n, double (*sG)[33], int tid) {
+    const int lane = tid & 63, w = tid >> 6, i = lane & 15, q = lane >> 4;
+    const int ma = 16 * (w >> 1) + i, nb = 16 * (w & 1) + i;
+    v4d acc = {0, 0, 0, 0};
+    for (int k0 = 0; k0 < n; k0 += 64) {
+        float a[16], b[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const float* row = Z + (int64_t)(k0 + 16 * (u >> 2) + 4 * q + (u & 3)) * kSk;
+            a[u] = row[ma];
+            b[u] = row[nb];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[u], (double)b[u], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sG[16 * (w >> 1) + q + 4 * r][16 * (w & 1) + i] = acc[r];
+}
+
+// value of v in lane l (l uniform), float64
+__device__ __forceinline__ double rld(double v, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// One wave factors a 32 x 32 Gram matrix in float64 registers and writes
+// L^-1 to sLi (float): lane i (< 32) holds row i in g[], and the values a
+// step needs from other rows are broadcast with readlane (lanes 32..63
+// mirror lanes 0..31 and store nothing).  `shift` adds the first pass's
+// diagonal shift.
+__device__ __forceinline__ void chol_inverse(double (&g)[32], float (*sLi)[36], int n, bool shift, int lane) {
+    const int ri = lane & 31;
+    if (shift) {
+        // shift 11 (n k + k (k + 1)) u tr(G), u = 2^-24 (Z is float32), k = 32
+        double tr = 0;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) tr += rld(g[k], k);
+        const double sh = 11.0 * (double)(n * 32 + 32 * 33) * 0x1p-24 * tr;
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+            if (k == ri) g[k] += sh;
+    }
+    // Cholesky G = L L^T, right-looking, lower triangle.  A pivot --
+    // the squared norm of column j orthogonal to the earlier columns
+    // -- at or below u^2 = 2^-48 of the largest diagonal entry (Z's own
+    // float32 rounding) marks column j as dependent: it is dropped
+    // (its row of L^-1 is zero, so Z's column j becomes 0).
+    double dmax = 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) dmax = fmax(dmax, rld(g[k], k));
+    const double tau = 0x1p-48 * dmax;
+    uint32_t dead = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const double piv = rld(g[j], j);
+        if (piv <= tau) {
+            dead |= 1u << j;
+            g[j] = ri == j ? 1.0 : (ri > j ? 0.0 : g[j]);
+            continue;
+        }
+        const double dj = sqrt(piv);
+        const double lij = g[j] / dj;
+        g[j] = ri == j ? dj : (ri > j ? lij : g[j]);
+#pragma unroll
+        for (int k = j + 1; k < 32; ++k) {
+            const double lkj = rld(g[j], k);        // L[k][j]
+            if (ri >= k) g[k] -= lij * lkj;
+        }
+    }
+    // L^-1 by forward substitution, lane c builds column c; rows of
+    // dropped columns are zero
+    double x[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+        double s = r == ri ? 1.0 : 0.0;
+#pragma unroll
+        for (int k = 0; k < r; ++k) s -= rld(g[k], r) * x[k];     // L[r][k]
+        x[r] = (r < ri || ((dead >> r) & 1u)) ? 0.0 : s / rld(g[r], r);
+    }
+    if (lane < 32) {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) sLi[r][lane] = (float)x[r];
+    }
+}
+
 __global__ __launch_bounds__(256) void orth_kernel(const FormOrthArgs A) {
-    __shared__ float sG[32][33];
+    __shared__ float sGf[32][33];
+    __shared__ double sGd[32][33];
     __shared__ __attribute__((aligned(16))) float sLi[32][36];
     const int tid = threadIdx.x, lane = tid & 63;
     float* Z = A.Z + (int64_t)blockIdx.x * A.n * kSk;
     for (int pass = 0; pass < 3; ++pass) {
-        gram32(Z, A.n, sG, tid);
+        // The factorization runs in float64.  The second pass's Gram matrix
+        // -- of the shifted pass's output, whose weakest genuine directions
+        // may sit below float32 rounding -- is accumulated in float64 too;
+        // the first (shifted) and last (near-orthonormal) ones in float32.
+        if (pass == 1) gram32_f64(Z, A.n, sGd, tid);
+        else           gram32(Z, A.n, sGf, tid);
         __syncthreads();
         if (tid < 64) {
-            // One wave factors the 32 x 32 Gram matrix in registers: lane i
-            // (< 32) holds row i in g[], and the values a step needs from
-            // other rows are broadcast with readlane (lanes 32..63 mirror
-            // lanes 0..31 and store nothing).
             const int ri = lane & 31;
-            float g[32];
+            double g[32];
 #pragma unroll
-            for (int k = 0; k < 32; ++k) g[k] = sG[ri][k];
-            if (pass == 0) {
-                // shift 11 (n k + k (k + 1)) u tr(G), u = 2^-24, k = 32
-                float tr = 0.f;
-#pragma unroll
-                for (int k = 0; k < 32; ++k) tr += rl(g[k], k);
-                const float sh = 11.f * (float)(A.n * 32 + 32 * 33) * 5.9604645e-8f * tr;
-#pragma unroll
-                for (int k = 0; k < 32; ++k)
-                    if (k == ri) g[k] += sh;
-            }
-            // Cholesky G = L L^T, right-looking, lower triangle.  A pivot --
-            // the squared norm of column j orthogonal to the earlier columns
-            // -- at or below 1e-8 of the largest diagonal entry marks column
-            // j as dependent: it is dropped (its row of L^-1 is zero, so Z's
-            // column j becomes 0).
-            float dmax = 0.f;
-#pragma unroll
-            for (int k = 0; k < 32; ++k) dmax = fmaxf(dmax, rl(g[k], k));
-            const float tau = 1e-8f * dmax;
-            uint32_t dead = 0;
-#pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const float piv = rl(g[j], j);
-                if (piv <= tau) {
-                    dead |= 1u << j;
-                    g[j] = ri == j ? 1.f : (ri > j ? 0.f : g[j]);
-                    continue;
-                }
-                const float dj = sqrtf(piv);
-                const float lij = g[j] / dj;
-                g[j] = ri == j ? dj : (ri > j ? lij : g[j]);
-#pragma unroll
-                for (int k = j + 1; k < 32; ++k) {
-                    const float lkj = rl(g[j], k);          // L[k][j]
-                    if (ri >= k) g[k] -= lij * lkj;
-                }
-            }
-            // L^-1 by forward substitution, lane c builds column c; rows of
-            // dropped columns are zero
-            float x[32];
-#pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                float s = r == ri ? 1.f : 0.f;
-#pragma unroll
-                for (int k = 0; k < r; ++k) s -= rl(g[k], r) * x[k];      // L[r][k]
-                x[r] = (r < ri || ((dead >> r) & 1u)) ? 0.f : s / rl(g[r], r);
-            }
-            if (lane < 32) {
-#pragma unroll
-                for (int r = 0; r < 32; ++r) sLi[r][lane] = x[r];
-            }
+            for (int k = 0; k < 32; ++k) g[k] = pass == 1 ? sGd[ri][k] : (double)sGf[ri][k];
+            chol_inverse(g, sLi, A.n, pass == 0, lane);
         }
         __syncthreads();
         // Z <- Z L^-T on the matrix cores: Z'[row][j] = sum_c Z[row][c] Li[j][c].
@@ -474,6 +721,18 @@ hipError_t launch_form_gemm(const FormGemmArgs& a, bool trans, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)a.n * (M / kTm)));
     if (trans) hipLaunchKernelGGL(sketch_gemm_kernel<true>, grid, dim3(256), 0, s, a);
     else       hipLaunchKernelGGL(sketch_gemm_kernel<false>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_form_power(const FormGemmArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)a.n), block(kPwWaves * 64);
+    switch (a.cols) {
+        case 256: hipLaunchKernelGGL(power_kernel<1>, grid, block, 0, s, a); break;
+        case 512: hipLaunchKernelGGL(power_kernel<2>, grid, block, 0, s, a); break;
+        case 768: hipLaunchKernelGGL(power_kernel<3>, grid, block, 0, s, a); break;
+        case 1024: hipLaunchKernelGGL(power_kernel<4>, grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -68,6 +68,29 @@ def test_formation_tall_and_wide():
             _check(d[b].cpu().double().numpy(), U[b], V[b], s[b], 16)
 
 
+def test_formation_one_pass_widths():
+    """Column counts 512, 768 and 1024 with few rows: the one-pass power
+    step at each of its slice widths (256 columns are covered above; 128,
+    192 and 576 take the two-pass form)."""
+    for rows, cols in [(64, 512), (320, 768), (128, 1024)]:
+        d = _deficits(2, rows, cols, (6, cols))
+        U, V, s = _run(d, 16, _omega(cols, 5))
+        for b in range(2):
+            _check(d[b].cpu().double().numpy(), U[b], V[b], s[b], 16)
+
+
+def test_formation_weak_sketch_direction():
+    """Deficits whose sketch Delta^T Delta Omega is ill-conditioned (the
+    last of these four meets Omega's columns at a singular value of ~1e-2
+    of the top-32 subspace): the orthonormalization's second pass then
+    sees a genuine direction at a pivot of ~2e-8 of the largest, which must
+    be kept, not dropped as dependent."""
+    d = _deficits(4, 128, 1024, (6, 1024))
+    U, V, s = _run(d, 16, _omega(1024, 5))
+    for b in range(4):
+        _check(d[b].cpu().double().numpy(), U[b], V[b], s[b], 16)
+
+
 def test_orbit_patch_of_the_mean_deficit():
     """Four orders per matrix (the chunk's low-rank directions, with
     order-specific noise at 5x the usual level): the factors are those of
