@@ -51,7 +51,7 @@ KERNEL_SOURCES = {
     "patch_kernel": ["patch.hip"],
     "mla_decode_kernel": ["decode.hip", "kvr_lds.h"],
     "gqa_decode_kernel": ["gqa_decode.hip", "kvr_lds.h"],
-    "sketch_gemm_kernel": ["patch_form.hip"],
+    "power_kernel": ["patch_form.hip"],
 }
 SHARED_SOURCES = ["kvr_device.h", "kvr_internal.h", "api.cpp"]
 
@@ -805,10 +805,15 @@ class PatchForm:
     """Kamera patch formation on the GQA patch shape: 32 layers x 16 chunks x
     2 tensors = 1024 deficits of 1024 tokens x 1024 features (float32,
     energy in 32 feature directions), rank-16 factors by the randomized range
-    finder (32-column sketch, two power steps: five passes over each
+    finder (32-column sketch, two power steps: five products with each
     deficit).  With orders > 1 (the orbit patch) each deficit is the mean of
-    that many order-specific deficits.  A unit is one deficit factored."""
-    kernel = "sketch_gemm_kernel + orth + eig"
+    that many order-specific deficits.  A unit is one deficit factored.
+
+    For widths that are a multiple of 256 up to 1024 (this workload's), each
+    power step Z = Delta^T (Delta X) is one pass over the deficit, so a step
+    reads every deficit three times (two power steps and the final
+    Y = Delta Z) for its five products; wider deficits take five passes."""
+    kernel = "power_kernel + sketch_gemm + orth + eig"
     dtype = "f32"
     unit = "deficits/s"
     metric = "deficits factored/sec (rank-m patch factors by randomized SVD)"
@@ -821,11 +826,17 @@ class PatchForm:
         self.name = "patch_formation" if orders == 1 else "orbit_patch"
         per = w.rows * w.cols * 4
         self.slots = w.n
-        # the mean of the orders (read them, write the mean), five sketch
-        # passes over each deficit, the 32-column sketches, the factors
+        # the mean of the orders (read them, write the mean), the passes over
+        # each deficit, the 32-column sketches (one pass: Z written, then
+        # read and written by each orthonormalization and the second power
+        # step, read by the last product and the eigensolve: 9 Z-sized
+        # transfers; Y written once and read once), the factors
         mean = w.n * per * (w.orders + 1) if w.orders > 1 else 0
-        sk = w.n * (w.rows + w.cols) * w.sketch * 4
-        self.bytes = mean + 5 * w.n * per + 5 * sk + w.n * ((w.rows + w.cols) * w.rank + w.rank) * 4
+        one_pass = w.cols % 256 == 0 and w.cols <= 1024
+        passes = 3 if one_pass else 5
+        zb, yb = w.n * w.cols * w.sketch * 4, w.n * w.rows * w.sketch * 4
+        sk = 9 * zb + 2 * yb if one_pass else 9 * zb + 6 * yb
+        self.bytes = mean + passes * w.n * per + sk + w.n * ((w.rows + w.cols) * w.rank + w.rank) * 4
         self.flops = 5 * 2 * w.n * w.rows * w.cols * w.sketch
         self.launches = 1
         self.config = {"workload": "kamera_patch_formation" if orders == 1 else "kamera_orbit_patch",
