@@ -531,7 +531,19 @@ kvr_status leyline_splice(const kvr_cache* cache, const int32_t* d_block_tables,
             nwg += (int64_t)L[i].item.tiles * cache->n_layers;
         }
         a.n_wg = (int32_t)nwg;
-        hipError_t e = launch_band(a, pl.band.pfi, pl.band.rs, cache->rope_dtype == KVR_F32, stream);
+        const bool one = L.size() == 1;
+        if (one) {
+            // the item's (cos, sin) per pair, reduced and evaluated in float64
+            // (the kernel's own table reduces in float64 and evaluates in float32)
+            const double shift = L[0].item.shift;
+            for (int j = 0; j < kMaxPairs; ++j) {
+                const double u = shift * pl.omega[j];
+                const double f = u - std::nearbyint(u);
+                a.cs[2 * j] = (float)std::cos(2.0 * M_PI * f);
+                a.cs[2 * j + 1] = (float)std::sin(2.0 * M_PI * f);
+            }
+        }
+        hipError_t e = launch_band(a, pl.band.pfi, pl.band.rs, cache->rope_dtype == KVR_F32, one, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
     for (auto& L : pl.launches) {

@@ -56,7 +56,13 @@ __device__ __forceinline__ uint64_t mad64(uint32_t a, uint32_t b, uint64_t c) { 
 // the last row of each chain; a tile copies the ones of its offsets after its
 // last group.  All other stub rows overlap no source and are copied by the
 // stub workgroups.
-template <int PFI, int RS, bool RF32>
+//
+// One-item launches (ONE: a single sequence, the common small call) skip the
+// search for the workgroup's item and take the item's (cos, sin) table from
+// the arguments.  Both would otherwise be chains of dependent reads of the
+// argument block before the first row load: on MI355X they cost about 0.9
+// and 0.4 us of a 6.5 us single-sequence splice.
+template <int PFI, int RS, bool RF32, bool ONE>
 __global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
     __shared__ float2 s_cs[kMaxPairs];
     __shared__ int32_t s_blk[4 * kBandMaxBands];
@@ -66,8 +72,10 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
     const int bid = blockIdx.x;
     const Pool& P = A.pool;
     int it = 0;
+    if (!ONE) {
 #pragma unroll
-    for (int i = 1; i < kMaxItems; ++i) it += bid >= A.offs[i] ? 1 : 0;
+        for (int i = 1; i < kMaxItems; ++i) it += bid >= A.offs[i] ? 1 : 0;
+    }
     const Item& I = A.items[it];
     const int local = bid - I.wg_off;
     const int layer = local / I.tiles;
@@ -197,7 +205,11 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
         s_blk[tid] = b;
         if (!(w & 1)) s_r0[2 * k + (w >> 1)] = in_block(slot);
     }
-    angle_table(s_cs, A.omega, P.n_pairs, I.shift, tid);
+    if (ONE) {
+        if (tid < P.n_pairs) s_cs[tid] = make_float2(A.cs[2 * tid], A.cs[2 * tid + 1]);
+    } else {
+        angle_table(s_cs, A.omega, P.n_pairs, I.shift, tid);
+    }
     __syncthreads();
 
     // tile row -> (band within the group, offset within the tile)
@@ -311,24 +323,24 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
     }
 }
 
-template <int PFI, int RS>
+template <int PFI, int RS, bool ONE>
 hipError_t launch_band_one(const RelocArgs& a, bool f32, hipStream_t s) {
-    if (f32) hipLaunchKernelGGL((band_kernel<PFI, RS, true>), dim3(a.n_wg), dim3(kThreads), 0, s, a);
-    else     hipLaunchKernelGGL((band_kernel<PFI, RS, false>), dim3(a.n_wg), dim3(kThreads), 0, s, a);
+    if (f32) hipLaunchKernelGGL((band_kernel<PFI, RS, true, ONE>), dim3(a.n_wg), dim3(kThreads), 0, s, a);
+    else     hipLaunchKernelGGL((band_kernel<PFI, RS, false, ONE>), dim3(a.n_wg), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 // Instantiated shapes: rotary slots RS in {1, 2, 4} (fp32 keys: {1, 2}),
 // RS <= PFI; the host lowers the tile height until its shape is one of them.
-template <int PFI>
+template <int PFI, bool ONE>
 hipError_t launch_band_rs(const RelocArgs& a, int rs, bool f32, hipStream_t s) {
     switch (rs) {
-        case 1: return launch_band_one<PFI, 1>(a, f32, s);
-        case 2: if (PFI >= 2) return launch_band_one<PFI, (PFI >= 2 ? 2 : 1)>(a, f32, s); break;
+        case 1: return launch_band_one<PFI, 1, ONE>(a, f32, s);
+        case 2: if (PFI >= 2) return launch_band_one<PFI, (PFI >= 2 ? 2 : 1), ONE>(a, f32, s); break;
         case 4:
             if (PFI >= 4 && !f32) {
-                hipLaunchKernelGGL((band_kernel<PFI, (PFI >= 4 ? 4 : 1), false>), dim3(a.n_wg), dim3(kThreads), 0,
-                                   s, a);
+                hipLaunchKernelGGL((band_kernel<PFI, (PFI >= 4 ? 4 : 1), false, ONE>), dim3(a.n_wg), dim3(kThreads),
+                                   0, s, a);
                 return hipGetLastError();
             }
             break;
@@ -336,17 +348,22 @@ hipError_t launch_band_rs(const RelocArgs& a, int rs, bool f32, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-}  // namespace
-
-hipError_t launch_band(const RelocArgs& a, int pfi, int rs, bool f32, hipStream_t s) {
+template <bool ONE>
+hipError_t launch_band_pfi(const RelocArgs& a, int pfi, int rs, bool f32, hipStream_t s) {
     switch (pfi) {
-        case 1: return launch_band_rs<1>(a, rs, f32, s);
-        case 2: return launch_band_rs<2>(a, rs, f32, s);
-        case 4: return launch_band_rs<4>(a, rs, f32, s);
-        case 8: return launch_band_rs<8>(a, rs, f32, s);
-        case 16: return launch_band_rs<16>(a, rs, f32, s);
+        case 1: return launch_band_rs<1, ONE>(a, rs, f32, s);
+        case 2: return launch_band_rs<2, ONE>(a, rs, f32, s);
+        case 4: return launch_band_rs<4, ONE>(a, rs, f32, s);
+        case 8: return launch_band_rs<8, ONE>(a, rs, f32, s);
+        case 16: return launch_band_rs<16, ONE>(a, rs, f32, s);
     }
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_band(const RelocArgs& a, int pfi, int rs, bool f32, bool one_item, hipStream_t s) {
+    return one_item ? launch_band_pfi<true>(a, pfi, rs, f32, s) : launch_band_pfi<false>(a, pfi, rs, f32, s);
 }
 
 uint32_t read_and_clear_errors_band() {

@@ -63,7 +63,11 @@ struct RelocArgs {
     uint32_t epoch;       // value a flag takes when set in this launch
     int32_t n_wg;
     int32_t n_tiles;      // gather: tiles per layer, all items
-    double omega[kMaxPairs];   // theta_j / (2 pi): revolutions per position
+    union {
+        double omega[kMaxPairs];   // theta_j / (2 pi): revolutions per position
+        float cs[2 * kMaxPairs];   // one-item band mover: (cos, sin) of its item's shift per pair,
+                                   // formed on the host in float64
+    };
     Item items[kMaxItems];
     int32_t offs[kMaxItems];   // items[i].wg_off side by side, INT32_MAX past n_items:
                                // a workgroup finds its item in one scalar pass
@@ -245,8 +249,9 @@ int32_t record_hip_error(hipError_t e);
 // of two up to 16, rope_slots <= pf_slots); rope_f32 selects fp32 keys.
 hipError_t launch_splice(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
 // Band mover (in-place splice without cross-workgroup ordering): tile_rows
-// is the band height (<= block size), the slot counts as above.
-hipError_t launch_band(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
+// is the band height (<= block size), the slot counts as above.  one_item:
+// the launch holds a single item and carries its (cos, sin) table in cs.
+hipError_t launch_band(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, bool one_item, hipStream_t s);
 uint32_t read_and_clear_errors_band();
 hipError_t launch_gather(const RelocArgs& a, int pf_slots, int rope_slots, bool rope_f32, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
