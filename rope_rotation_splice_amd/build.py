@@ -27,6 +27,14 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  band.hip: its kernel's leading scalar arguments are
+# preloaded into scalar registers at launch (gfx950 kernarg preloading; the
+# compiler also emits the fallback that loads them itself).
+SOURCE_FLAGS = {
+    "band.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+}
+
+
 def _hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -45,7 +53,7 @@ def build(verbose=False):
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *FLAGS, "-c", src, "-o", obj]
+        cmd = [hipcc, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -62,8 +62,18 @@ __device__ __forceinline__ uint64_t mad64(uint32_t a, uint32_t b, uint64_t c) { 
 // the arguments.  Both would otherwise be chains of dependent reads of the
 // argument block before the first row load: on MI355X they cost about 0.9
 // and 0.4 us of a 6.5 us single-sequence splice.
+//
+// The values the block-table staging needs come first, as scalar arguments
+// (the item's table row, its slots, shift, moved rows and tile counts, the
+// tile height and the block size).  Built with kernarg preloading, they
+// arrive in scalar registers at launch, so a one-item launch issues its
+// staging lookups at once, while the argument block is still being read.
+// Launches of several items pass their first item's values and ignore them.
 template <int PFI, int RS, bool RF32, bool ONE>
-__global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
+__global__ __launch_bounds__(kThreads) void band_kernel(const int32_t* lead_bt, int32_t lead_a, int32_t lead_b,
+                                                        int32_t lead_shift, int32_t lead_moved, int32_t lead_tiles,
+                                                        int32_t lead_move_tiles, int32_t lead_r_len, int32_t lead_tr,
+                                                        int32_t lead_bs, const RelocArgs A) {
     __shared__ float2 s_cs[kMaxPairs];
     __shared__ int32_t s_blk[4 * kBandMaxBands];
     __shared__ int32_t s_r0[2 * kBandMaxBands];
@@ -77,26 +87,32 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
         for (int i = 1; i < kMaxItems; ++i) it += bid >= A.offs[i] ? 1 : 0;
     }
     const Item& I = A.items[it];
-    const int local = bid - I.wg_off;
-    const int layer = local / I.tiles;
-    const int t = local - layer * I.tiles;
-    const int32_t* bt = A.bt + I.bt_off;
+    // the item's scalars: from the leading arguments in a one-item launch
+    const int Ia = ONE ? lead_a : I.a, Ib = ONE ? lead_b : I.b, Ishift = ONE ? lead_shift : I.shift;
+    const int Imoved = ONE ? lead_moved : I.moved, Itiles = ONE ? lead_tiles : I.tiles;
+    const int Imove_tiles = ONE ? lead_move_tiles : I.move_tiles, Ir_len = ONE ? lead_r_len : I.r_len;
+    const int Bsz = ONE ? lead_bs : P.block_size;
+    const int bs_shift = ONE ? ((Bsz & (Bsz - 1)) == 0 ? __builtin_ctz((unsigned)Bsz) : -1) : P.bs_shift;
+    const int local = ONE ? bid : bid - I.wg_off;
+    const int layer = local / Itiles;
+    const int t = local - layer * Itiles;
+    const int32_t* bt = ONE ? lead_bt : A.bt + I.bt_off;
     const unsigned nb = (unsigned)P.n_blocks;
-    auto bt_index = [&](int slot) { return P.bs_shift >= 0 ? (slot >> P.bs_shift) : slot / P.block_size; };
+    auto bt_index = [&](int slot) { return bs_shift >= 0 ? (slot >> bs_shift) : slot / Bsz; };
     auto in_block = [&](int slot) {
-        return P.bs_shift >= 0 ? (slot & (P.block_size - 1)) : slot - (slot / P.block_size) * P.block_size;
+        return bs_shift >= 0 ? (slot & (Bsz - 1)) : slot - (slot / Bsz) * Bsz;
     };
     const char* pfl = P.pf + (int64_t)layer * P.pf_l;
     const char* rpl = P.rp + (int64_t)layer * P.rp_l;
     const uint32_t pf_b = (uint32_t)P.pf_b, pf_r = (uint32_t)P.pf_r;    // host-checked < 2^32
     const uint32_t rp_b = (uint32_t)P.rp_b, rp_r = (uint32_t)P.rp_r;
     const int pfc = P.pf_chunks, ri = P.rope_items;
-    const int L = I.shift < 0 ? -I.shift : I.shift;
-    const int M = I.moved;
+    const int L = Ishift < 0 ? -Ishift : Ishift;
+    const int M = Imoved;
     const int span = min(L, M);
-    const int S = I.a - I.b;               // |S|: stub row S + i lands on moved row i's source slot
-    const bool mirror = I.shift > 0;
-    const int TR = A.tile_rows;
+    const int S = Ia - Ib;                 // |S|: stub row S + i lands on moved row i's source slot
+    const bool mirror = Ishift > 0;
+    const int TR = ONE ? lead_tr : A.tile_rows;
 
     // this thread's items: 16-byte chunks of the position-free part and (lo,
     // hi) chunk pairs of the rotary part of tile rows 0..TR-1 (row TR: none)
@@ -125,15 +141,15 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
         }
     }
 
-    const int B = P.block_size;
-    if (t >= I.move_tiles) {
+    const int B = Bsz;
+    if (t >= Imove_tiles) {
         // ---- stub rows that overlap no source --------------------------------
         // Rows [r0, r0 + n) of the stub land on consecutive slots from
-        // I.b + r0, in at most two blocks (TR <= block size).
-        const int r0 = (t - I.move_tiles) * TR;
-        const int n = min(TR, I.r_len - r0);
+        // Ib + r0, in at most two blocks (TR <= block size).
+        const int r0 = (t - Imove_tiles) * TR;
+        const int n = min(TR, Ir_len - r0);
         if (tid < 2) {
-            const int slot = I.b + r0 + (tid ? n - 1 : 0);
+            const int slot = Ib + r0 + (tid ? n - 1 : 0);
             int b = bt[bt_index(slot)];
             if ((unsigned)b >= nb) { raise_error(KVR_DEV_BAD_BLOCK); b = -1; }
             s_blk[tid] = b;
@@ -192,14 +208,14 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
     const int o0 = t * TO;
     const int nrow = min(TO, span - o0);
     const int Kt = (M - o0 + L - 1) / L;       // bands of offset o0 (the most of any offset here)
-    // processing-order row -> moved row (slot I.a + moved row)
+    // processing-order row -> moved row (slot Ia + moved row)
     auto moved_row = [&](int ip) { return mirror ? M - 1 - ip : ip; };
     if (tid < 4 * Kt) {
         // block ids of band k's first (w & 1 == 0) and last row, source (w < 2)
         // or destination, and the first row's row within its block
         const int k = tid >> 2, w = tid & 3;
         const int ip = o0 + k * L + ((w & 1) ? min(nrow, M - o0 - k * L) - 1 : 0);
-        const int slot = I.a + moved_row(ip) + ((w & 2) ? I.shift : 0);
+        const int slot = Ia + moved_row(ip) + ((w & 2) ? Ishift : 0);
         int b = bt[bt_index(slot)];
         if ((unsigned)b >= nb) { raise_error(KVR_DEV_BAD_BLOCK); b = -1; }
         s_blk[tid] = b;
@@ -208,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
     if (ONE) {
         if (tid < P.n_pairs) s_cs[tid] = make_float2(A.cs[2 * tid], A.cs[2 * tid + 1]);
     } else {
-        angle_table(s_cs, A.omega, P.n_pairs, I.shift, tid);
+        angle_table(s_cs, A.omega, P.n_pairs, Ishift, tid);
     }
     __syncthreads();
 
@@ -285,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
     // ---- Delta > 0: stub rows that land on the last row of each chain -------
     // Every chain's last row was read before the last group's stores.  Tile
     // rows 0..TO-1 (band 0 of a group) stand for the tile's offsets here.
-    if (mirror && I.r_len > 0) {
+    if (mirror && Ir_len > 0) {
         const char* spf = I.src.pf + (int64_t)layer * I.src.pf_l;
         const char* srp = I.src.rp + (int64_t)layer * I.src.rp_l;
         // offset o's last row is moved row (M - 1 - o) mod L, in band kl; the
@@ -323,10 +339,17 @@ __global__ __launch_bounds__(kThreads) void band_kernel(const RelocArgs A) {
     }
 }
 
+template <int PFI, int RS, bool RF32, bool ONE>
+void launch_band_kernel(const RelocArgs& a, hipStream_t s) {
+    const Item& I = a.items[0];
+    hipLaunchKernelGGL((band_kernel<PFI, RS, RF32, ONE>), dim3(a.n_wg), dim3(kThreads), 0, s, a.bt + I.bt_off, I.a,
+                       I.b, I.shift, I.moved, I.tiles, I.move_tiles, I.r_len, a.tile_rows, a.pool.block_size, a);
+}
+
 template <int PFI, int RS, bool ONE>
 hipError_t launch_band_one(const RelocArgs& a, bool f32, hipStream_t s) {
-    if (f32) hipLaunchKernelGGL((band_kernel<PFI, RS, true, ONE>), dim3(a.n_wg), dim3(kThreads), 0, s, a);
-    else     hipLaunchKernelGGL((band_kernel<PFI, RS, false, ONE>), dim3(a.n_wg), dim3(kThreads), 0, s, a);
+    if (f32) launch_band_kernel<PFI, RS, true, ONE>(a, s);
+    else     launch_band_kernel<PFI, RS, false, ONE>(a, s);
     return hipGetLastError();
 }
 
@@ -339,8 +362,7 @@ hipError_t launch_band_rs(const RelocArgs& a, int rs, bool f32, hipStream_t s) {
         case 2: if (PFI >= 2) return launch_band_one<PFI, (PFI >= 2 ? 2 : 1), ONE>(a, f32, s); break;
         case 4:
             if (PFI >= 4 && !f32) {
-                hipLaunchKernelGGL((band_kernel<PFI, (PFI >= 4 ? 4 : 1), false, ONE>), dim3(a.n_wg), dim3(kThreads),
-                                   0, s, a);
+                launch_band_kernel<PFI, (PFI >= 4 ? 4 : 1), false, ONE>(a, s);
                 return hipGetLastError();
             }
             break;
