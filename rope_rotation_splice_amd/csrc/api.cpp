@@ -111,12 +111,13 @@ TileShape choose_tile(const Pool& P, bool rope_f32, bool splice) {
     return s;
 }
 
-// Chain tiles of the band mover hold about 9 KB of rows (8 MLA rows), and at
-// most a block of rows, so that the rows a tile takes from one band span at
+// Chain tiles of the band mover hold about 4.5 KB of rows (4 MLA rows), and
+// at most a block of rows, so that the rows a tile takes from one band span at
 // most two blocks.  Latency-bound calls finish sooner in many small tiles:
-// the single 4096-slot splice (2,296 rows) took 8.2, 6.6, 6.4, 6.7 and 7.2 us
-// on MI355X with tiles of 32, 16, 8, 4 and 2 rows.
-constexpr int kBandBytes = 9216;
+// the single 4096-slot splice (2,296 rows, one-item launch with preloaded
+// arguments) took a median of 5.24, 5.12, 4.96 and 5.86 us on MI355X with
+// tiles of 16, 8, 4 and 2 rows.
+constexpr int kBandBytes = 4608;
 // Calls that move fewer rows than this (all layers; 256 compute units x 8
 // workgroups x 32 rows) are bound by latency and take the band mover; larger
 // ones stream through the ticketed mover.  Measured on MI355X: the single
