@@ -137,6 +137,26 @@ def test_splice_block_size_not_a_power_of_two(delta):
     _run(rc.MLA, 2, 24, 43, seqs, (24, delta + 2000))
 
 
+@pytest.mark.parametrize("layout", ["MLA", "GQA", "MLA_F32"])
+@pytest.mark.parametrize("block_size", [1, 24, 64])
+@pytest.mark.parametrize("delta", [-700, -1, 25, 130])
+def test_splice_single_sequence_one_item_launch(layout, block_size, delta):
+    """A small call with one sequence takes the band mover's one-item form:
+    the item's scalars arrive as leading (preloaded) kernel arguments and its
+    (cos, sin) table is formed on the host in float64.  Every layout (MLA
+    bf16, GQA with 8 rotary heads, fp32 keys), a block size of 1, one that is
+    not a power of two, and shrinks and growth (the stub rows that land on the
+    chains' last sources) against the oracle."""
+    lay = getattr(rc, layout)
+    cap = 24 * 43 if block_size == 24 else 1024
+    n = min(1000, cap - max(delta, 0))
+    s_len = max(40, -delta + 3)
+    r_len = s_len + delta
+    s0 = 100
+    _run(lay, 2, block_size, cap // block_size, [(n, s0, s0 + s_len, r_len, 0)],
+         (block_size, delta + 3000, len(layout)))
+
+
 def test_splice_gqa_layout():
     seqs = [(900, 10, 300, 17, 0), (1024 - 40, 500, 510, 50, 0), (513, 0, 513, 5, 0)]
     _run(rc.GQA, 2, 16, 64, seqs, (77,))
