@@ -174,7 +174,7 @@ def test_decode_negative_control_zero_delta():
         assert tolerance.decode_close(o[b], o0, lse[b], l0).all()
 
 
-def test_decode_workload_sampled():
+def test_decode_workload_every_sequence():
     """The full decode workload (batch 32, 32768 tokens, 128 heads, pending
     delta ~ U{-1e5..1e5} per 64-token block) in the launch configuration the
     benchmark times; every sequence is compared with the oracle on

@@ -61,7 +61,7 @@ def test_gather_gqa_and_fp32():
     _run(rc.MLA_F32, 2, 32, 24, 2, chunks, (15,))
 
 
-def test_gather_registry_workload_sampled():
+def test_gather_registry_workload_every_layer():
     """The 61-layer registry workload at full size (32 entries into a
     40960-slot paged sequence), in the launch configuration the benchmark
     times: every layer is compared in full with the oracle (moved rows,

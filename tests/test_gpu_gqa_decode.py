@@ -175,7 +175,7 @@ def test_gqa_decode_bad_block_skipped_and_flagged():
     _check(o, lse, host, scale, [1])
 
 
-def test_gqa_decode_workload_sampled():
+def test_gqa_decode_workload_every_sequence():
     """The full GQA decode workload (batch 32, 32768 tokens, 32 query heads on
     8 KV heads of 128, pending delta ~ U{-30000..30000} per 64-token block) in
     the launch configuration the benchmark times; every sequence is compared

@@ -80,16 +80,16 @@ def test_keys_bad_token_flagged():
     assert rrs.device_errors() & 16
 
 
-def test_keys_full_workload_sampled():
+def test_keys_full_workload_every_stream():
     """The keying workload at full size (64 streams x 32768 tokens, vocab
-    131072, threshold 2^56, chunks 64..2048, S1 windows of 128), streams 0,
-    31 and 63 compared with the oracle."""
+    131072, threshold 2^56, chunks 64..2048, S1 windows of 128), every stream
+    compared with the oracle: chunk ends, chunk fingerprints, S1 windows."""
     import rope_rotation_splice_amd as rrs
     w = kvsynth.registry_streams()
     streams = list(w.tokens)
     off, out = _run(streams, w.gear, w.threshold, w.min_len, w.max_len, w.s1_window, with_hash=False)
     assert rrs.device_errors() == 0
-    for s in (0, 31, 63):
+    for s in range(len(streams)):
         sub = {k: (v[s:s + 1] if v is not None else None) for k, v in out.items()}
         _check([streams[s]], w.gear, w.threshold, w.min_len, w.max_len, w.s1_window, w.seed, [0, len(streams[s])],
                sub, check_hash=False)

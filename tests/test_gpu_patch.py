@@ -130,7 +130,7 @@ def test_patch_in_place(part, ranges):
     assert np.array_equal(after[:, ~touched], before[:, ~touched])
 
 
-def test_gqa_patch_workload_sampled():
+def test_gqa_patch_workload_every_layer():
     """The full GQA workload (32 layers, 16 chunks x 1024 tokens, rank 16,
     factors N(0, 0.01^2)) in the launch configuration the benchmark times;
     every layer of every chunk is compared in full with the oracle."""
